@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-quantized hot path on one MI355X.
+
+Headline (one JSON line on stdout): batch-1 dequant-GEMV of an 11008 x 4096
+super-block Type 0 matrix (138-byte blocks, per-row std log-uniform in
+[0.005, 0.05]), x fp16 ~N(0,1), y fp32 -- effective HBM GB/s = algorithmic
+bytes (blocks + x + y = 24,357,888 B) / time per GEMV.
+
+A step is one GEMV launch.  The weights rotate through enough distinct copies
+(> 2x the 256 MB last-level cache) that every step streams them from HBM.  The
+K steps are captured in a HIP graph (no host launch gaps) and timed with HIP
+events on the capture/replay stream; the average launch duration is the timed
+region / K.
+
+Also measured (field "rows"): every other step of the hot path at the shapes
+of the synthetic workloads -- quantization (Q4_0, super-block Type 0 and
+Type 1 over a 32-layer 7B-shaped stack from fp16), dequantization, the Q4_0 and
+Type 1 GEMVs and the prefill GEMM (N = 16, 64, 512).
+
+cpu_baseline: the CPU oracle (oracle/, plain C, one thread, fp64 sums) timed
+on this host on the same GEMV workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MALL_BYTES = 256 << 20
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_sb4_11008x4096.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("qblk_gemv.hip", "qblk_device.h"):
+        with open(os.path.join(ROOT, "bit_block_quant_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """Capture `launch(i)` for i in range(n) into a HIP graph; time replays."""
+
+    def __init__(self, torch, launch, n):
+        self.torch = torch
+        self.n = n
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(n):  # eager pass (also loads the kernels)
+                launch(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g):
+            for i in range(n):
+                launch(i)
+        torch.cuda.synchronize()
+
+    def run(self, reps, warmup=1):
+        t = self.torch
+        for _ in range(warmup):
+            self.g.replay()
+        t.cuda.synchronize()
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            self.g.replay()
+        b.record()
+        t.cuda.synchronize()
+        return a.elapsed_time(b) / (reps * self.n)  # ms per launch
+
+
+def n_copies(nbytes):
+    return max(2, -(-2 * MALL_BYTES // nbytes) + 1)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000, help="timed GEMV launches")
+    ap.add_argument("--warmup", type=int, default=200, help="untimed GEMV launches")
+    ap.add_argument("--rows", type=int, default=1, help="1: also time the other hot-path steps")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from __graft_entry__ import _ensure_built
+    _ensure_built()
+    import bit_block_quant_amd as q
+    import workloads as WL
+
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    dev = torch.device("cuda:0")
+
+    # ------------------------------------------------------------ headline
+    w, x = WL.sb4_decode("up")
+    M, K = w.shape
+    blocks0 = q.quantize(torch.from_numpy(w).to(dev), q.SB4)
+    nbytes = blocks0.numel()
+    C = n_copies(nbytes)
+    copies = [blocks0] + [blocks0.clone() for _ in range(C - 1)]
+    xd = torch.from_numpy(x).to(dev)
+    yd = torch.empty(M, dtype=torch.float32, device=dev)
+    algo_bytes = nbytes + 2 * K + 4 * M
+    log(f"gemv sb4 {M}x{K}: {nbytes} B of blocks, {C} rotating copies ({C * nbytes / 2**20:.0f} MiB)")
+
+    # one graph of C launches (one per copy); replayed ceil(steps / C) times
+    reps = max(1, -(-args.steps // C))
+    steps = reps * C
+    wreps = max(1, -(-args.warmup // C))
+    timer = Timer(torch, lambda i: q.gemv(copies[i % C], q.SB4, M, K, xd, out=yd), C)
+    timer.run(wreps, warmup=0)
+    ms = timer.run(reps, warmup=0)
+    gbs = algo_bytes / (ms * 1e-3) / 1e9
+    log(f"  {ms * 1e3:.2f} us per GEMV, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        t = json.load(open(TRAFFIC_FILE))
+        if t.get("kernel_source_hash") == kernel_source_hash():
+            traffic = t.get("bytes_per_launch")
+
+    result = {
+        "metric": "dequant-GEMV effective HBM GB/s (% of ~8 TB/s peak), 11008x4096 batch 1",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": wreps * C,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "sb4_type0_gemv_11008x4096_batch1",
+            "format": "super-block Type 0, 138 B per 256 weights",
+            "m": M, "k": K, "x": "f16", "y": "f32",
+            "algorithmic_bytes": algo_bytes,
+            "rotating_copies": C,
+            "timing": "HIP graph of back-to-back launches, HIP events",
+        },
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+        },
+        "device": props.name,
+        "weights_per_s": round(M * K / (ms * 1e-3), 1),
+        "gemv_per_s": round(1.0 / (ms * 1e-3), 1),
+    }
+    del copies
+
+    if args.rows:
+        result["rows"] = measure_rows(torch, q, WL, np, dev)
+
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(np, WL, w, x, algo_bytes, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+# ----------------------------------------------------------------- other rows
+def measure_rows(torch, q, WL, np, dev):
+    rows = {}
+    gen = torch.Generator(device=dev)
+
+    def randn(shape, std, seed, dtype=torch.float32):
+        gen.manual_seed(seed)
+        t = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+        return (t * std).to(dtype)
+
+    def hbm_row(name, ms, nbytes, **extra):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        rows[name] = dict(us=round(ms * 1e3, 3), bytes=nbytes, GBps=round(gbs, 1),
+                          frac_hbm=round(gbs / HBM_PEAK_GBS, 4), **extra)
+        log(f"  {name}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s")
+
+    # GEMVs with rotation
+    def gemv_row(name, fmt, w, x):
+        m, k = w.shape
+        b0 = q.quantize(w, fmt)
+        C = n_copies(b0.numel())
+        cps = [b0] + [b0.clone() for _ in range(C - 1)]
+        y = torch.empty(m, dtype=torch.float32, device=dev)
+        t = Timer(torch, lambda i: q.gemv(cps[i], fmt, m, k, x, out=y), C)
+        ms = t.run(max(1, 400 // C))
+        hbm_row(name, ms, b0.numel() + x.numel() * x.element_size() + 4 * m, m=m, k=k)
+
+    w, x = WL.sb4_decode("down")
+    gemv_row("gemv_sb4_4096x11008_f16", q.SB4, torch.from_numpy(w).to(dev), torch.from_numpy(x).to(dev))
+    w, x = WL.q4_0_decode()
+    gemv_row("gemv_q4_0_4096x4096_f16", q.Q4_0, torch.from_numpy(w).to(dev), torch.from_numpy(x).to(dev))
+    w, x = WL.q4_0_small()
+    gemv_row("gemv_q4_0_256x4096_f32", q.Q4_0, torch.from_numpy(w).to(dev), torch.from_numpy(x).to(dev))
+
+    # quantizers
+    def quant_row(name, fmt, w, reps=20):
+        out = torch.empty(q.packed_bytes(fmt, *w.shape), dtype=torch.uint8, device=dev)
+        t = Timer(torch, lambda i: q.quantize(w, fmt, out=out), 1)
+        ms = t.run(reps)
+        nb = w.numel() * w.element_size() + out.numel()
+        hbm_row(name, ms, nb, weights_per_s=round(w.numel() / (ms * 1e-3), 1))
+
+    w, _ = WL.q4_0_decode()
+    quant_row("quantize_q4_0_4096x4096_f32", q.Q4_0, torch.from_numpy(w).to(dev))
+    w, _ = WL.sb4_decode("up")
+    wup = torch.from_numpy(w).to(dev)
+    quant_row("quantize_sb4_11008x4096_f32", q.SB4, wup)
+    quant_row("quantize_sb4a_11008x4096_f32", q.SB4_AFFINE, wup)
+
+    # dequant
+    b = q.quantize(wup, q.SB4)
+    out = torch.empty(wup.shape, dtype=torch.float32, device=dev)
+    t = Timer(torch, lambda i: q.dequant(b, q.SB4, *wup.shape, out=out), 1)
+    hbm_row("dequant_sb4_11008x4096_to_f32", t.run(20), b.numel() + out.numel() * 4)
+    del wup, out, b
+
+    # 7B-shaped 32-layer stack, Type 1: quantize from fp16, then one GEMV pass
+    mats, outs, xs = [], [], []
+    for layer in range(WL.STACK_LAYERS):
+        for p, (_, r, k) in enumerate(WL.STACK_PROJ):
+            sw, sx = WL.stack_seed(layer, p)
+            mats.append(randn((r, k), 0.02, sw, torch.float16))
+            outs.append(torch.empty(q.packed_bytes(q.SB4_AFFINE, r, k), dtype=torch.uint8, device=dev))
+            xs.append(randn((k,), 1.0, sx, torch.float16))
+    n = len(mats)
+    t = Timer(torch, lambda i: q.quantize(mats[i], q.SB4_AFFINE, out=outs[i]), n)
+    ms = t.run(2) * n
+    src = sum(m.numel() * 2 for m in mats)
+    dst = sum(o.numel() for o in outs)
+    hbm_row("quantize_sb4a_stack_32x7_f16", ms, src + dst,
+            weights=sum(m.numel() for m in mats), weights_per_s=round(sum(m.numel() for m in mats) / (ms * 1e-3), 1))
+    del mats
+    ys = [torch.empty(WL.STACK_PROJ[i % 7][1], dtype=torch.float32, device=dev) for i in range(n)]
+
+    def stack_gemv(i):
+        _, r, k = WL.STACK_PROJ[i % 7]
+        q.gemv(outs[i], q.SB4_AFFINE, r, k, xs[i], out=ys[i])
+
+    t = Timer(torch, stack_gemv, n)
+    ms = t.run(3) * n
+    nb = dst + sum(xx.numel() * 2 for xx in xs) + sum(yy.numel() * 4 for yy in ys)
+    hbm_row("gemv_sb4a_stack_32x7_f16", ms, nb, tokens_per_s_equivalent=round(1.0 / (ms * 1e-3), 1))
+    del outs, xs, ys
+
+    # prefill GEMM
+    for shape in ("up", "down"):
+        w, _ = WL.sb4_prefill(shape, 16)
+        m, k = w.shape
+        b0 = q.quantize(torch.from_numpy(w).to(dev), q.SB4)
+        C = n_copies(b0.numel())
+        cps = [b0] + [b0.clone() for _ in range(C - 1)]
+        for n_tok in (16, 64, 512):
+            _, X = WL.sb4_prefill(shape, n_tok)
+            Xd = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16)
+            Y = torch.empty((n_tok, m), dtype=torch.float32, device=dev)
+            t = Timer(torch, lambda i: q.gemm(cps[i], q.SB4, m, k, Xd, out=Y), C)
+            ms = t.run(max(1, 100 // C))
+            flops = 2.0 * m * k * n_tok
+            nb = b0.numel() + X.size * 2 + Y.numel() * 4
+            tf = flops / (ms * 1e-3) / 1e12
+            gbs = nb / (ms * 1e-3) / 1e9
+            name = f"gemm_sb4_{m}x{k}_n{n_tok}_bf16"
+            rows[name] = dict(us=round(ms * 1e3, 3), bytes=nb, GBps=round(gbs, 1),
+                              frac_hbm=round(gbs / HBM_PEAK_GBS, 4), TFLOPs=round(tf, 2),
+                              frac_mfma_bf16=round(tf / BF16_PEAK_TFLOPS, 4))
+            log(f"  {name}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s, {tf:.1f} TFLOP/s")
+        del cps
+    return rows
+
+
+# --------------------------------------------------------------- CPU oracle
+def cpu_baseline(np, WL, w, x, algo_bytes, budget_s):
+    import oracle as O
+
+    m, k = w.shape
+    blocks = O.quantize_sb4(w)  # the oracle quantizes its own input (untimed)
+    xd = x.astype(np.float64)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.gemv(O.SB4, blocks, m, k, xd)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 1000:
+            break
+    per = el / reps
+    return {
+        "value": round(algo_bytes / per / 1e9, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{reps} full {m}x{k} super-block GEMVs (C oracle: per-row fp32 dequant, fp64 sums), "
+                  f"{el:.1f} s, {per * 1e3:.1f} ms each",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,168 @@
+// qblk_abi.hip -- the C ABI of libqblk (declared in include/qblk.h): argument
+// checks on the host, then one kernel launch on the caller's stream.
+#include <stdint.h>
+
+#include "../../include/qblk.h"
+#include "qblk_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxBytes = int64_t(1) << 40;
+
+int elems_of(int fmt) {
+  switch (fmt) {
+    case QBLK_Q4_0: return 32;
+    case QBLK_SB4:
+    case QBLK_SB4_AFFINE: return 256;
+    default: return 0;
+  }
+}
+
+size_t bytes_of(int fmt) {
+  switch (fmt) {
+    case QBLK_Q4_0: return 18;
+    case QBLK_SB4: return 138;
+    case QBLK_SB4_AFFINE: return 148;
+    default: return 0;
+  }
+}
+
+bool dtype_ok(int t) { return t == QBLK_F32 || t == QBLK_F16 || t == QBLK_BF16; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape of a packed rows x k matrix: sizes in range, k a multiple of the block.
+qblk_status_t check_shape(int fmt, int64_t rows, int64_t k) {
+  const int e = elems_of(fmt);
+  if (e == 0) return QBLK_ERR_FORMAT;
+  if (rows < 0 || k < 0 || rows > kMaxDim || k > kMaxDim || k % e != 0) return QBLK_ERR_SHAPE;
+  if (rows > 0 && k > 0 && rows * (k / e) > kMaxBytes / static_cast<int64_t>(bytes_of(fmt)))
+    return QBLK_ERR_SHAPE;
+  return QBLK_OK;
+}
+
+qblk_status_t check_ptr(const void* p, bool needed) {
+  if (!needed) return QBLK_OK;
+  if (!p) return QBLK_ERR_NULL;
+  if (!aligned16(p)) return QBLK_ERR_ALIGN;
+  return QBLK_OK;
+}
+
+qblk_status_t from_hip(hipError_t e) { return e == hipSuccess ? QBLK_OK : QBLK_ERR_LAUNCH; }
+
+#define QBLK_TRY(expr)                 \
+  do {                                 \
+    const qblk_status_t st_ = (expr);  \
+    if (st_ != QBLK_OK) return st_;    \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t qblk_block_bytes(qblk_format_t fmt) { return bytes_of(fmt); }
+
+int qblk_block_elems(qblk_format_t fmt) { return elems_of(fmt); }
+
+size_t qblk_packed_bytes(qblk_format_t fmt, int64_t rows, int64_t k) {
+  if (check_shape(fmt, rows, k) != QBLK_OK) return 0;
+  return static_cast<size_t>(rows) * static_cast<size_t>(k / elems_of(fmt)) * bytes_of(fmt);
+}
+
+qblk_status_t qblk_quantize_q4_0(const void* w, qblk_dtype_t wt, int64_t rows, int64_t k,
+                                 void* blocks, qblk_stream_t stream) {
+  QBLK_TRY(check_shape(QBLK_Q4_0, rows, k));
+  if (!dtype_ok(wt)) return QBLK_ERR_DTYPE;
+  const bool work = rows > 0 && k > 0;
+  QBLK_TRY(check_ptr(w, work));
+  QBLK_TRY(check_ptr(blocks, work));
+  if (!work) return QBLK_OK;
+  return from_hip(qblk::launch_quantize_q4_0(w, wt, rows, k, blocks,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+qblk_status_t qblk_quantize_q4_0_ref(const void* w, qblk_dtype_t wt, int64_t rows, int64_t k,
+                                     void* blocks, qblk_stream_t stream) {
+  QBLK_TRY(check_shape(QBLK_Q4_0, rows, k));
+  if (wt != QBLK_F32) return QBLK_ERR_DTYPE;
+  const bool work = rows > 0 && k > 0;
+  QBLK_TRY(check_ptr(w, work));
+  QBLK_TRY(check_ptr(blocks, work));
+  if (!work) return QBLK_OK;
+  return from_hip(qblk::launch_quantize_q4_0_ref(static_cast<const float*>(w), rows, k, blocks,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+qblk_status_t qblk_quantize_sb4(const void* w, qblk_dtype_t wt, int64_t rows, int64_t k,
+                                int affine, void* blocks, qblk_stream_t stream) {
+  const int fmt = affine ? QBLK_SB4_AFFINE : QBLK_SB4;
+  QBLK_TRY(check_shape(fmt, rows, k));
+  if (!dtype_ok(wt)) return QBLK_ERR_DTYPE;
+  const bool work = rows > 0 && k > 0;
+  QBLK_TRY(check_ptr(w, work));
+  QBLK_TRY(check_ptr(blocks, work));
+  if (!work) return QBLK_OK;
+  return from_hip(qblk::launch_quantize_sb4(w, wt, rows, k, affine ? 1 : 0, blocks,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+qblk_status_t qblk_dequant(qblk_format_t fmt, const void* blocks, int64_t rows, int64_t k,
+                           void* out, qblk_dtype_t ot, qblk_stream_t stream) {
+  QBLK_TRY(check_shape(fmt, rows, k));
+  if (!dtype_ok(ot)) return QBLK_ERR_DTYPE;
+  const bool work = rows > 0 && k > 0;
+  QBLK_TRY(check_ptr(blocks, work));
+  QBLK_TRY(check_ptr(out, work));
+  if (!work) return QBLK_OK;
+  return from_hip(qblk::launch_dequant(fmt, blocks, rows, k, out, ot,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+qblk_status_t qblk_gemv(qblk_format_t fmt, const void* blocks, int64_t m, int64_t k,
+                        const void* x, qblk_dtype_t xt, float* y, qblk_stream_t stream) {
+  QBLK_TRY(check_shape(fmt, m, k));
+  if (!dtype_ok(xt)) return QBLK_ERR_DTYPE;
+  QBLK_TRY(check_ptr(blocks, m > 0 && k > 0));
+  QBLK_TRY(check_ptr(x, m > 0 && k > 0));
+  QBLK_TRY(check_ptr(y, m > 0));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (m == 0) return QBLK_OK;
+  if (k == 0) return from_hip(qblk::launch_fill_zero(y, m, s));
+  return from_hip(qblk::launch_gemv(fmt, blocks, m, k, x, xt, y, s));
+}
+
+qblk_status_t qblk_gemm(qblk_format_t fmt, const void* blocks, int64_t m, int64_t k,
+                        const void* x, qblk_dtype_t xt, int64_t n, float* y,
+                        qblk_stream_t stream) {
+  QBLK_TRY(check_shape(fmt, m, k));
+  if (!dtype_ok(xt)) return QBLK_ERR_DTYPE;
+  if (n < 0 || n > kMaxDim) return QBLK_ERR_SHAPE;
+  if (fmt != QBLK_SB4 || xt != QBLK_BF16) return QBLK_ERR_UNSUPPORTED;
+  const bool out = m > 0 && n > 0;
+  QBLK_TRY(check_ptr(blocks, out && k > 0));
+  QBLK_TRY(check_ptr(x, out && k > 0));
+  QBLK_TRY(check_ptr(y, out));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!out) return QBLK_OK;
+  if (k == 0) return from_hip(qblk::launch_fill_zero(y, m * n, s));
+  return from_hip(qblk::launch_gemm(fmt, blocks, m, k, x, xt, n, y, s));
+}
+
+const char* qblk_status_string(qblk_status_t st) {
+  switch (st) {
+    case QBLK_OK: return "ok";
+    case QBLK_ERR_NULL: return "a required pointer is NULL";
+    case QBLK_ERR_SHAPE: return "invalid size (negative, too large, or k not a multiple of the block size)";
+    case QBLK_ERR_DTYPE: return "element type not accepted by this call";
+    case QBLK_ERR_ALIGN: return "a data pointer is not 16-byte aligned";
+    case QBLK_ERR_UNSUPPORTED: return "format/type combination not implemented";
+    case QBLK_ERR_LAUNCH: return "kernel launch failed";
+    case QBLK_ERR_FORMAT: return "unknown block format";
+  }
+  return "unknown status";
+}
+
+const char* qblk_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// qblk_device.h -- device-side helpers shared by the gfx950 kernels of libqblk:
+// number conversions, the rounding rule, wave reductions and loads of the
+// 2-byte-aligned fields of the packed block streams.
+//
+// Every kernel is compiled with -ffp-contract=off (no implicit fused
+// multiply-add; dequantization must reproduce separate IEEE products), with
+// correctly rounded fp32 division and with fp32/fp16 denormals kept; fused
+// multiply-adds that are wanted (accumulation) are written explicitly.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qblk {
+
+typedef _Float16 half_t;
+typedef half_t half2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef short bf16x8_t __attribute__((ext_vector_type(8)));
+// 16 bytes with only dword alignment: global_load_dwordx4 needs 4-byte
+// alignment, and the fields of the block streams sit at 2-byte granularity.
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+typedef uint32_t u32x3_a4 __attribute__((ext_vector_type(3), aligned(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- numbers
+// fp32 -> fp16 bits, round to nearest even (v_cvt_f16_f32 under the default
+// round mode; fp16 denormals are kept by the default FP16/64 denorm mode).
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float v) {
+  return __builtin_bit_cast(uint16_t, static_cast<half_t>(v));
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>(b)));
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __builtin_bit_cast(float, b << 16);
+}
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Round half away from zero (roundf is exactly that operation).
+__device__ __forceinline__ float rha(float v) { return __builtin_roundf(v); }
+
+// Quotient used by every quantizer: zero scale -> 0.  True IEEE division.
+__device__ __forceinline__ float qdiv(float v, float s) { return s == 0.0f ? 0.0f : v / s; }
+
+// round-half-away quotient clamped into [lo, hi]; NaN lands on lo.
+__device__ __forceinline__ int code_of(float v, float s, float lo, float hi) {
+  float t = rha(qdiv(v, s));
+  t = __builtin_fmaxf(t, lo);  // fmax(NaN, lo) = lo
+  t = __builtin_fminf(t, hi);
+  return static_cast<int>(t);
+}
+
+// Optimisation barrier: the value is materialised in a VGPR, so a following
+// narrowing conversion cannot be fused with the arithmetic that produced it
+// (a fused v_fma_mix with a +0 addend would turn -0 into +0).
+__device__ __forceinline__ float opaque(float v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
+// (a & mask) | bits in one v_and_or_b32 (mask from an SGPR, bits from a VGPR).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t bits) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(bits));
+  return r;
+}
+
+// ---------------------------------------------------------------- waves
+// Sum over the 64 lanes of a wave with DPP moves; the total lands in lane 63.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));  // quad_perm 2,3,0,1
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true)); // row_half_mirror
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true)); // row_mirror
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false)); // row_bcast:15
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false)); // row_bcast:31
+  return v;
+}
+
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int m = 1; m < W; m <<= 1) v = __builtin_fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+template <int W>
+__device__ __forceinline__ float group_min(float v) {
+#pragma unroll
+  for (int m = 1; m < W; m <<= 1) v = __builtin_fminf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+
+// ---------------------------------------------------------------- loads
+// 16 bytes starting at a 2-byte-aligned address p: a dword-aligned 16-byte
+// load from p rounded down to 4, plus the 2 bytes that spill past it, realigned
+// with v_alignbyte.  Every byte read lies inside [p - 2, p + 16).
+__device__ __forceinline__ void load16_a2(const uint8_t* p, uint32_t out[4]) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(a & ~uintptr_t(3));
+  const uint32_t tail = *reinterpret_cast<const uint16_t*>(p + 14);
+  const uint32_t sh = static_cast<uint32_t>(a & 3u);  // 0 or 2
+  out[0] = __builtin_amdgcn_alignbyte(v.y, v.x, sh);
+  out[1] = __builtin_amdgcn_alignbyte(v.z, v.y, sh);
+  out[2] = __builtin_amdgcn_alignbyte(v.w, v.z, sh);
+  out[3] = __builtin_amdgcn_alignbyte(tail, v.w, sh);
+}
+
+__device__ __forceinline__ uint32_t load_u16(const uint8_t* p) {
+  return *reinterpret_cast<const uint16_t*>(p);
+}
+
+}  // namespace qblk

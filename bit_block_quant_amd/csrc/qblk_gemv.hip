@@ -1,0 +1,578 @@
+// qblk_gemv.hip -- batch-1 dequantize-and-multiply y = W x on gfx950.
+//
+// What is computed: y[i] = sum_k W[i,k] x[k] where W[i,k] is the block
+// format's rebuilt weight (Q4_0: d*(code-8), "GGUF 量化内幕 第4章 Q4_0" 4.3;
+// super-block Type 0: (S*sc_j)*(code-8) and Type 1: (Ss*sc_j)*code + Sa*ac_j,
+// "GGUF K-quants" blog, "套娃" step 5).  The pages only say that dequantized
+// weights feed the matrix product; this kernel never materialises W.
+//
+// Work split.  A 32-weight unit (a Q4_0 block or one super-block sub-block)
+// shares one scale.  Lane l of a wave takes units l, l+64, ... of a row and
+// R rows at once (x is read once per unit and used R times); each wave then
+// reduces its R partial sums across the 64 lanes.  Adjacent lanes read
+// adjacent 16-byte code groups, so each load instruction of a wave covers a
+// contiguous ~1 KB stretch of the packed stream.
+//
+// Arithmetic (x in fp16).  Codes are turned into exact fp16 values by OR-ing a
+// nibble into the mantissa of 1024.0 (0x6400) and subtracting 1032 (or, for
+// the high nibbles, which sit 4 bits up, 1024 + 16*8 giving 16*(code-8));
+// v_dot2_f32_f16 then forms exact fp16 x fp16 products and accumulates them in
+// fp32.  To pair codes with x without shuffling the codes, x is staged in LDS
+// in the matching order: for code word t (bytes 4t..4t+3 of a unit) the pairs
+// are (x[4t], x[4t+2]), (x[4t+16], x[4t+18]), (x[4t+1], x[4t+3]),
+// (x[4t+17], x[4t+19]).  The unit's fp32 scale multiplies the two partial
+// sums; Type 1 adds offset * sum(x over the unit).
+// With x in fp32 (or bf16, widened exactly to fp32) the codes are converted
+// with v_cvt_f32_ubyte and accumulated with fp32 fused multiply-adds.
+#include "qblk_device.h"
+#include "qblk_launch.h"
+
+namespace qblk {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kChunkF16 = 16384;  // x elements staged per pass (32 KB of fp16)
+constexpr int kChunkF32 = 8192;   // (32 KB of fp32)
+
+template <int FMT>
+struct Fmt;
+template <>
+struct Fmt<QBLK_Q4_0> {
+  static constexpr int E = 32, B = 18;
+};
+template <>
+struct Fmt<QBLK_SB4> {
+  static constexpr int E = 256, B = 138;
+};
+template <>
+struct Fmt<QBLK_SB4_AFFINE> {
+  static constexpr int E = 256, B = 148;
+};
+
+// Scale, offset and the 16 code bytes of unit s of a row.
+template <int FMT>
+__device__ __forceinline__ void load_unit(const uint8_t* row, int s, float& sc, float& off,
+                                          uint32_t q[4]) {
+  if constexpr (FMT == QBLK_Q4_0) {
+    const uint8_t* p = row + static_cast<int64_t>(s) * 18;
+    sc = f16_bits_to_f32(load_u16(p));
+    off = 0.0f;
+    load16_a2(p + 2, q);
+  } else if constexpr (FMT == QBLK_SB4) {
+    const int b = s >> 3, j = s & 7;
+    const uint8_t* p = row + static_cast<int64_t>(b) * 138;
+    const float S = f16_bits_to_f32(load_u16(p));
+    sc = S * static_cast<float>(static_cast<int8_t>(p[2 + j]));
+    off = 0.0f;
+    load16_a2(p + 10 + 16 * j, q);
+  } else {
+    const int b = s >> 3, j = s & 7;
+    const uint8_t* p = row + static_cast<int64_t>(b) * 148;
+    const uint32_t h = *reinterpret_cast<const uint32_t*>(p);
+    sc = f16_bits_to_f32(h & 0xffffu) * static_cast<float>(static_cast<int8_t>(p[4 + j]));
+    off = f16_bits_to_f32(h >> 16) * static_cast<float>(static_cast<int8_t>(p[12 + j]));
+    const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(p + 20 + 16 * j);
+    q[0] = v.x;
+    q[1] = v.y;
+    q[2] = v.z;
+    q[3] = v.w;
+  }
+}
+
+__device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+
+// sum over a unit of (code - 8) * x (signed formats) or code * x (affine),
+// returned as lo + hi/16 in two fp32 partials.
+template <bool AFFINE>
+__device__ __forceinline__ void dot_unit_f16(const uint32_t q[4], const uint4 X[4], float& lo,
+                                             float& hi) {
+  // 1024+n -> n-8: subtract 1032; 1024+16n -> 16(n-8): subtract 1152.
+  const half2_t kLo = AFFINE ? half2_t{-1024.0f16, -1024.0f16} : half2_t{-1032.0f16, -1032.0f16};
+  const half2_t kHi = AFFINE ? half2_t{-1024.0f16, -1024.0f16} : half2_t{-1152.0f16, -1152.0f16};
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    const uint32_t a = q[t], b = q[t] >> 8;
+    const half2_t v0 = as_h2((a & 0x000F000Fu) | 0x64006400u) + kLo;
+    const half2_t v1 = as_h2((a & 0x00F000F0u) | 0x64006400u) + kHi;
+    const half2_t v2 = as_h2((b & 0x000F000Fu) | 0x64006400u) + kLo;
+    const half2_t v3 = as_h2((b & 0x00F000F0u) | 0x64006400u) + kHi;
+    const uint4 x = X[t];
+    lo = __builtin_amdgcn_fdot2(v0, as_h2(x.x), lo, false);
+    hi = __builtin_amdgcn_fdot2(v1, as_h2(x.y), hi, false);
+    lo = __builtin_amdgcn_fdot2(v2, as_h2(x.z), lo, false);
+    hi = __builtin_amdgcn_fdot2(v3, as_h2(x.w), hi, false);
+  }
+}
+
+template <bool AFFINE>
+__device__ __forceinline__ float dot_unit_f32(const uint32_t q[4], const float* xs) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    const uint32_t lo = q[t] & 0x0F0F0F0Fu, hi = (q[t] >> 4) & 0x0F0F0F0Fu;
+    const float4 xl = *reinterpret_cast<const float4*>(xs + 4 * t);
+    const float4 xh = *reinterpret_cast<const float4*>(xs + 16 + 4 * t);
+    const float xlv[4] = {xl.x, xl.y, xl.z, xl.w};
+    const float xhv[4] = {xh.x, xh.y, xh.z, xh.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      float cl = static_cast<float>((lo >> (8 * i)) & 0xFFu);
+      float ch = static_cast<float>((hi >> (8 * i)) & 0xFFu);
+      if (!AFFINE) {
+        cl -= 8.0f;
+        ch -= 8.0f;
+      }
+      acc = __builtin_fmaf(cl, xlv[i], acc);
+      acc = __builtin_fmaf(ch, xhv[i], acc);
+    }
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// Stage x[k0, k0+kc) into LDS.  fp16 path: permuted pairs, 16 words per unit.
+// fp32 path: natural order.  Affine formats also get the per-unit sum of x.
+template <int XT, bool AFFINE>
+__device__ void stage_x(const void* x, int k0, int kc, uint32_t* xs, float* xsum) {
+  const int nchunk = kc / 8;  // groups of 8 elements; 4 per unit
+  for (int c = threadIdx.x; c < (nchunk + 3) / 4 * 4; c += kThreads) {
+    float part = 0.0f;
+    if (c < nchunk) {
+      const int e0 = k0 + 8 * c;
+      if constexpr (XT == QBLK_F16) {
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + e0);
+        const int unit = c >> 2, cc = c & 3;
+        const int tb = (cc & 1) * 2, hi = cc >> 1;  // elements 8cc..8cc+7 of the unit
+        uint32_t* d = xs + unit * 16;
+        d[4 * tb + hi] = (u.x & 0xffffu) | (u.y << 16);            // (e0, e2)
+        d[4 * tb + 2 + hi] = (u.x >> 16) | (u.y & 0xffff0000u);    // (e1, e3)
+        d[4 * tb + 4 + hi] = (u.z & 0xffffu) | (u.w << 16);        // (e4, e6)
+        d[4 * tb + 6 + hi] = (u.z >> 16) | (u.w & 0xffff0000u);    // (e5, e7)
+        if (AFFINE) {
+          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int i = 0; i < 4; i++) part += f16_bits_to_f32(w[i] & 0xffffu) + f16_bits_to_f32(w[i] >> 16);
+        }
+      } else {
+        float v[8];
+        if constexpr (XT == QBLK_F32) {
+          const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + e0);
+          const float4 a = p[0], b = p[1];
+          v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+          v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        } else {
+          const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + e0);
+          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            v[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+            v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+          }
+        }
+        float* d = reinterpret_cast<float*>(xs) + 8 * c;
+        reinterpret_cast<float4*>(d)[0] = make_float4(v[0], v[1], v[2], v[3]);
+        reinterpret_cast<float4*>(d)[1] = make_float4(v[4], v[5], v[6], v[7]);
+        if (AFFINE) {
+#pragma unroll
+          for (int i = 0; i < 8; i++) part += v[i];
+        }
+      }
+    }
+    if (AFFINE) {
+      // the 4 chunks of a unit sit on 4 consecutive lanes
+      part += __shfl_xor(part, 1, kWave);
+      part += __shfl_xor(part, 2, kWave);
+      if ((c & 3) == 0 && c < nchunk) xsum[c >> 2] = part;
+    }
+  }
+}
+
+template <int FMT, int XT, int R>
+__global__ __launch_bounds__(kThreads) void k_gemv(const uint8_t* __restrict__ blocks,
+                                                   const void* __restrict__ x,
+                                                   float* __restrict__ y, int M, int K) {
+  constexpr bool AFFINE = FMT == QBLK_SB4_AFFINE;
+  constexpr bool XH = XT == QBLK_F16;
+  constexpr int KC = XH ? kChunkF16 : kChunkF32;
+  extern __shared__ uint4 smem[];
+  // LDS: the staged x chunk (kcmax elements) followed by one sum per unit
+  const int kcmax = K < KC ? K : KC;
+  uint32_t* xs = reinterpret_cast<uint32_t*>(smem);
+  float* xsum = reinterpret_cast<float*>(xs + (XH ? kcmax / 2 : kcmax));
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int64_t r0 = (static_cast<int64_t>(blockIdx.x) * kWaves + wave) * R;
+  const int64_t rowbytes = static_cast<int64_t>(K / Fmt<FMT>::E) * Fmt<FMT>::B;
+  const uint8_t* rowp[R];
+#pragma unroll
+  for (int i = 0; i < R; i++) {
+    const int64_t r = r0 + i < M ? r0 + i : M - 1;  // rows past the end re-read the last row
+    rowp[i] = blocks + r * rowbytes;
+  }
+  float acc[R];
+#pragma unroll
+  for (int i = 0; i < R; i++) acc[i] = 0.0f;
+
+  for (int k0 = 0; k0 < K; k0 += KC) {
+    const int kc = K - k0 < KC ? K - k0 : KC;
+    __syncthreads();
+    stage_x<XT, AFFINE>(x, k0, kc, xs, xsum);
+    __syncthreads();
+    if (r0 >= M) continue;
+    const int s0 = k0 / 32, ns = kc / 32;
+#pragma unroll 2
+    for (int su = lane; su < ns; su += kWave) {
+      float sc[R], off[R];
+      uint32_t q[R][4];
+#pragma unroll
+      for (int i = 0; i < R; i++) load_unit<FMT>(rowp[i], s0 + su, sc[i], off[i], q[i]);
+      if constexpr (XH) {
+        uint4 X[4];
+#pragma unroll
+        for (int t = 0; t < 4; t++) X[t] = smem[su * 4 + t];
+#pragma unroll
+        for (int i = 0; i < R; i++) {
+          float lo = 0.0f, hi = 0.0f;
+          dot_unit_f16<AFFINE>(q[i], X, lo, hi);
+          acc[i] = __builtin_fmaf(sc[i], lo, acc[i]);
+          acc[i] = __builtin_fmaf(sc[i] * 0.0625f, hi, acc[i]);
+        }
+      } else {
+        const float* xf = reinterpret_cast<const float*>(xs) + su * 32;
+#pragma unroll
+        for (int i = 0; i < R; i++) acc[i] = __builtin_fmaf(sc[i], dot_unit_f32<AFFINE>(q[i], xf), acc[i]);
+      }
+      if constexpr (AFFINE) {
+        const float sx = xsum[su];
+#pragma unroll
+        for (int i = 0; i < R; i++) acc[i] = __builtin_fmaf(off[i], sx, acc[i]);
+      }
+    }
+  }
+  if (r0 >= M) return;
+#pragma unroll
+  for (int i = 0; i < R; i++) {
+    const float v = wave_sum(acc[i]);
+    if (lane == 0 && r0 + i < M) y[r0 + i] = v;
+  }
+}
+
+// ===================================================================
+// fp16-x kernel: every load of a wave issued up front, no LDS, no barrier.
+//
+// The rows are split evenly over the workgroups (one 16-wave workgroup per
+// CU); wave w of a workgroup takes rows w, w+16, w+32 of its slice (RMAX of
+// them at most) and lane l takes units l, l+64, ... (UPL of them at most) of
+// each row.  A lane therefore sees the same units of x in every row: it
+// loads their 32 halves once, issued first, and forms the fp16 pairs in
+// registers (v_perm), to be reused for its RMAX rows.  All weight loads
+// follow, group by group -- unit k of row i, unit-major -- with the row base
+// in SGPRs and a fixed 32-bit offset per (lane, unit); the products consume
+// the groups in the same order, so each waits only for its own loads (the
+// load counter drains in issue order).  Nothing here waits for another wave.
+//
+// Code groups of Q4_0 blocks and Type 0 sub-blocks start 2 bytes past a dword
+// boundary every other unit: a dword-aligned 16-byte load from just below,
+// plus the 2 bytes that spill past it, realigned with v_alignbyte.
+// ===================================================================
+constexpr int kWavesH = 16;
+constexpr int kThreadsH = kWavesH * kWave;
+
+template <int FMT>
+struct UnitAddr {
+  // byte offset of the 16 code bytes of unit u inside a row
+  static __device__ __forceinline__ uint32_t codes(int u) {
+    if constexpr (FMT == QBLK_Q4_0) return 18u * u + 2u;
+    else if constexpr (FMT == QBLK_SB4) return 138u * (u >> 3) + 10u + 16u * (u & 7);
+    else return 148u * (u >> 3) + 20u + 16u * (u & 7);
+  }
+};
+
+// KS waves share a row (KS = 2 splits the row's units in two halves whose
+// sums meet in LDS after the only barrier of the kernel).
+template <int FMT, int RMAX, int UPL, int KS>
+__global__ __launch_bounds__(kThreadsH) void k_gemv_h(const uint8_t* __restrict__ blocks,
+                                                      const uint16_t* __restrict__ x,
+                                                      float* __restrict__ y, int M, int K,
+                                                      int rows_per_wg) {
+  constexpr bool AFFINE = FMT == QBLK_SB4_AFFINE;
+  constexpr int E = Fmt<FMT>::E, B = Fmt<FMT>::B;
+  constexpr int SLOTS = kWavesH / KS;  // rows in flight per workgroup round
+  const int S = K >> 5;                // units per row
+  const int SP = (S + KS - 1) / KS;    // units per part
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int slot = wave / KS, part = wave % KS;
+  const int row0 = blockIdx.x * rows_per_wg;
+  const int row_end = min(M, row0 + rows_per_wg);
+  if (KS == 1 && row0 + slot >= row_end) return;  // (KS > 1: every wave meets the barrier)
+  const int64_t rowbytes = static_cast<int64_t>(K / E) * B;
+
+  // per (lane, unit): byte offsets inside a row of the codes, the scale
+  // header and the INT8 sub-scale (Type 1: offset 8 bytes further)
+  uint32_t off[UPL], hoff[UPL], coff[UPL];
+  bool live[UPL];
+#pragma unroll
+  for (int k = 0; k < UPL; k++) {
+    const int uu = part * SP + lane + 64 * k;
+    live[k] = lane + 64 * k < SP && uu < S;
+    const int u = min(uu, S - 1);
+    off[k] = UnitAddr<FMT>::codes(u);
+    hoff[k] = FMT == QBLK_Q4_0 ? off[k] - 2u : static_cast<uint32_t>(B) * (u >> 3);
+    coff[k] = hoff[k] + (AFFINE ? 4u : 2u) + (u & 7);
+  }
+
+  // (1) x of this lane's units, 32 halves each (issued first)
+  uint4 xr[UPL][4];
+#pragma unroll
+  for (int k = 0; k < UPL; k++) {
+    const int u = min(part * SP + lane + 64 * k, S - 1);
+    const uint4* p = reinterpret_cast<const uint4*>(x + 32 * u);
+#pragma unroll
+    for (int c = 0; c < 4; c++) xr[k][c] = p[c];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // (2) every weight load of this wave, group by group
+  uint32_t q[RMAX][UPL][5];
+  int hs[RMAX][UPL], hc[RMAX][UPL], ha[RMAX][UPL];
+  uint32_t rbm[RMAX];  // 2 when the row starts 2 bytes past a dword boundary
+#pragma unroll
+  for (int k = 0; k < UPL; k++) {
+#pragma unroll
+    for (int i = 0; i < RMAX; i++) {
+      const int r = min(row0 + slot + SLOTS * i, row_end - 1);
+      const uint8_t* rb = blocks + static_cast<int64_t>(r) * rowbytes;  // wave-uniform
+      rbm[i] = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(rb) & 3u);
+      hs[i][k] = AFFINE ? *reinterpret_cast<const int32_t*>(rb + hoff[k])
+                        : *reinterpret_cast<const uint16_t*>(rb + hoff[k]);
+      if constexpr (FMT != QBLK_Q4_0) hc[i][k] = *reinterpret_cast<const int8_t*>(rb + coff[k]);
+      if constexpr (AFFINE) ha[i][k] = *reinterpret_cast<const int8_t*>(rb + coff[k] + 8);
+      if constexpr (AFFINE) {
+        const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(rb + off[k]);  // 4-aligned
+        q[i][k][0] = v.x; q[i][k][1] = v.y; q[i][k][2] = v.z; q[i][k][3] = v.w;
+        q[i][k][4] = 0;
+      } else {
+        // dword-aligned start at or below the code bytes; covers [o-2, o+14)
+        const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(rb - rbm[i] + ((off[k] + rbm[i]) & ~3u));
+        q[i][k][0] = v.x; q[i][k][1] = v.y; q[i][k][2] = v.z; q[i][k][3] = v.w;
+        q[i][k][4] = *reinterpret_cast<const uint16_t*>(rb + off[k] + 14);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Nothing may use x before the weight loads above are issued: the empty asm
+  // "redefines" the x registers here (waiting only for the x loads, which went
+  // out first), and everything below reads its outputs.
+#pragma unroll
+  for (int k = 0; k < UPL; k++)
+#pragma unroll
+    for (int c = 0; c < 4; c++)
+      asm volatile("" : "+v"(xr[k][c].x), "+v"(xr[k][c].y), "+v"(xr[k][c].z), "+v"(xr[k][c].w)::"memory");
+
+  // (3) x pairs matching the code words: for word t (bytes 4t..4t+3) the pairs
+  // are (x[4t], x[4t+2]), (x[4t+16], x[4t+18]), (x[4t+1], x[4t+3]),
+  // (x[4t+17], x[4t+19]); Type 1 also needs the unit's sum of x.
+  uint4 X[UPL][4];
+  float sx[UPL];
+  const half2_t kOne = {1.0f16, 1.0f16};
+#pragma unroll
+  for (int k = 0; k < UPL; k++) {
+    const uint32_t* h = reinterpret_cast<const uint32_t*>(xr[k]);  // h[d] = x[2d], x[2d+1]
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      const uint32_t a0 = h[2 * t], a1 = h[2 * t + 1], b0 = h[2 * t + 8], b1 = h[2 * t + 9];
+      X[k][t] = make_uint4(__builtin_amdgcn_perm(a1, a0, 0x05040100u), __builtin_amdgcn_perm(b1, b0, 0x05040100u),
+                           __builtin_amdgcn_perm(a1, a0, 0x07060302u), __builtin_amdgcn_perm(b1, b0, 0x07060302u));
+    }
+    sx[k] = 0.0f;
+    if constexpr (AFFINE) {
+#pragma unroll
+      for (int d = 0; d < 16; d++) sx[k] = __builtin_amdgcn_fdot2(as_h2(h[d]), kOne, sx[k], false);
+    }
+  }
+
+  // (4) products
+  const uint32_t kMagic = 0x64006400u;
+  const half2_t kLo = AFFINE ? half2_t{-1024.0f16, -1024.0f16} : half2_t{-1032.0f16, -1032.0f16};
+  const half2_t kHi = AFFINE ? half2_t{-1024.0f16, -1024.0f16} : half2_t{-1152.0f16, -1152.0f16};
+  float acc[RMAX];
+#pragma unroll
+  for (int i = 0; i < RMAX; i++) acc[i] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < UPL; k++) {
+#pragma unroll
+    for (int i = 0; i < RMAX; i++) {
+      uint32_t c[4];
+      if constexpr (AFFINE) {
+        c[0] = q[i][k][0]; c[1] = q[i][k][1]; c[2] = q[i][k][2]; c[3] = q[i][k][3];
+      } else {
+        const uint32_t a = (off[k] + rbm[i]) & 3u;  // 0 or 2
+        c[0] = __builtin_amdgcn_alignbyte(q[i][k][1], q[i][k][0], a);
+        c[1] = __builtin_amdgcn_alignbyte(q[i][k][2], q[i][k][1], a);
+        c[2] = __builtin_amdgcn_alignbyte(q[i][k][3], q[i][k][2], a);
+        c[3] = __builtin_amdgcn_alignbyte(q[i][k][4], q[i][k][3], a);
+      }
+      float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 4; t++) {
+        const uint32_t b = c[t] >> 8;
+        const half2_t v0 = as_h2(and_or(c[t], 0x000F000Fu, kMagic)) + kLo;
+        const half2_t v1 = as_h2(and_or(c[t], 0x00F000F0u, kMagic)) + kHi;
+        const half2_t v2 = as_h2(and_or(b, 0x000F000Fu, kMagic)) + kLo;
+        const half2_t v3 = as_h2(and_or(b, 0x00F000F0u, kMagic)) + kHi;
+        lo = __builtin_amdgcn_fdot2(v0, as_h2(X[k][t].x), lo, false);
+        hi = __builtin_amdgcn_fdot2(v1, as_h2(X[k][t].y), hi, false);
+        lo = __builtin_amdgcn_fdot2(v2, as_h2(X[k][t].z), lo, false);
+        hi = __builtin_amdgcn_fdot2(v3, as_h2(X[k][t].w), hi, false);
+      }
+      float sc;
+      if constexpr (FMT == QBLK_Q4_0) sc = f16_bits_to_f32(hs[i][k]);
+      else sc = f16_bits_to_f32(hs[i][k] & 0xffff) * static_cast<float>(hc[i][k]);
+      sc = live[k] ? sc : 0.0f;  // lanes past the row's last unit add 0
+      acc[i] = __builtin_fmaf(sc, __builtin_fmaf(hi, 0.0625f, lo), acc[i]);
+      if constexpr (AFFINE) {
+        float oa = f16_bits_to_f32(static_cast<uint32_t>(hs[i][k]) >> 16) * static_cast<float>(ha[i][k]);
+        oa = live[k] ? oa : 0.0f;
+        acc[i] = __builtin_fmaf(oa, sx[k], acc[i]);
+      }
+    }
+  }
+  // (5) one sum per row; lane 63 holds it
+  if constexpr (KS == 1) {
+#pragma unroll
+    for (int i = 0; i < RMAX; i++) {
+      const float v = wave_sum_dpp(acc[i]);
+      const int r = row0 + slot + SLOTS * i;
+      if (lane == kWave - 1 && r < row_end) y[r] = v;
+    }
+  } else {
+    __shared__ float part_sum[kWavesH][RMAX];
+#pragma unroll
+    for (int i = 0; i < RMAX; i++) {
+      const float v = wave_sum_dpp(acc[i]);
+      if (lane == kWave - 1) part_sum[wave][i] = v;
+    }
+    __syncthreads();
+    if (part == 0 && lane == kWave - 1) {
+#pragma unroll
+      for (int i = 0; i < RMAX; i++) {
+        float v = part_sum[wave][i];
+#pragma unroll
+        for (int p = 1; p < KS; p++) v += part_sum[wave + p][i];
+        const int r = row0 + slot + SLOTS * i;
+        if (r < row_end) y[r] = v;
+      }
+    }
+  }
+}
+
+__global__ void k_fill_zero(float* y, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) y[i] = 0.0f;
+}
+
+constexpr int kRows = 4;
+
+template <int FMT, int XT>
+hipError_t launch_t(const void* blocks, int64_t m, int64_t k, const void* x, float* y,
+                    hipStream_t s) {
+  constexpr bool XH = XT == QBLK_F16;
+  constexpr int KC = XH ? kChunkF16 : kChunkF32;
+  const int64_t kc = k < KC ? k : KC;
+  const size_t lds = (XH ? kc * 2 : kc * 4) + (kc / 32) * 4;
+  const int64_t groups = (m + kRows - 1) / kRows;
+  const unsigned grid = static_cast<unsigned>((groups + kWaves - 1) / kWaves);
+  hipLaunchKernelGGL((k_gemv<FMT, XT, kRows>), dim3(grid), dim3(kThreads), lds, s,
+                     static_cast<const uint8_t*>(blocks), x, y, static_cast<int>(m),
+                     static_cast<int>(k));
+  return hipGetLastError();
+}
+
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
+template <int FMT, int RMAX, int UPL, int KS>
+hipError_t launch_h_t(const void* blocks, int64_t m, int64_t k, const void* x, float* y,
+                      int rows_per_wg, hipStream_t s) {
+  const unsigned grid = static_cast<unsigned>((m + rows_per_wg - 1) / rows_per_wg);
+  hipLaunchKernelGGL((k_gemv_h<FMT, RMAX, UPL, KS>), dim3(grid), dim3(kThreadsH), 0, s,
+                     static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
+                     static_cast<int>(m), static_cast<int>(k), rows_per_wg);
+  return hipGetLastError();
+}
+
+// Rows per workgroup: an even share of the rows over the CUs, between one and
+// rmax_cap rounds of `slots` rows.
+inline int rows_per_wg(int64_t m, int slots, int rmax_cap) {
+  int64_t per = (m + cu_count() - 1) / cu_count();
+  per = per < slots ? slots : per;
+  per = per > static_cast<int64_t>(slots) * rmax_cap ? static_cast<int64_t>(slots) * rmax_cap : per;
+  return static_cast<int>(per);
+}
+
+// fp16 x and at most 384 units (12288 weights) per row: the up-front kernel,
+// 2 units per lane (one wave per row) or 3 (two waves per row).
+template <int FMT>
+bool launch_h(const void* blocks, int64_t m, int64_t k, const void* x, float* y, hipStream_t s,
+              hipError_t* err) {
+  const int64_t S = k / 32;
+  if (S > 6 * 64) return false;
+  if (S <= 2 * 64) {
+    const int rpw = rows_per_wg(m, kWavesH, 3);
+    const int rmax = (rpw + kWavesH - 1) / kWavesH;
+    if (rmax == 1) *err = launch_h_t<FMT, 1, 2, 1>(blocks, m, k, x, y, rpw, s);
+    else if (rmax == 2) *err = launch_h_t<FMT, 2, 2, 1>(blocks, m, k, x, y, rpw, s);
+    else *err = launch_h_t<FMT, 3, 2, 1>(blocks, m, k, x, y, rpw, s);
+  } else {
+    const int rpw = rows_per_wg(m, kWavesH / 2, 2);
+    const int rmax = (rpw + kWavesH / 2 - 1) / (kWavesH / 2);
+    if (rmax == 1) *err = launch_h_t<FMT, 1, 3, 2>(blocks, m, k, x, y, rpw, s);
+    else *err = launch_h_t<FMT, 2, 3, 2>(blocks, m, k, x, y, rpw, s);
+  }
+  return true;
+}
+
+template <int FMT>
+hipError_t launch_fmt(const void* blocks, int64_t m, int64_t k, const void* x, int xt, float* y,
+                      hipStream_t s) {
+  hipError_t err = hipSuccess;
+  if (xt == QBLK_F16 && launch_h<FMT>(blocks, m, k, x, y, s, &err)) return err;
+  if (xt == QBLK_F16) return launch_t<FMT, QBLK_F16>(blocks, m, k, x, y, s);
+  if (xt == QBLK_F32) return launch_t<FMT, QBLK_F32>(blocks, m, k, x, y, s);
+  return launch_t<FMT, QBLK_BF16>(blocks, m, k, x, y, s);
+}
+
+}  // namespace
+
+hipError_t launch_gemv(int fmt, const void* blocks, int64_t m, int64_t k, const void* x, int xt,
+                       float* y, hipStream_t s) {
+  if (fmt == QBLK_Q4_0) return launch_fmt<QBLK_Q4_0>(blocks, m, k, x, xt, y, s);
+  if (fmt == QBLK_SB4) return launch_fmt<QBLK_SB4>(blocks, m, k, x, xt, y, s);
+  return launch_fmt<QBLK_SB4_AFFINE>(blocks, m, k, x, xt, y, s);
+}
+
+hipError_t launch_fill_zero(float* y, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_zero, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+                     y, n);
+  return hipGetLastError();
+}
+
+}  // namespace qblk

@@ -1,0 +1,400 @@
+// qblk_quant.hip -- quantization kernels (dense fp32/fp16/bf16 -> packed blocks)
+// and dequantization kernels (packed blocks -> dense fp32/fp16/bf16) for gfx950.
+//
+// A dense row-major matrix and its packed stream are both contiguous, so these
+// kernels work on the flat sequence of blocks: block g covers weights
+// [g*E, (g+1)*E) and bytes [g*B, (g+1)*B).  A workgroup of 256 threads owns
+// 2048 consecutive weights (64 Q4_0 blocks or 8 super-blocks), 8 weights per
+// thread; since 64*18 = 1152, 8*138 = 1104 and 8*148 = 1184 are multiples of
+// 16, each workgroup's slice of the packed stream is 16-byte aligned and is
+// moved between HBM and LDS with 16-byte loads/stores.
+//
+// Definitions followed (field order and the rounding readings are stated in
+// qblk.h):
+//   Q4_0 block ("GGUF 量化内幕 第4章 Q4_0", 4.1.1 absmax/7 scale, 4.1.2 layout,
+//     4.2.1 low nibble = weight j / high nibble = weight j+16, 4.2.2 code+8,
+//     4.3 value = d*(code-8)).
+//   Super-block ("GGUF K-quants" blog, "套娃"): eight sub-block scales stored
+//     as fp16, then quantized to INT8 in [-127, 127] against the fp16
+//     super-scale max/127 (steps 1-4), rebuilt as code*super-scale (step 5).
+#include "qblk_device.h"
+#include "qblk_launch.h"
+
+namespace qblk {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPerThread = 8;
+constexpr int kWgWeights = kThreads * kPerThread;  // 2048
+
+// ------------------------------------------------------------- dense I/O
+template <int DT>
+__device__ __forceinline__ void load8(const void* w, int64_t idx, bool valid, float v[8]) {
+  if (!valid) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = 0.0f;
+    return;
+  }
+  if constexpr (DT == QBLK_F32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(w) + idx);
+    float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(w) + idx);
+    const uint32_t r[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      if constexpr (DT == QBLK_F16) {
+        v[2 * i] = f16_bits_to_f32(r[i] & 0xffffu);
+        v[2 * i + 1] = f16_bits_to_f32(r[i] >> 16);
+      } else {
+        v[2 * i] = bf16_bits_to_f32(r[i] & 0xffffu);
+        v[2 * i + 1] = bf16_bits_to_f32(r[i] >> 16);
+      }
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void store8(void* out, int64_t idx, const float v[8]) {
+  if constexpr (DT == QBLK_F32) {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + idx);
+    p[0] = make_float4(v[0], v[1], v[2], v[3]);
+    p[1] = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    uint32_t r[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      uint32_t a, b;
+      if constexpr (DT == QBLK_F16) {
+        a = f32_to_f16_bits(opaque(v[2 * i]));
+        b = f32_to_f16_bits(opaque(v[2 * i + 1]));
+      } else {
+        a = f32_to_bf16_bits(v[2 * i]);
+        b = f32_to_bf16_bits(v[2 * i + 1]);
+      }
+      r[i] = a | (b << 16);
+    }
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + idx) = make_uint4(r[0], r[1], r[2], r[3]);
+  }
+}
+
+// ------------------------------------------------------ LDS <-> packed stream
+// Copy `nbytes` (even) of the workgroup's packed slice between LDS and global
+// memory.  Whole 16-byte pieces move as uint4, a 2-byte-granular tail as u16.
+__device__ __forceinline__ void lds_to_global(const uint8_t* lds, uint8_t* g, int nbytes) {
+  const int n16 = nbytes >> 4;
+  for (int i = threadIdx.x; i < n16; i += kThreads)
+    reinterpret_cast<uint4*>(g)[i] = reinterpret_cast<const uint4*>(lds)[i];
+  for (int i = (n16 << 3) + threadIdx.x; i < (nbytes >> 1); i += kThreads)
+    reinterpret_cast<uint16_t*>(g)[i] = reinterpret_cast<const uint16_t*>(lds)[i];
+}
+__device__ __forceinline__ void global_to_lds(const uint8_t* g, uint8_t* lds, int nbytes) {
+  const int n16 = nbytes >> 4;
+  for (int i = threadIdx.x; i < n16; i += kThreads)
+    reinterpret_cast<uint4*>(lds)[i] = reinterpret_cast<const uint4*>(g)[i];
+  for (int i = (n16 << 3) + threadIdx.x; i < (nbytes >> 1); i += kThreads)
+    reinterpret_cast<uint16_t*>(lds)[i] = reinterpret_cast<const uint16_t*>(g)[i];
+}
+
+// Nibble packing.  Inside a 32-weight group, thread u (0..3) holds weights
+// 8u..8u+7.  Byte b of the group stores weight b (low nibble) and weight b+16
+// (high nibble), so thread u < 2 combines its codes with those of thread u+2.
+// Returns the 8 bytes 8u..8u+7 (meaningful for u < 2) as two words.
+__device__ __forceinline__ void pack_group(const int n[8], uint32_t& w0, uint32_t& w1) {
+  uint32_t a0 = n[0] | (n[1] << 8) | (n[2] << 16) | (n[3] << 24);
+  uint32_t a1 = n[4] | (n[5] << 8) | (n[6] << 16) | (n[7] << 24);
+  uint32_t b0 = __shfl_xor(a0, 2, kWave);
+  uint32_t b1 = __shfl_xor(a1, 2, kWave);
+  w0 = a0 | (b0 << 4);
+  w1 = a1 | (b1 << 4);
+}
+
+__device__ __forceinline__ void lds_put8(uint8_t* lds, int off, uint32_t w0, uint32_t w1) {
+  uint16_t* p = reinterpret_cast<uint16_t*>(lds + off);  // off is even
+  p[0] = static_cast<uint16_t>(w0);
+  p[1] = static_cast<uint16_t>(w0 >> 16);
+  p[2] = static_cast<uint16_t>(w1);
+  p[3] = static_cast<uint16_t>(w1 >> 16);
+}
+
+// ------------------------------------------------------------- Q4_0 quantize
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_quant_q4_0(const void* __restrict__ w,
+                                                         uint8_t* __restrict__ out,
+                                                         int64_t nblocks) {
+  __shared__ uint4 stage4[64 * 18 / 16];
+  uint8_t* stage = reinterpret_cast<uint8_t*>(stage4);
+  const int t = threadIdx.x;
+  const int64_t blk0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int bl = t >> 2, u = t & 3;
+  const bool valid = blk0 + bl < nblocks;
+  float v[8];
+  load8<DT>(w, (blk0 + bl) * 32 + u * 8, valid, v);
+
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+  amax = group_max<4>(amax);
+  const uint16_t d16 = f32_to_f16_bits(amax / 7.0f);
+  const float d = f16_bits_to_f32(d16);
+  int n[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) n[i] = code_of(v[i], d, -8.0f, 7.0f) + 8;
+  uint32_t w0, w1;
+  pack_group(n, w0, w1);
+  if (valid) {
+    if (u == 0) *reinterpret_cast<uint16_t*>(stage + bl * 18) = d16;
+    if (u < 2) lds_put8(stage, bl * 18 + 2 + 8 * u, w0, w1);
+  }
+  __syncthreads();
+  const int64_t nb = nblocks - blk0 < 64 ? nblocks - blk0 : 64;
+  lds_to_global(stage, out + blk0 * 18, static_cast<int>(nb * 18));
+}
+
+// Q4_0 as the chapter's reference listing computes it (section 4.4): the
+// signed value of largest magnitude (first one on ties) over -8 is the scale,
+// codes min(15, trunc(w * (1/d) + 8.5)) with the fp32 reciprocal.
+__global__ __launch_bounds__(kThreads) void k_quant_q4_0_ref(const float* __restrict__ w,
+                                                             uint8_t* __restrict__ out,
+                                                             int64_t nblocks) {
+  __shared__ uint4 stage4[64 * 18 / 16];
+  uint8_t* stage = reinterpret_cast<uint8_t*>(stage4);
+  const int t = threadIdx.x;
+  const int64_t blk0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int bl = t >> 2, u = t & 3;
+  const bool valid = blk0 + bl < nblocks;
+  float v[8];
+  load8<QBLK_F32>(w, (blk0 + bl) * 32 + u * 8, valid, v);
+  // first element of largest magnitude in weight order: reduce (|v|, -index)
+  float amax = 0.0f, ext = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i++)
+    if (__builtin_fabsf(v[i]) > amax) {
+      amax = __builtin_fabsf(v[i]);
+      ext = v[i];
+    }
+#pragma unroll
+  for (int m = 1; m < 4; m <<= 1) {
+    const float oa = __shfl_xor(amax, m, kWave);
+    const float oe = __shfl_xor(ext, m, kWave);
+    const bool other_first = (u ^ m) < u;  // the partner holds earlier weights
+    if (oa > amax || (oa == amax && other_first && oa != 0.0f)) {
+      amax = oa;
+      ext = oe;
+    }
+  }
+  const float d = ext / -8.0f;
+  const float inv = d != 0.0f ? 1.0f / d : 0.0f;
+  int n[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float s = v[i] * inv + 8.5f;  // separate multiply and add (no contraction)
+    const int c = static_cast<int>(s);
+    n[i] = c < 15 ? c : 15;
+  }
+  uint32_t w0, w1;
+  pack_group(n, w0, w1);
+  if (valid) {
+    if (u == 0) *reinterpret_cast<uint16_t*>(stage + bl * 18) = f32_to_f16_bits(d);
+    if (u < 2) lds_put8(stage, bl * 18 + 2 + 8 * u, w0, w1);
+  }
+  __syncthreads();
+  const int64_t nb = nblocks - blk0 < 64 ? nblocks - blk0 : 64;
+  lds_to_global(stage, out + blk0 * 18, static_cast<int>(nb * 18));
+}
+
+// ---------------------------------------------------------- super-blocks
+// Threads 32*s .. 32*s+31 of the workgroup own super-block s (0..7); thread
+// v = t % 32 holds weights 8v..8v+7, i.e. sub-block j = v/4, part u = v%4.
+template <int DT, bool AFFINE>
+__global__ __launch_bounds__(kThreads) void k_quant_sb4(const void* __restrict__ w,
+                                                        uint8_t* __restrict__ out,
+                                                        int64_t nsb) {
+  constexpr int B = AFFINE ? 148 : 138;
+  __shared__ uint4 stage4[8 * B / 16];
+  uint8_t* stage = reinterpret_cast<uint8_t*>(stage4);
+  const int t = threadIdx.x;
+  const int64_t sb0 = static_cast<int64_t>(blockIdx.x) * 8;
+  const int sl = t >> 5, v = t & 31, j = v >> 2, u = v & 3;
+  const bool valid = sb0 + sl < nsb;
+  float x[8];
+  load8<DT>(w, (sb0 + sl) * 256 + v * 8, valid, x);
+  uint8_t* blk = stage + sl * B;
+  int n[8];
+  if constexpr (!AFFINE) {
+    // first level: a Q4_0 block per sub-block
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+    amax = group_max<4>(amax);
+    const float d = f16_bits_to_f32(f32_to_f16_bits(amax / 7.0f));
+#pragma unroll
+    for (int i = 0; i < 8; i++) n[i] = code_of(x[i], d, -8.0f, 7.0f) + 8;
+    // second level: the eight fp16 scales -> INT8 under one fp16 super-scale
+    float smax = d;
+#pragma unroll
+    for (int m = 4; m < 32; m <<= 1) smax = __builtin_fmaxf(smax, __shfl_xor(smax, m, kWave));
+    const uint16_t S16 = f32_to_f16_bits(smax / 127.0f);
+    const int sc = code_of(d, f16_bits_to_f32(S16), -127.0f, 127.0f);
+    if (valid) {
+      if (v == 0) *reinterpret_cast<uint16_t*>(blk) = S16;
+      if (u == 0) blk[2 + j] = static_cast<uint8_t>(sc);
+    }
+  } else {
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; i++) {
+      mn = __builtin_fminf(mn, x[i]);
+      mx = __builtin_fmaxf(mx, x[i]);
+    }
+    mn = group_min<4>(mn);
+    mx = group_max<4>(mx);
+    const float s = f16_bits_to_f32(f32_to_f16_bits((mx - mn) / 15.0f));
+    const float a = f16_bits_to_f32(f32_to_f16_bits(mn));
+#pragma unroll
+    for (int i = 0; i < 8; i++) n[i] = code_of(x[i] - a, s, 0.0f, 15.0f);
+    float smax = s, amax = __builtin_fabsf(a);
+#pragma unroll
+    for (int m = 4; m < 32; m <<= 1) {
+      smax = __builtin_fmaxf(smax, __shfl_xor(smax, m, kWave));
+      amax = __builtin_fmaxf(amax, __shfl_xor(amax, m, kWave));
+    }
+    const uint16_t Ss16 = f32_to_f16_bits(smax / 127.0f);
+    const uint16_t Sa16 = f32_to_f16_bits(amax / 127.0f);
+    const int sc = code_of(s, f16_bits_to_f32(Ss16), -127.0f, 127.0f);
+    const int ac = code_of(a, f16_bits_to_f32(Sa16), -127.0f, 127.0f);
+    if (valid) {
+      if (v == 0) reinterpret_cast<uint32_t*>(blk)[0] = Ss16 | (static_cast<uint32_t>(Sa16) << 16);
+      if (u == 0) {
+        blk[4 + j] = static_cast<uint8_t>(sc);
+        blk[12 + j] = static_cast<uint8_t>(ac);
+      }
+    }
+  }
+  uint32_t w0, w1;
+  pack_group(n, w0, w1);
+  if (valid && u < 2) lds_put8(stage, sl * B + (AFFINE ? 20 : 10) + 16 * j + 8 * u, w0, w1);
+  __syncthreads();
+  const int64_t ns = nsb - sb0 < 8 ? nsb - sb0 : 8;
+  lds_to_global(stage, out + sb0 * B, static_cast<int>(ns * B));
+}
+
+// ------------------------------------------------------------- dequantize
+// 4-bit code of weight i (0..7 of this thread's 8) from the staged qs bytes of
+// a 32-weight group: threads u = 0,1 take low nibbles of bytes 8u..8u+7,
+// threads u = 2,3 the high nibbles of bytes 8(u-2)..8(u-2)+7.
+__device__ __forceinline__ void group_codes(const uint8_t* qs, int u, int c[8]) {
+  const uint8_t* p = qs + 8 * (u & 1);
+  const int sh = (u >> 1) * 4;
+#pragma unroll
+  for (int i = 0; i < 8; i++) c[i] = (p[i] >> sh) & 0xF;
+}
+
+template <int FMT, int OT>
+__global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict__ blocks,
+                                                      void* __restrict__ out, int64_t nblocks) {
+  constexpr int E = FMT == QBLK_Q4_0 ? 32 : 256;
+  constexpr int B = FMT == QBLK_Q4_0 ? 18 : (FMT == QBLK_SB4 ? 138 : 148);
+  constexpr int PER_WG = kWgWeights / E;  // 64 or 8
+  __shared__ uint4 stage4[PER_WG * B / 16];
+  uint8_t* stage = reinterpret_cast<uint8_t*>(stage4);
+  const int t = threadIdx.x;
+  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * PER_WG;
+  const int64_t ng = nblocks - g0 < PER_WG ? nblocks - g0 : PER_WG;
+  global_to_lds(blocks + g0 * B, stage, static_cast<int>(ng * B));
+  __syncthreads();
+  const int gl = t / (E / 8);  // block of this thread inside the workgroup
+  if (gl >= ng) return;
+  const uint8_t* blk = stage + gl * B;
+  const int u = t & 3;
+  int c[8];
+  float y[8];
+  if constexpr (FMT == QBLK_Q4_0) {
+    const float d = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(blk));
+    group_codes(blk + 2, u, c);
+#pragma unroll
+    for (int i = 0; i < 8; i++) y[i] = d * static_cast<float>(c[i] - 8);
+  } else if constexpr (FMT == QBLK_SB4) {
+    const int j = (t & 31) >> 2;
+    const float S = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(blk));
+    const float sj = S * static_cast<float>(static_cast<int8_t>(blk[2 + j]));
+    group_codes(blk + 10 + 16 * j, u, c);
+#pragma unroll
+    for (int i = 0; i < 8; i++) y[i] = sj * static_cast<float>(c[i] - 8);
+  } else {
+    const int j = (t & 31) >> 2;
+    const uint32_t hdr = *reinterpret_cast<const uint32_t*>(blk);
+    const float sj = f16_bits_to_f32(hdr & 0xffffu) * static_cast<float>(static_cast<int8_t>(blk[4 + j]));
+    const float aj = f16_bits_to_f32(hdr >> 16) * static_cast<float>(static_cast<int8_t>(blk[12 + j]));
+    group_codes(blk + 20 + 16 * j, u, c);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const float p = sj * static_cast<float>(c[i]);
+      y[i] = p + aj;
+    }
+  }
+  store8<OT>(out, (g0 + gl) * E + (t % (E / 8)) * 8, y);
+}
+
+inline unsigned grid_for(int64_t weights) {
+  return static_cast<unsigned>((weights + kWgWeights - 1) / kWgWeights);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------- launchers
+hipError_t launch_quantize_q4_0(const void* w, int wt, int64_t rows, int64_t k, void* blocks,
+                                hipStream_t s) {
+  const int64_t nb = rows * k / 32;
+  const unsigned g = grid_for(rows * k);
+  uint8_t* out = static_cast<uint8_t*>(blocks);
+  if (wt == QBLK_F32) hipLaunchKernelGGL(k_quant_q4_0<QBLK_F32>, dim3(g), dim3(kThreads), 0, s, w, out, nb);
+  else if (wt == QBLK_F16) hipLaunchKernelGGL(k_quant_q4_0<QBLK_F16>, dim3(g), dim3(kThreads), 0, s, w, out, nb);
+  else hipLaunchKernelGGL(k_quant_q4_0<QBLK_BF16>, dim3(g), dim3(kThreads), 0, s, w, out, nb);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_q4_0_ref(const float* w, int64_t rows, int64_t k, void* blocks,
+                                    hipStream_t s) {
+  hipLaunchKernelGGL(k_quant_q4_0_ref, dim3(grid_for(rows * k)), dim3(kThreads), 0, s, w,
+                     static_cast<uint8_t*>(blocks), rows * k / 32);
+  return hipGetLastError();
+}
+
+template <bool A>
+static void launch_sb4_t(const void* w, int wt, int64_t nsb, uint8_t* out, hipStream_t s) {
+  const unsigned g = static_cast<unsigned>((nsb + 7) / 8);
+  if (wt == QBLK_F32) hipLaunchKernelGGL((k_quant_sb4<QBLK_F32, A>), dim3(g), dim3(kThreads), 0, s, w, out, nsb);
+  else if (wt == QBLK_F16) hipLaunchKernelGGL((k_quant_sb4<QBLK_F16, A>), dim3(g), dim3(kThreads), 0, s, w, out, nsb);
+  else hipLaunchKernelGGL((k_quant_sb4<QBLK_BF16, A>), dim3(g), dim3(kThreads), 0, s, w, out, nsb);
+}
+
+hipError_t launch_quantize_sb4(const void* w, int wt, int64_t rows, int64_t k, int affine,
+                               void* blocks, hipStream_t s) {
+  const int64_t nsb = rows * k / 256;
+  uint8_t* out = static_cast<uint8_t*>(blocks);
+  if (affine) launch_sb4_t<true>(w, wt, nsb, out, s);
+  else launch_sb4_t<false>(w, wt, nsb, out, s);
+  return hipGetLastError();
+}
+
+template <int FMT>
+static void launch_deq_t(const uint8_t* b, int64_t nblk, void* out, int ot, unsigned g, hipStream_t s) {
+  if (ot == QBLK_F32) hipLaunchKernelGGL((k_dequant<FMT, QBLK_F32>), dim3(g), dim3(kThreads), 0, s, b, out, nblk);
+  else if (ot == QBLK_F16) hipLaunchKernelGGL((k_dequant<FMT, QBLK_F16>), dim3(g), dim3(kThreads), 0, s, b, out, nblk);
+  else hipLaunchKernelGGL((k_dequant<FMT, QBLK_BF16>), dim3(g), dim3(kThreads), 0, s, b, out, nblk);
+}
+
+hipError_t launch_dequant(int fmt, const void* blocks, int64_t rows, int64_t k, void* out, int ot,
+                          hipStream_t s) {
+  const uint8_t* b = static_cast<const uint8_t*>(blocks);
+  const unsigned g = grid_for(rows * k);
+  if (fmt == QBLK_Q4_0) launch_deq_t<QBLK_Q4_0>(b, rows * k / 32, out, ot, g, s);
+  else if (fmt == QBLK_SB4) launch_deq_t<QBLK_SB4>(b, rows * k / 256, out, ot, g, s);
+  else launch_deq_t<QBLK_SB4_AFFINE>(b, rows * k / 256, out, ot, g, s);
+  return hipGetLastError();
+}
+
+}  // namespace qblk

@@ -1,0 +1,290 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Quantization and dequantization must match the oracle bit for bit; products
+must satisfy |y - y_ref| <= 2e-5 * sum_k |W[i,k] x[k]| element by element
+against the oracle's fp64 sums.  Inputs come from the seeded generators in
+workloads/ (the configs' shapes and distributions) plus hand-made edge cases.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as WL
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-5
+FMTS = [O.Q4_0, O.SB4, O.SB4_AFFINE]
+NAMES = {O.Q4_0: "q4_0", O.SB4: "sb4", O.SB4_AFFINE: "sb4a"}
+
+
+@pytest.fixture(scope="module")
+def q():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_block_quant_amd as q
+    return q
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def dev_bf16(bits):
+    return dev(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def gpu_input(w, dtype):
+    """Host f32 matrix -> (device tensor of dtype, host array the oracle reads)."""
+    if dtype == "f32":
+        return dev(w), w
+    if dtype == "f16":
+        h = w.astype(np.float16)
+        return dev(h), h
+    bits = WL.bf16_bits(w)
+    return dev_bf16(bits), (bits, O.BF16)
+
+
+def mixed_blocks(rows, k, seed):
+    """Rows of several flavours (the edge cases of the formats)."""
+    rng = np.random.default_rng(seed)
+    w = np.empty((rows, k), np.float32)
+    for r in range(rows):
+        kind = r % 8
+        if kind == 0:
+            w[r] = rng.standard_normal(k) * 0.02
+        elif kind == 1:
+            w[r] = rng.standard_t(2, k) * 0.05
+        elif kind == 2:  # exact half steps: ties of the rounding rule
+            w[r] = (rng.integers(-15, 16, k) / 2.0) * 2.0 ** -6
+            w[r, ::32] = 7 * 2.0 ** -6
+        elif kind == 3:
+            w[r] = rng.standard_normal(k) * 1e-6  # fp16-subnormal scales
+        elif kind == 4:
+            w[r] = 0.0
+        elif kind == 5:  # constant sub-blocks and zeros
+            w[r] = np.repeat(rng.standard_normal(k // 32), 32) * 0.01
+            w[r, 64:128] = 0.0
+        elif kind == 6:  # one outlier per 32 (the Q4_0 chapter's failure mode)
+            w[r] = rng.uniform(-0.01, 0.01, k)
+            w[r, 31::32] = 10.0
+        else:
+            w[r] = rng.standard_normal(k) * np.exp(rng.uniform(np.log(0.005), np.log(0.05)))
+    return w
+
+
+def near_ties(rows, k, seed):
+    """Weights one fp32 ulp either side of a rounding tie of their block's quotient."""
+    rng = np.random.default_rng(seed)
+    w = (rng.integers(-14, 15, (rows, k)) / 2.0).astype(np.float32)
+    w[:, ::32] = 7.0  # fixes each 32-block's scale at exactly 1.0
+    flip = rng.integers(-1, 2, (rows, k)).astype(np.float32)
+    w = np.where(flip > 0, np.nextafter(w, np.float32(np.inf)),
+                 np.where(flip < 0, np.nextafter(w, np.float32(-np.inf)), w)).astype(np.float32)
+    return w * np.float32(2.0 ** -8)
+
+
+# ----------------------------------------------------------------- quantize
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: NAMES[f])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_quantize_bit_exact(q, fmt, dtype):
+    # 7 x 2304: 63 super-blocks (7 workgroups + a ragged tail) or 504 Q4_0 blocks
+    for w in (mixed_blocks(16, 2304, 1), near_ties(7, 2304, 2)):
+        d, h = gpu_input(w, dtype)
+        got = host(q.quantize(d, fmt))
+        ref = O.quantize(fmt, h)
+        assert got.shape == ref.shape
+        assert np.array_equal(got, ref), f"first mismatch at byte {np.argmax(got != ref)}"
+
+
+def test_quantize_extreme_f16_inputs(q):
+    w = np.full((2, 256), 65504.0, np.float16)
+    w[0, ::2] = -65504.0
+    w[1, :] = np.float16(6e-8)  # fp16 subnormal weights
+    for fmt in FMTS:
+        got = host(q.quantize(dev(w), fmt))
+        assert np.array_equal(got, O.quantize(fmt, w)), NAMES[fmt]
+
+
+def test_quantize_q4_0_reference_mode(q):
+    w = mixed_blocks(8, 4096, 3)
+    vals = np.array([0.01 * (i - 15) / 15 for i in range(31)] + [10.0], np.float32)
+    w[0, :32] = vals
+    got = host(q.quantize(dev(w), q.Q4_0, ref=True))
+    assert np.array_equal(got, O.quantize_q4_0_ref(w))
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: NAMES[f])
+def test_quantize_full_size(q, fmt):
+    w, _ = WL.sb4_decode("up") if fmt != O.Q4_0 else WL.q4_0_decode()
+    got = host(q.quantize(dev(w), fmt))
+    assert np.array_equal(got, O.quantize(fmt, w))
+
+
+def test_quantize_stack_matrix_f16(q):
+    for p in (0, 6):  # q (4096 x 4096) and down (4096 x 11008) of layer 0
+        w, _ = WL.sb4a_stack_matrix(0, p)
+        got = host(q.quantize(dev(w), q.SB4_AFFINE))
+        assert np.array_equal(got, O.quantize_sb4(w, affine=True))
+
+
+# ------------------------------------------------------------------ dequant
+def random_blocks(fmt, nblk, seed):
+    """Arbitrary bytes with finite fp16 scales."""
+    rng = np.random.default_rng(seed)
+    nb = O.block_bytes(fmt)
+    b = rng.integers(0, 256, (nblk, nb), dtype=np.uint8)
+    nscale = 1 if fmt != O.SB4_AFFINE else 2
+    s = rng.integers(0, 0x7C00, (nblk, nscale)).astype(np.uint16)  # finite, incl. subnormal
+    s |= (rng.integers(0, 2, (nblk, nscale)) << 15).astype(np.uint16)
+    b[:, : 2 * nscale] = s.view(np.uint8).reshape(nblk, 2 * nscale)
+    return b.reshape(-1)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: NAMES[f])
+@pytest.mark.parametrize("ot", ["f32", "f16", "bf16"])
+def test_dequant_bit_exact(q, fmt, ot):
+    E = O.block_elems(fmt)
+    rows, k = 5, E * 13  # ragged tail of the 2048-weight workgroups
+    for blocks in (random_blocks(fmt, rows * k // E, 4),
+                   O.quantize(fmt, mixed_blocks(rows, k, 5))):
+        dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[ot]
+        got = q.dequant(dev(blocks), fmt, rows, k, dt)
+        ref = O.dequant(fmt, blocks, rows, k)
+        if ot == "f32":
+            assert np.array_equal(host(got).view(np.uint32), ref.view(np.uint32))
+        elif ot == "f16":
+            assert np.array_equal(host(got).view(np.uint16), ref.astype(np.float16).view(np.uint16))
+        else:
+            refb = torch.from_numpy(ref).to(torch.bfloat16).view(torch.int16).numpy()
+            assert np.array_equal(host(got.view(torch.int16)), refb)
+
+
+# --------------------------------------------------------------------- GEMV
+def check_products(y, y_ref, bound, what):
+    err = np.abs(y.astype(np.float64) - y_ref)
+    ok = err <= TOL * bound
+    assert ok.all(), f"{what}: {np.count_nonzero(~ok)} outputs out of tolerance, worst ratio {np.max(err / np.maximum(bound, 1e-300)):.3e}"
+    zero = bound == 0
+    assert np.all(y[zero] == 0), f"{what}: an all-zero product is not exactly 0"
+
+
+def x_dev(x):
+    if x.dtype == np.uint16:  # bf16 bits
+        return dev_bf16(x), WL.bf16_values(x)
+    return dev(x), x.astype(np.float64)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: NAMES[f])
+@pytest.mark.parametrize("xt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 256), (37, 2304), (130, 11008)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_gemv_tolerance(q, fmt, xt, shape):
+    m, k = shape
+    w = mixed_blocks(m, k, 7 + m)
+    blocks = O.quantize(fmt, w)
+    xs = np.random.default_rng(8).standard_normal(k).astype(np.float32)
+    x = {"f32": xs, "f16": xs.astype(np.float16), "bf16": WL.bf16_bits(xs)}[xt]
+    xd, xr = x_dev(x)
+    y = host(q.gemv(dev(blocks), fmt, m, k, xd))
+    y_ref, bound = O.gemv(fmt, blocks, m, k, xr)
+    check_products(y, y_ref, bound, f"{NAMES[fmt]} {xt} {shape}")
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: NAMES[f])
+@pytest.mark.parametrize("xt", ["f32", "f16"])
+def test_gemv_unit_vector_is_a_column(q, fmt, xt):
+    m, k = 70, 2048
+    blocks = O.quantize(fmt, mixed_blocks(m, k, 9))
+    W = O.dequant(fmt, blocks, m, k)
+    bd = dev(blocks)
+    for col in (0, 17, 1000, k - 1):
+        x = np.zeros(k, np.float32 if xt == "f32" else np.float16)
+        x[col] = 1
+        y = host(q.gemv(bd, fmt, m, k, dev(x)))
+        # exact values; a rebuilt weight of -0.0 (INT8 scale 0, code < 8) sums to +0.0
+        assert np.array_equal(y, W[:, col]), col
+
+
+def test_gemv_q4_0_small_config(q):
+    w, x = WL.q4_0_small()
+    b = q.quantize(dev(w), q.Q4_0)
+    assert np.array_equal(host(b), O.quantize_q4_0(w))
+    y = host(q.gemv(b, q.Q4_0, 256, 4096, dev(x)))
+    y_ref, bound = O.gemv(O.Q4_0, O.quantize_q4_0(w), 256, 4096, x)
+    check_products(y, y_ref, bound, "q4_0 256x4096 f32")
+
+
+def test_gemv_q4_0_decode_config(q):
+    w, x = WL.q4_0_decode()
+    blocks = O.quantize_q4_0(w)
+    y = host(q.gemv(dev(blocks), q.Q4_0, 4096, 4096, dev(x)))
+    y_ref, bound = O.gemv(O.Q4_0, blocks, 4096, 4096, x.astype(np.float64))
+    check_products(y, y_ref, bound, "q4_0 4096x4096 f16")
+
+
+@pytest.mark.parametrize("shape", ["up", "down"])
+def test_gemv_sb4_decode_config(q, shape):
+    w, x = WL.sb4_decode(shape)
+    m, k = w.shape
+    blocks = O.quantize_sb4(w)
+    y = host(q.gemv(dev(blocks), q.SB4, m, k, dev(x)))
+    y_ref, bound = O.gemv(O.SB4, blocks, m, k, x.astype(np.float64))
+    check_products(y, y_ref, bound, f"sb4 {m}x{k} f16")
+
+
+def test_gemv_stack_matrices(q):
+    for layer, p in ((0, 0), (0, 4), (31, 6)):
+        w, x = WL.sb4a_stack_matrix(layer, p)
+        m, k = w.shape
+        blocks = O.quantize_sb4(w, affine=True)
+        y = host(q.gemv(dev(blocks), q.SB4_AFFINE, m, k, dev(x)))
+        y_ref, bound = O.gemv(O.SB4_AFFINE, blocks, m, k, x.astype(np.float64))
+        check_products(y, y_ref, bound, f"sb4a layer {layer} proj {p}")
+
+
+def test_gemv_empty_k_writes_zeros(q):
+    y = torch.full((33,), 7.0, device="cuda")
+    q.gemv(torch.empty(0, dtype=torch.uint8, device="cuda"), q.SB4, 33, 0,
+           torch.empty(0, dtype=torch.float16, device="cuda"), out=y)
+    assert np.all(host(y) == 0)
+
+
+def test_misaligned_pointer_is_rejected(q):
+    b = torch.zeros(1024, dtype=torch.uint8, device="cuda")
+    x = torch.zeros(256, dtype=torch.float16, device="cuda")
+    with pytest.raises(q.QblkError) as e:
+        q.gemv(b[2:], q.SB4, 1, 256, x)
+    assert e.value.status == 4
+
+
+# --------------------------------------------------------------------- GEMM
+@pytest.mark.parametrize("n", [1, 5, 16, 33, 64, 100])
+def test_gemm_tolerance_small(q, n):
+    m, k = 150, 2304
+    w = mixed_blocks(m, k, 11)
+    blocks = O.quantize_sb4(w)
+    X = WL.bf16_bits(np.random.default_rng(12).standard_normal((n, k)).astype(np.float32))
+    Y = host(q.gemm(dev(blocks), q.SB4, m, k, dev_bf16(X)))
+    Y_ref, B = O.gemm(O.SB4, blocks, m, k, WL.bf16_values(X).astype(np.float64))
+    check_products(Y, Y_ref, B, f"gemm n={n}")
+
+
+@pytest.mark.parametrize("shape", ["up", "down"])
+@pytest.mark.parametrize("n", [16, 64, 512])
+def test_gemm_prefill_config(q, shape, n):
+    w, X = WL.sb4_prefill(shape, n)
+    m, k = w.shape
+    blocks = O.quantize_sb4(w)
+    bd = q.quantize(dev(w), q.SB4)
+    assert np.array_equal(host(bd), blocks)
+    Y = host(q.gemm(bd, q.SB4, m, k, dev_bf16(X)))
+    rows = np.random.default_rng(n).choice(m, size=64 if n == 512 else 256, replace=False)
+    rows = np.concatenate([rows, [0, m - 1]])
+    Y_ref, B = O.gemm(O.SB4, blocks, m, k, WL.bf16_values(X).astype(np.float64), rows=rows)
+    check_products(Y[:, rows], Y_ref, B, f"gemm {shape} n={n}")
