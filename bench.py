@@ -92,6 +92,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=200, help="untimed GEMV launches")
     ap.add_argument("--rows", type=int, default=1, help="1: also time the other hot-path steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget (0: skip)")
+    ap.add_argument("--mode", choices=("full", "traffic"), default="full",
+                    help="traffic: a 256 MiB device copy (counter calibration) then a few "
+                         "headline GEMV launches, for rocprofv3 --pmc runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -109,6 +112,10 @@ def main():
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
     dev = torch.device("cuda:0")
+
+    if args.mode == "traffic":
+        traffic_run(torch, q, WL, dev)
+        return
 
     # ------------------------------------------------------------ headline
     w, x = WL.sb4_decode("up")
@@ -176,6 +183,34 @@ def main():
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(np, WL, w, x, algo_bytes, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+# ------------------------------------------------------- counter calibration
+CALIB_BYTES = 256 << 20
+
+
+def traffic_run(torch, q, WL, dev):
+    """A known-size streaming kernel (fp32 multiply: reads and writes
+    CALIB_BYTES once each), then 8 GEMV launches on distinct copies of the
+    headline blocks."""
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    w, x = WL.sb4_decode("up")
+    M, K = w.shape
+    b0 = q.quantize(torch.from_numpy(w).to(dev), q.SB4)
+    C = n_copies(b0.numel())
+    cps = [b0] + [b0.clone() for _ in range(C - 1)]
+    xd = torch.from_numpy(x).to(dev)
+    y = torch.empty(M, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    for i in range(8):
+        q.gemv(cps[(i + 1) % C], q.SB4, M, K, xd, out=y)
+    torch.cuda.synchronize()
+    log("traffic run done")
 
 
 # ----------------------------------------------------------------- other rows
