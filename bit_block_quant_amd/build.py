@@ -11,6 +11,7 @@ hipcc cross-compiles for gfx950 without a GPU present.  Flags:
                                keep fp32 denormals (fp16 denormals are kept by
                                the default mode; super-scales can be subnormal)
   -packed-fp32-ops (disabled)  no packed-fp32 instructions in generated code
+  -amdgpu-mfma-vgpr-form       MFMA results written to VGPRs, not AGPRs
 """
 import os
 import subprocess
@@ -28,6 +29,8 @@ FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs (the GEMM scales every partial product on the VALU)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -6,23 +6,29 @@
 // Q4_0" 4.2.2).
 //
 // One v_mfma_f32_16x16x32_bf16 spans K = 32, exactly one sub-block, so the
-// weight operand holds the exact integers (code - 8) in bf16 and the
-// sub-block's fp32 scale S*sc_j multiplies each 16x16 partial product before
-// it is added to the fp32 accumulator.  (Rounding the scaled weights to bf16
-// instead would break the 2e-5 relative error bound.)
+// weight operand holds the exact integers (code - 8)/16 in bf16 and the
+// sub-block's fp32 scale 16*S*sc_j multiplies each 16x16 partial product
+// before it is added to the fp32 accumulator.  (Rounding the scaled weights
+// to bf16 instead would break the 2e-5 relative error bound.)  The codes are
+// widened with v_cvt_off_f32_i4 (a 4-bit two's-complement field / 16; code
+// XOR 8 is exactly code - 8 in that form), selecting bytes with SDWA, and
+// packed with v_cvt_pk_bf16_f32 (exact: at most 4 significant bits).
 //
 // Operand layout of the 16x16x32 MFMA: lane l holds row (l % 16) of A and
-// column (l % 16) of B, each with 8 consecutive-in-register k values of the
-// k-group (l / 16); lane l receives D[4*(l/16) + r][l % 16], r = 0..3.  Only
-// A and B having the same k assignment matters, so lane group g takes the
-// codes of qs bytes 4g..4g+3 of the sub-block -- weights 4g..4g+3 (low
-// nibbles) and 4g+16..4g+19 (high nibbles) -- and the same eight X entries.
+// column (l % 16) of B, each with 8 k values of the k-group (l / 16); lane l
+// receives D[4*(l/16) + r][l % 16], r = 0..3.  Only A and B having the same k
+// assignment matters, so lane group g takes the codes of qs bytes 4g..4g+3 of
+// the sub-block -- weights 4g..4g+3 (low nibbles) and 4g+16..4g+19 (high
+// nibbles) -- and the same eight X entries.
 //
 // Tiling: A = X (16 tokens per tile), B = W^T (16 weight rows per tile), so a
 // lane's outputs share one weight row and one scale.  A workgroup of 4 waves
-// owns 64*TM weight rows (16*TM per wave) and 16*TN tokens; the X tile of the
-// current super-block (16*TN x 256 bf16) is staged in LDS once and read by all
-// four waves; weight codes go from HBM straight to registers.
+// owns 64*TM weight rows (16*TM per wave) and 16*TN tokens.  Per super-block
+// (256 k) the X tile (16*TN x 256 bf16) is double-buffered in LDS (one barrier
+// per super-block) and the next super-block's codes and header are fetched
+// into registers while the current one is multiplied.  When the M x N tiling
+// leaves too few workgroups for the GPU, the K range is split over a third
+// grid dimension and the partial products are added into Y (zeroed first).
 #include "qblk_device.h"
 #include "qblk_launch.h"
 
@@ -30,41 +36,101 @@ namespace qblk {
 namespace {
 
 typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
-constexpr int kLdsRow = 256 + 8;  // bf16 per staged X row (+16 B pad against bank conflicts)
+// A staged X row holds one super-block (256 bf16) in MFMA order: for sub-block
+// j and k-group g, the 8 entries 32j+4g..+3 and 32j+16+4g..+3 sit together at
+// 32j+8g, so a lane's A operand is one 16-byte LDS read.  Rows are padded by
+// 16 bf16 (8 dwords) so that 16 rows read at the same column fall in
+// different banks.
+constexpr int kLdsRow = 256 + 16;
 
-__device__ __forceinline__ uint32_t pack_bf16_ints(float a, float b) {
-  // a, b are small integers: their bf16 patterns are the upper halves exactly
-  return (__builtin_bit_cast(uint32_t, a) >> 16) | (__builtin_bit_cast(uint32_t, b) & 0xffff0000u);
+template <int BYTE>
+__device__ __forceinline__ float off_i4(uint32_t v) {
+  float r;
+  if constexpr (BYTE == 0)
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(v));
+  else if constexpr (BYTE == 1)
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(v));
+  else if constexpr (BYTE == 2)
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(v));
+  else
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(v));
+  return r;
 }
 
-// (code - 8) of weights 4g..4g+3 and 4g+16..4g+19 as 8 bf16 values.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2v_t));
+}
+
+// (code - 8)/16 of weights 4g..4g+3 and 4g+16..4g+19 as 8 bf16 values.
 __device__ __forceinline__ bf16x8v_t decode_codes(uint32_t q) {
-  float lo[4], hi[4];
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    lo[i] = static_cast<float>((q >> (8 * i)) & 0xFu) - 8.0f;
-    hi[i] = static_cast<float>((q >> (8 * i + 4)) & 0xFu) - 8.0f;
-  }
-  const uint4 w = make_uint4(pack_bf16_ints(lo[0], lo[1]), pack_bf16_ints(lo[2], lo[3]),
-                             pack_bf16_ints(hi[0], hi[1]), pack_bf16_ints(hi[2], hi[3]));
+  const uint32_t lo = q ^ 0x88888888u;  // each nibble n -> n XOR 8, a 4-bit field worth n-8
+  const uint32_t hi = lo >> 4;           // high nibbles moved into the low half of each byte
+  const uint4 w = make_uint4(pk_bf16(off_i4<0>(lo), off_i4<1>(lo)), pk_bf16(off_i4<2>(lo), off_i4<3>(lo)),
+                             pk_bf16(off_i4<0>(hi), off_i4<1>(hi)), pk_bf16(off_i4<2>(hi), off_i4<3>(hi)));
   return __builtin_bit_cast(bf16x8v_t, w);
 }
 
-template <int TM, int TN>
+// The registers a lane needs from one super-block of one weight row:
+// the 8 code dwords of its k-group (one per sub-block) and the header.
+struct SbRegs {
+  uint32_t code[8];
+  float scale[8];  // 16 * S * sc_j
+};
+
+constexpr int kRaw = 3 + 16;  // header dwords + two u16 per sub-block
+
+__device__ __forceinline__ void load_sb(const uint8_t* p, int g, uint32_t raw[kRaw]) {
+  // header: dword-aligned 12 bytes covering the 10 header bytes (all inside
+  // the super-block: [p-2, p+10) or [p, p+12))
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const u32x3_a4 h = *reinterpret_cast<const u32x3_a4*>(a & ~uintptr_t(3));
+  raw[0] = h.x;
+  raw[1] = h.y;
+  raw[2] = h.z;
+  // code bytes 4g..4g+3 of each sub-block (2-byte aligned): two u16 each
+#pragma unroll
+  for (int s = 0; s < 8; s++) {
+    const uint8_t* o = p + 10 + 16 * s + 4 * g;
+    raw[3 + 2 * s] = load_u16(o);
+    raw[4 + 2 * s] = load_u16(o + 2);
+  }
+}
+
+__device__ __forceinline__ void finish_sb(const uint8_t* p, const uint32_t raw[kRaw], SbRegs& r) {
+  const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
+  const uint32_t w0 = __builtin_amdgcn_alignbyte(raw[1], raw[0], sh);  // S16, sc0, sc1
+  const uint32_t w1 = __builtin_amdgcn_alignbyte(raw[2], raw[1], sh);  // sc2..sc5
+  const uint32_t w2 = raw[2] >> (8 * sh);                              // sc6, sc7
+  const float S16 = f16_bits_to_f32(w0 & 0xffffu) * 16.0f;
+  const uint32_t sc03 = (w0 >> 16) | (w1 << 16), sc47 = (w1 >> 16) | (w2 << 16);
+#pragma unroll
+  for (int s = 0; s < 8; s++) {
+    r.code[s] = raw[3 + 2 * s] | (raw[4 + 2 * s] << 16);
+    const uint32_t word = s < 4 ? sc03 : sc47;
+    const int8_t c = static_cast<int8_t>((word >> (8 * (s & 3))) & 0xffu);
+    r.scale[s] = S16 * static_cast<float>(c);
+  }
+}
+
+template <int TM, int TN, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void k_gemm_sb4(const uint8_t* __restrict__ W,
                                                        const uint16_t* __restrict__ X,
-                                                       float* __restrict__ Y, int M, int K,
-                                                       int N) {
+                                                       float* __restrict__ Y, int M, int K, int N,
+                                                       int sb_per_split) {
   constexpr int NT = 16 * TN;
-  __shared__ uint4 xs4[NT * kLdsRow / 8];
-  uint16_t* xs = reinterpret_cast<uint16_t*>(xs4);
+  __shared__ uint4 xs4[2][NT * kLdsRow / 8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t mw = static_cast<int64_t>(blockIdx.x) * 64 * TM + wave * 16 * TM;
   const int n0 = blockIdx.y * NT;
-  const int64_t rowbytes = static_cast<int64_t>(K / 256) * 138;
+  const int nsb = K / 256;
+  const int b_begin = SPLIT ? blockIdx.z * sb_per_split : 0;
+  const int b_end = SPLIT ? min(nsb, b_begin + sb_per_split) : nsb;
+  const int64_t rowbytes = static_cast<int64_t>(nsb) * 138;
   const uint8_t* rowp[TM];
 #pragma unroll
   for (int tm = 0; tm < TM; tm++) {
@@ -72,6 +138,36 @@ __global__ __launch_bounds__(kThreads) void k_gemm_sb4(const uint8_t* __restrict
     m = m < M ? m : M - 1;
     rowp[tm] = W + m * rowbytes;
   }
+
+  // X tile staging: thread t moves uint4 c = t, t+256, ... of the NT x 256 tile
+  auto load_x = [&](int b, uint4 xv[(NT * 32 + kThreads - 1) / kThreads]) {
+#pragma unroll
+    for (int i = 0; i < (NT * 32 + kThreads - 1) / kThreads; i++) {
+      const int c = threadIdx.x + i * kThreads;
+      const int r = c >> 5, col = c & 31;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (c < NT * 32 && n0 + r < N)
+        v = *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(n0 + r) * K + 256 * b + 8 * col);
+      xv[i] = v;
+    }
+  };
+  auto store_x = [&](int buf, const uint4 xv[(NT * 32 + kThreads - 1) / kThreads]) {
+    uint16_t* xs = reinterpret_cast<uint16_t*>(xs4[buf]);
+#pragma unroll
+    for (int i = 0; i < (NT * 32 + kThreads - 1) / kThreads; i++) {
+      const int c = threadIdx.x + i * kThreads;
+      if (c < NT * 32) {
+        // entries 8cc..8cc+7 of sub-block j: the first half of k-groups 2cc and
+        // 2cc+1 (cc < 2) or the second half of k-groups 2cc-4, 2cc-3 (cc >= 2)
+        const int j = (c & 31) >> 2, cc = c & 3;
+        const int g0 = 2 * (cc & 1), half = cc >> 1;
+        uint16_t* row = xs + (c >> 5) * kLdsRow + 32 * j + 4 * half;
+        *reinterpret_cast<uint2*>(row + 8 * g0) = make_uint2(xv[i].x, xv[i].y);
+        *reinterpret_cast<uint2*>(row + 8 * (g0 + 1)) = make_uint2(xv[i].z, xv[i].w);
+      }
+    }
+  };
+
   float4_t acc[TM][TN];
 #pragma unroll
   for (int tm = 0; tm < TM; tm++)
@@ -79,62 +175,63 @@ __global__ __launch_bounds__(kThreads) void k_gemm_sb4(const uint8_t* __restrict
     for (int tn = 0; tn < TN; tn++) acc[tm][tn] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int nsb = K / 256;
-  for (int b = 0; b < nsb; b++) {
-    __syncthreads();
-    for (int i = threadIdx.x; i < NT * 32; i += kThreads) {
-      const int r = i >> 5, c = i & 31;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (n0 + r < N) v = *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(n0 + r) * K + 256 * b + 8 * c);
-      *reinterpret_cast<uint4*>(xs + r * kLdsRow + 8 * c) = v;
-    }
-    __syncthreads();
-    // super-block header of each of this lane's weight rows
-    float S[TM];
-    uint32_t scw[TM][2];  // sc_0..sc_7 as bytes
+  uint4 xv[(NT * 32 + kThreads - 1) / kThreads];
+  uint32_t raw[TM][kRaw];
+  SbRegs cur[TM];
+  if (b_begin < b_end) {
+    load_x(b_begin, xv);
 #pragma unroll
-    for (int tm = 0; tm < TM; tm++) {
-      const uint8_t* p = rowp[tm] + static_cast<int64_t>(b) * 138;
-      const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-      const u32x3_a4 h = *reinterpret_cast<const u32x3_a4*>(a & ~uintptr_t(3));
-      const uint32_t sh = static_cast<uint32_t>(a & 3u);
-      const uint32_t w0 = __builtin_amdgcn_alignbyte(h.y, h.x, sh);  // S16, sc0, sc1
-      const uint32_t w1 = __builtin_amdgcn_alignbyte(h.z, h.y, sh);  // sc2..sc5
-      const uint32_t w2 = h.z >> (8 * sh);                           // sc6, sc7
-      S[tm] = f16_bits_to_f32(w0 & 0xffffu);
-      scw[tm][0] = (w0 >> 16) | (w1 << 16);  // sc0..sc3
-      scw[tm][1] = (w1 >> 16) | (w2 << 16);  // sc4..sc7
+    for (int tm = 0; tm < TM; tm++) load_sb(rowp[tm] + static_cast<int64_t>(b_begin) * 138, g, raw[tm]);
+    store_x(0, xv);
+#pragma unroll
+    for (int tm = 0; tm < TM; tm++) finish_sb(rowp[tm] + static_cast<int64_t>(b_begin) * 138, raw[tm], cur[tm]);
+  }
+
+  for (int b = b_begin; b < b_end; b++) {
+    const int buf = (b - b_begin) & 1;
+    __syncthreads();
+    const bool more = b + 1 < b_end;
+    if (more) {
+      load_x(b + 1, xv);
+#pragma unroll
+      for (int tm = 0; tm < TM; tm++) load_sb(rowp[tm] + static_cast<int64_t>(b + 1) * 138, g, raw[tm]);
     }
-#pragma unroll 2
+    const uint16_t* xs = reinterpret_cast<const uint16_t*>(xs4[buf]);
+#pragma unroll
     for (int j = 0; j < 8; j++) {
       bf16x8v_t Bop[TM];
-      float scale[TM];
 #pragma unroll
-      for (int tm = 0; tm < TM; tm++) {
-        const uint8_t* o = rowp[tm] + static_cast<int64_t>(b) * 138 + 10 + 16 * j + 4 * g;
-        const uint32_t q = load_u16(o) | (load_u16(o + 2) << 16);
-        Bop[tm] = decode_codes(q);
-        const int8_t scj = static_cast<int8_t>((scw[tm][j >> 2] >> (8 * (j & 3))) & 0xffu);
-        scale[tm] = S[tm] * static_cast<float>(scj);
-      }
+      for (int tm = 0; tm < TM; tm++) Bop[tm] = decode_codes(cur[tm].code[j]);
 #pragma unroll
       for (int tn = 0; tn < TN; tn++) {
-        const uint16_t* xr = xs + (16 * tn + l16) * kLdsRow + 32 * j + 4 * g;
-        const uint2 a0 = *reinterpret_cast<const uint2*>(xr);
-        const uint2 a1 = *reinterpret_cast<const uint2*>(xr + 16);
-        const bf16x8v_t Aop = __builtin_bit_cast(bf16x8v_t, make_uint4(a0.x, a0.y, a1.x, a1.y));
+        const bf16x8v_t Aop = *reinterpret_cast<const bf16x8v_t*>(xs + (16 * tn + l16) * kLdsRow + 32 * j + 8 * g);
 #pragma unroll
         for (int tm = 0; tm < TM; tm++) {
           const float4_t P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aop, Bop[tm], zero, 0, 0, 0);
+          const float sc = cur[tm].scale[j];
           float4_t& A = acc[tm][tn];
-          A.x = __builtin_fmaf(scale[tm], P.x, A.x);
-          A.y = __builtin_fmaf(scale[tm], P.y, A.y);
-          A.z = __builtin_fmaf(scale[tm], P.z, A.z);
-          A.w = __builtin_fmaf(scale[tm], P.w, A.w);
+          A.x = __builtin_fmaf(sc, P.x, A.x);
+          A.y = __builtin_fmaf(sc, P.y, A.y);
+          A.z = __builtin_fmaf(sc, P.z, A.z);
+          A.w = __builtin_fmaf(sc, P.w, A.w);
         }
       }
+      // One sub-block at a time: the accumulators are "used" here, so the
+      // scaled additions cannot be sunk past later sub-blocks' MFMAs (which
+      // would keep every partial product live at once).
+#pragma unroll
+      for (int tm = 0; tm < TM; tm++)
+#pragma unroll
+        for (int tn = 0; tn < TN; tn++)
+          asm volatile("" : "+v"(acc[tm][tn].x), "+v"(acc[tm][tn].y), "+v"(acc[tm][tn].z), "+v"(acc[tm][tn].w));
+    }
+    if (more) {
+      store_x(buf ^ 1, xv);
+#pragma unroll
+      for (int tm = 0; tm < TM; tm++) finish_sb(rowp[tm] + static_cast<int64_t>(b + 1) * 138, raw[tm], cur[tm]);
     }
   }
+
 #pragma unroll
   for (int tm = 0; tm < TM; tm++) {
     const int64_t m = mw + 16 * tm + l16;
@@ -145,20 +242,54 @@ __global__ __launch_bounds__(kThreads) void k_gemm_sb4(const uint8_t* __restrict
 #pragma unroll
       for (int r = 0; r < 4; r++) {
         const int n = n0 + 16 * tn + 4 * g + r;
-        if (n < N) Y[static_cast<int64_t>(n) * M + m] = v[r];
+        if (n < N) {
+          float* dst = Y + static_cast<int64_t>(n) * M + m;
+          if constexpr (SPLIT) atomicAdd(dst, v[r]);
+          else *dst = v[r];
+        }
       }
     }
   }
 }
 
+int cu_count_gemm() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
 template <int TM, int TN>
 hipError_t launch_t(const void* blocks, int64_t m, int64_t k, const void* x, int64_t n, float* y,
                     hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((m + 64 * TM - 1) / (64 * TM)),
-                  static_cast<unsigned>((n + 16 * TN - 1) / (16 * TN)));
-  hipLaunchKernelGGL((k_gemm_sb4<TM, TN>), grid, dim3(kThreads), 0, s,
-                     static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
-                     static_cast<int>(m), static_cast<int>(k), static_cast<int>(n));
+  const unsigned gx = static_cast<unsigned>((m + 64 * TM - 1) / (64 * TM));
+  const unsigned gy = static_cast<unsigned>((n + 16 * TN - 1) / (16 * TN));
+  const int nsb = static_cast<int>(k / 256);
+  // split K when the tiles alone fill less than two workgroups per CU
+  const int64_t tiles = static_cast<int64_t>(gx) * gy;
+  int split = 1;
+  if (tiles < 2 * cu_count_gemm()) {
+    split = static_cast<int>((2 * cu_count_gemm() + tiles - 1) / tiles);
+    const int max_split = nsb / 2 > 1 ? nsb / 2 : 1;  // keep >= 2 super-blocks per piece
+    split = split > max_split ? max_split : split;
+  }
+  const int per = (nsb + split - 1) / split;
+  split = (nsb + per - 1) / per;
+  if (split > 1) {
+    const hipError_t e = launch_fill_zero(y, m * n, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_gemm_sb4<TM, TN, true>), dim3(gx, gy, split), dim3(kThreads), 0, s,
+                       static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
+                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), per);
+  } else {
+    hipLaunchKernelGGL((k_gemm_sb4<TM, TN, false>), dim3(gx, gy, 1), dim3(kThreads), 0, s,
+                       static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
+                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), nsb);
+  }
   return hipGetLastError();
 }
 
