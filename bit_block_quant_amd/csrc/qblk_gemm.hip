@@ -252,6 +252,197 @@ __global__ __launch_bounds__(kThreads) void k_gemm_sb4(const uint8_t* __restrict
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wide tiles on the 32x32x16 matrix op.
+//
+// Operand layout of v_mfma_f32_32x32x16_bf16: lane l holds row (l % 32) of A
+// and column (l % 32) of B, each with the 8 k values 8*(l / 32) .. +7 of the
+// 16-wide step; lane l receives D[8*(r/4) + 4*(l/32) + r%4][l % 32], r = 0..15.
+// A sub-block (32 k) is two steps.  In natural k order, step 0 holds weights
+// 0..15 of the sub-block (the low nibbles of its 16 code bytes) and step 1
+// weights 16..31 (the high nibbles), so lane half h needs code bytes
+// 8h..8h+7 -- low nibbles for step 0, high for step 1 -- and X entries
+// 16*step + 8h .. +7, one contiguous 16-byte piece of the token row.
+//
+// A workgroup of 4 waves owns 128 weight rows (32 per wave, decoded in the
+// wave's registers) and 32*T32 tokens shared by the 4 waves through LDS.
+// X is staged per half super-block (128 k = 16 pieces of 16 bytes per token),
+// double-buffered; piece c of token t is stored at slot c ^ (t % 16) so that
+// the 16 lanes of one LDS read phase hit 16 different bank groups.
+// ---------------------------------------------------------------------------
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// 16 codes (8 bytes, two dwords) -> (code - 8)/16 in bf16: low nibbles (step 0)
+// and high nibbles (step 1), each in byte order.
+__device__ __forceinline__ void decode16(uint32_t d0, uint32_t d1, bf16x8v_t& lo, bf16x8v_t& hi) {
+  const uint32_t a = d0 ^ 0x88888888u, b = d1 ^ 0x88888888u;
+  const uint32_t ah = a >> 4, bh = b >> 4;
+  lo = __builtin_bit_cast(bf16x8v_t, make_uint4(pk_bf16(off_i4<0>(a), off_i4<1>(a)), pk_bf16(off_i4<2>(a), off_i4<3>(a)),
+                                                pk_bf16(off_i4<0>(b), off_i4<1>(b)), pk_bf16(off_i4<2>(b), off_i4<3>(b))));
+  hi = __builtin_bit_cast(bf16x8v_t, make_uint4(pk_bf16(off_i4<0>(ah), off_i4<1>(ah)), pk_bf16(off_i4<2>(ah), off_i4<3>(ah)),
+                                                pk_bf16(off_i4<0>(bh), off_i4<1>(bh)), pk_bf16(off_i4<2>(bh), off_i4<3>(bh))));
+}
+
+constexpr int kRawW = 3 + 8 * 3;  // header dwords + three dwords per sub-block
+
+// Fetch what lane half h needs of one super-block at p: the header (as in
+// load_sb) and, per sub-block, the aligned 12 bytes holding code bytes 8h..8h+7.
+__device__ __forceinline__ void load_sb_w(const uint8_t* p, int h, uint32_t raw[kRawW]) {
+  // p - (p & 3) keeps the pointer's provenance, so these stay global loads
+  const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
+  const u32x3_a4 hd = *reinterpret_cast<const u32x3_a4*>(p - mis);
+  raw[0] = hd.x;
+  raw[1] = hd.y;
+  raw[2] = hd.z;
+  const uint8_t* c = p - mis + ((mis + 10 + 8 * h) & ~3u);
+#pragma unroll
+  for (int s = 0; s < 8; s++) {
+    const u32x3_a4 v = *reinterpret_cast<const u32x3_a4*>(c + 16 * s);
+    raw[3 + 3 * s] = v.x;
+    raw[4 + 3 * s] = v.y;
+    raw[5 + 3 * s] = v.z;
+  }
+}
+
+struct SbRegsW {
+  uint32_t code[8][2];
+  float scale[8];  // 16 * S * sc_j
+};
+
+__device__ __forceinline__ void finish_sb_w(const uint8_t* p, const uint32_t raw[kRawW], SbRegsW& r) {
+  const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
+  const uint32_t w0 = __builtin_amdgcn_alignbyte(raw[1], raw[0], sh);  // S16, sc0, sc1
+  const uint32_t w1 = __builtin_amdgcn_alignbyte(raw[2], raw[1], sh);  // sc2..sc5
+  const uint32_t w2 = raw[2] >> (8 * sh);                              // sc6, sc7
+  const float S16 = f16_bits_to_f32(w0 & 0xffffu) * 16.0f;
+  const uint32_t sc03 = (w0 >> 16) | (w1 << 16), sc47 = (w1 >> 16) | (w2 << 16);
+  // code bytes start at p + 10 (+ 8h): offset (sh + 2) & 3 inside the aligned dwords
+  const uint32_t cs = (sh + 2) & 3u;
+#pragma unroll
+  for (int s = 0; s < 8; s++) {
+    r.code[s][0] = __builtin_amdgcn_alignbyte(raw[4 + 3 * s], raw[3 + 3 * s], cs);
+    r.code[s][1] = __builtin_amdgcn_alignbyte(raw[5 + 3 * s], raw[4 + 3 * s], cs);
+    const uint32_t word = s < 4 ? sc03 : sc47;
+    const int8_t c = static_cast<int8_t>((word >> (8 * (s & 3))) & 0xffu);
+    r.scale[s] = S16 * static_cast<float>(c);
+  }
+}
+
+template <int T32, bool SPLIT>
+__global__ __launch_bounds__(kThreads, 2) void k_gemm_sb4_w(const uint8_t* __restrict__ W,
+                                                          const uint16_t* __restrict__ X,
+                                                          float* __restrict__ Y, int M, int K, int N,
+                                                          int sb_per_split) {
+  constexpr int NT = 32 * T32;             // tokens per workgroup
+  constexpr int kPieces = NT * 16;         // 16-byte pieces per stage (128 k per token)
+  constexpr int kPer = kPieces / kThreads; // pieces moved per thread per stage
+  static_assert(kPieces % kThreads == 0, "stage must split evenly over the workgroup");
+  __shared__ uint4 xs[2][kPieces];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j32 = lane & 31, h = lane >> 5;
+  const int64_t m = static_cast<int64_t>(blockIdx.x) * 128 + wave * 32 + j32;
+  const int n0 = blockIdx.y * NT;
+  const int nsb = K / 256;
+  const int b_begin = SPLIT ? blockIdx.z * sb_per_split : 0;
+  const int b_end = SPLIT ? min(nsb, b_begin + sb_per_split) : nsb;
+  const int64_t rowbytes = static_cast<int64_t>(nsb) * 138;
+  const uint8_t* rowp = W + (m < M ? m : M - 1) * rowbytes;
+
+  // stage q = 2*b + half: thread t moves pieces t, t+256, ...; piece i of the
+  // stage is token i/16, 16-byte piece i%16 of that token's 128 k.  Tokens
+  // past N read the last token's row instead: their products are never stored.
+  uint32_t xoff[kPer];  // byte offset of the thread's pieces from token n0, k 0
+#pragma unroll
+  for (int i = 0; i < kPer; i++) {
+    const int c = threadIdx.x + i * kThreads;
+    const int t = min(c >> 4, N - 1 - n0), pc = c & 15;
+    xoff[i] = static_cast<uint32_t>(t) * static_cast<uint32_t>(K) * 2u + 16u * pc;
+  }
+  const uint8_t* xtile = reinterpret_cast<const uint8_t*>(X + static_cast<int64_t>(n0) * K);
+  auto load_x = [&](int q, uint4 xv[kPer]) {
+    const uint8_t* xq = xtile + 256 * q;
+#pragma unroll
+    for (int i = 0; i < kPer; i++) xv[i] = *reinterpret_cast<const uint4*>(xq + xoff[i]);
+  };
+  auto store_x = [&](int buf, const uint4 xv[kPer]) {
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+      const int c = threadIdx.x + i * kThreads;
+      const int t = c >> 4, pc = c & 15;
+      xs[buf][t * 16 + (pc ^ (t & 15))] = xv[i];
+    }
+  };
+
+  f32x16_t acc[T32];
+#pragma unroll
+  for (int tt = 0; tt < T32; tt++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[tt][r] = 0.0f;
+  f32x16_t zero;
+#pragma unroll
+  for (int r = 0; r < 16; r++) zero[r] = 0.0f;
+
+  uint4 xv[kPer];
+  uint32_t raw[kRawW];
+  SbRegsW cur;
+  if (b_begin < b_end) {
+    load_x(2 * b_begin, xv);
+    load_sb_w(rowp + static_cast<int64_t>(b_begin) * 138, h, raw);
+    store_x(0, xv);
+    finish_sb_w(rowp + static_cast<int64_t>(b_begin) * 138, raw, cur);
+  }
+
+  // Stage hs of super-block b reads buffer hs; the next stage's X is fetched
+  // into registers meanwhile, and the next super-block's codes during stage 0.
+  // The last stage fetches (and parks in the idle buffer) a copy of itself,
+  // so the loop body has no data-dependent branches.
+  for (int b = b_begin; b < b_end; b++) {
+    const int bn = b + 1 < b_end ? b + 1 : b;
+#pragma unroll
+    for (int hs = 0; hs < 2; hs++) {
+      __syncthreads();
+      load_x(hs == 0 ? 2 * b + 1 : 2 * bn, xv);
+      if (hs == 0) load_sb_w(rowp + static_cast<int64_t>(bn) * 138, h, raw);
+      const uint4* xb = xs[hs];
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const int s = 4 * hs + jj;
+        bf16x8v_t B0, B1;
+        decode16(cur.code[s][0], cur.code[s][1], B0, B1);
+        const float sc = cur.scale[s];
+#pragma unroll
+        for (int tt = 0; tt < T32; tt++) {
+          const int t = 32 * tt + j32;
+          const bf16x8v_t A0 = __builtin_bit_cast(bf16x8v_t, xb[t * 16 + ((4 * jj + h) ^ (t & 15))]);
+          const bf16x8v_t A1 = __builtin_bit_cast(bf16x8v_t, xb[t * 16 + ((4 * jj + 2 + h) ^ (t & 15))]);
+          f32x16_t P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, B0, zero, 0, 0, 0);
+          P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B1, P, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 16; r++) acc[tt][r] = __builtin_fmaf(sc, P[r], acc[tt][r]);
+        }
+#pragma unroll
+        for (int tt = 0; tt < T32; tt++) asm volatile("" : "+v"(acc[tt]));
+      }
+      store_x(hs ^ 1, xv);
+      if (hs == 1) finish_sb_w(rowp + static_cast<int64_t>(bn) * 138, raw, cur);
+    }
+  }
+
+  if (m < M) {
+#pragma unroll
+    for (int tt = 0; tt < T32; tt++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int n = n0 + 32 * tt + 8 * (r / 4) + 4 * h + (r % 4);
+        if (n < N) {
+          float* dst = Y + static_cast<int64_t>(n) * M + m;
+          if constexpr (SPLIT) atomicAdd(dst, acc[tt][r]);
+          else *dst = acc[tt][r];
+        }
+      }
+  }
+}
+
 int cu_count_gemm() {
   static int n = 0;
   if (n == 0) {
@@ -293,6 +484,37 @@ hipError_t launch_t(const void* blocks, int64_t m, int64_t k, const void* x, int
   return hipGetLastError();
 }
 
+template <int T32>
+hipError_t launch_w(const void* blocks, int64_t m, int64_t k, const void* x, int64_t n, float* y,
+                    hipStream_t s) {
+  const unsigned gx = static_cast<unsigned>((m + 127) / 128);
+  const unsigned gy = static_cast<unsigned>((n + 32 * T32 - 1) / (32 * T32));
+  const int nsb = static_cast<int>(k / 256);
+  // split K when the tiles alone leave CUs idle (two workgroups fit per CU)
+  const int64_t tiles = static_cast<int64_t>(gx) * gy;
+  const int cus = cu_count_gemm();
+  int split = 1;
+  if (tiles < cus) {
+    split = static_cast<int>((2 * cus + tiles - 1) / tiles);
+    const int max_split = nsb / 2 > 1 ? nsb / 2 : 1;  // keep >= 2 super-blocks per piece
+    split = split > max_split ? max_split : split;
+  }
+  const int per = (nsb + split - 1) / split;
+  split = (nsb + per - 1) / per;
+  if (split > 1) {
+    const hipError_t e = launch_fill_zero(y, m * n, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_gemm_sb4_w<T32, true>), dim3(gx, gy, split), dim3(kThreads), 0, s,
+                       static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
+                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), per);
+  } else {
+    hipLaunchKernelGGL((k_gemm_sb4_w<T32, false>), dim3(gx, gy, 1), dim3(kThreads), 0, s,
+                       static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
+                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), nsb);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm(int fmt, const void* blocks, int64_t m, int64_t k, const void* x, int xt,
@@ -302,7 +524,7 @@ hipError_t launch_gemm(int fmt, const void* blocks, int64_t m, int64_t k, const 
   if (n <= 16) return launch_t<1, 1>(blocks, m, k, x, n, y, s);
   if (n <= 32) return launch_t<1, 2>(blocks, m, k, x, n, y, s);
   if (n <= 64) return launch_t<1, 4>(blocks, m, k, x, n, y, s);
-  return launch_t<2, 4>(blocks, m, k, x, n, y, s);
+  return launch_w<4>(blocks, m, k, x, n, y, s);
 }
 
 }  // namespace qblk
