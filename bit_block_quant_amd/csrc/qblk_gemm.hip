@@ -443,6 +443,167 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_sb4_w(const uint8_t* __res
   }
 }
 
+// ---------------------------------------------------------------------------
+// Few tokens (at most 64): the product is bound by streaming W, so each
+// workgroup issues every load it needs up front -- the codes of its 128 rows
+// over NSB super-blocks straight into registers, and the matching X slice into
+// LDS -- then multiplies and adds its partial sums into Y (zeroed first when
+// K is split over the grid).  Layout as in k_gemm_sb4: 16x16x32 steps, X in
+// MFMA order in LDS, lane k-group g taking code bytes 4g..4g+3.
+// ---------------------------------------------------------------------------
+constexpr int kRawS = 3 + 8 * 2;  // header dwords + an aligned dword pair per sub-block
+
+// Header and the aligned 8 bytes holding code bytes 4g..4g+3 of each sub-block.
+__device__ __forceinline__ void load_sb_s(const uint8_t* p, int g, uint32_t raw[kRawS]) {
+  const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
+  const u32x3_a4 hd = *reinterpret_cast<const u32x3_a4*>(p - mis);
+  raw[0] = hd.x;
+  raw[1] = hd.y;
+  raw[2] = hd.z;
+  const uint8_t* c = p - mis + ((mis + 10 + 4 * g) & ~3u);
+#pragma unroll
+  for (int s = 0; s < 8; s++) {
+    const u32x2_a4 v = *reinterpret_cast<const u32x2_a4*>(c + 16 * s);
+    raw[3 + 2 * s] = v.x;
+    raw[4 + 2 * s] = v.y;
+  }
+}
+
+__device__ __forceinline__ void finish_sb_s(const uint8_t* p, const uint32_t raw[kRawS], SbRegs& r) {
+  const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
+  const uint32_t w0 = __builtin_amdgcn_alignbyte(raw[1], raw[0], sh);  // S16, sc0, sc1
+  const uint32_t w1 = __builtin_amdgcn_alignbyte(raw[2], raw[1], sh);  // sc2..sc5
+  const uint32_t w2 = raw[2] >> (8 * sh);                              // sc6, sc7
+  const float S16 = f16_bits_to_f32(w0 & 0xffffu) * 16.0f;
+  const uint32_t sc03 = (w0 >> 16) | (w1 << 16), sc47 = (w1 >> 16) | (w2 << 16);
+  const uint32_t cs = (sh + 2) & 3u;  // code bytes start at p + 10
+#pragma unroll
+  for (int s = 0; s < 8; s++) {
+    r.code[s] = __builtin_amdgcn_alignbyte(raw[4 + 2 * s], raw[3 + 2 * s], cs);
+    const uint32_t word = s < 4 ? sc03 : sc47;
+    const int8_t c = static_cast<int8_t>((word >> (8 * (s & 3))) & 0xffu);
+    r.scale[s] = S16 * static_cast<float>(c);
+  }
+}
+
+template <int R16, int T16, int NSB, bool SPLIT>
+__global__ __launch_bounds__(kThreads) void k_gemm_sb4_s(const uint8_t* __restrict__ W,
+                                                       const uint16_t* __restrict__ X,
+                                                       float* __restrict__ Y, int M, int K, int N) {
+  constexpr int NT = 16 * T16;
+  constexpr int kPieces = NSB * NT * 32;  // 16-byte pieces of the X slice
+  constexpr int kPer = (kPieces + kThreads - 1) / kThreads;
+  __shared__ uint4 xs4[NSB * NT * kLdsRow / 8];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int64_t mw = static_cast<int64_t>(blockIdx.x) * 64 * R16 + wave * 16 * R16;
+  const int n0 = blockIdx.y * NT;
+  const int nsb = K / 256;
+  const int b0 = blockIdx.z * NSB;
+  const int nb = min(NSB, nsb - b0);  // super-blocks in this piece of K (>= 1)
+  const int64_t rowbytes = static_cast<int64_t>(nsb) * 138;
+  const uint8_t* rowp[R16];
+#pragma unroll
+  for (int tm = 0; tm < R16; tm++) {
+    const int64_t m = mw + 16 * tm + l16;
+    rowp[tm] = W + (m < M ? m : M - 1) * rowbytes + static_cast<int64_t>(b0) * 138;
+  }
+
+  // X first (L2-resident, needed before the barrier), then all the codes.
+  // Pieces past the piece's last super-block or past token N-1 re-read valid
+  // data that is never used or never stored.
+  uint4 xv[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; i++) {
+    const int c = min(static_cast<int>(threadIdx.x) + i * kThreads, kPieces - 1);
+    const int sb = c / (NT * 32), rem = c % (NT * 32);
+    const int t = min(n0 + (rem >> 5), N - 1), col = rem & 31;
+    const int b = b0 + min(sb, nb - 1);
+    xv[i] = *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(t) * K + 256 * b + 8 * col);
+  }
+  uint32_t raw[R16][NSB][kRawS];
+#pragma unroll
+  for (int sb = 0; sb < NSB; sb++)
+#pragma unroll
+    for (int tm = 0; tm < R16; tm++) load_sb_s(rowp[tm] + 138 * min(sb, nb - 1), g, raw[tm][sb]);
+
+  uint16_t* xs = reinterpret_cast<uint16_t*>(xs4);
+#pragma unroll
+  for (int i = 0; i < kPer; i++) {
+    const int c = static_cast<int>(threadIdx.x) + i * kThreads;
+    if (kPieces % kThreads == 0 || c < kPieces) {
+      const int sb = c / (NT * 32), rem = c % (NT * 32);
+      // entries 8cc..8cc+7 of sub-block j go to the k-group slots 32j + 8g (+4)
+      const int j = (rem & 31) >> 2, cc = rem & 3;
+      const int g0 = 2 * (cc & 1), half = cc >> 1;
+      uint16_t* row = xs + (sb * NT + (rem >> 5)) * kLdsRow + 32 * j + 4 * half;
+      *reinterpret_cast<uint2*>(row + 8 * g0) = make_uint2(xv[i].x, xv[i].y);
+      *reinterpret_cast<uint2*>(row + 8 * (g0 + 1)) = make_uint2(xv[i].z, xv[i].w);
+    }
+  }
+  __syncthreads();
+
+  float4_t acc[R16][T16];
+#pragma unroll
+  for (int tm = 0; tm < R16; tm++)
+#pragma unroll
+    for (int tn = 0; tn < T16; tn++) acc[tm][tn] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+
+#pragma unroll
+  for (int sb = 0; sb < NSB; sb++) {
+    if (sb >= nb) break;
+    SbRegs cur[R16];
+#pragma unroll
+    for (int tm = 0; tm < R16; tm++) finish_sb_s(rowp[tm] + 138 * sb, raw[tm][sb], cur[tm]);
+    const uint16_t* xb = xs + sb * NT * kLdsRow;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      bf16x8v_t Bop[R16];
+#pragma unroll
+      for (int tm = 0; tm < R16; tm++) Bop[tm] = decode_codes(cur[tm].code[j]);
+#pragma unroll
+      for (int tn = 0; tn < T16; tn++) {
+        const bf16x8v_t Aop = *reinterpret_cast<const bf16x8v_t*>(xb + (16 * tn + l16) * kLdsRow + 32 * j + 8 * g);
+#pragma unroll
+        for (int tm = 0; tm < R16; tm++) {
+          const float4_t P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aop, Bop[tm], zero, 0, 0, 0);
+          const float sc = cur[tm].scale[j];
+          float4_t& A = acc[tm][tn];
+          A.x = __builtin_fmaf(sc, P.x, A.x);
+          A.y = __builtin_fmaf(sc, P.y, A.y);
+          A.z = __builtin_fmaf(sc, P.z, A.z);
+          A.w = __builtin_fmaf(sc, P.w, A.w);
+        }
+      }
+#pragma unroll
+      for (int tm = 0; tm < R16; tm++)
+#pragma unroll
+        for (int tn = 0; tn < T16; tn++)
+          asm volatile("" : "+v"(acc[tm][tn].x), "+v"(acc[tm][tn].y), "+v"(acc[tm][tn].z), "+v"(acc[tm][tn].w));
+    }
+  }
+
+#pragma unroll
+  for (int tm = 0; tm < R16; tm++) {
+    const int64_t m = mw + 16 * tm + l16;
+    if (m >= M) continue;
+#pragma unroll
+    for (int tn = 0; tn < T16; tn++) {
+      const float v[4] = {acc[tm][tn].x, acc[tm][tn].y, acc[tm][tn].z, acc[tm][tn].w};
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int n = n0 + 16 * tn + 4 * g + r;
+        if (n < N) {
+          float* dst = Y + static_cast<int64_t>(n) * M + m;
+          if constexpr (SPLIT) atomicAdd(dst, v[r]);
+          else *dst = v[r];
+        }
+      }
+    }
+  }
+}
+
 int cu_count_gemm() {
   static int n = 0;
   if (n == 0) {
@@ -515,14 +676,35 @@ hipError_t launch_w(const void* blocks, int64_t m, int64_t k, const void* x, int
   return hipGetLastError();
 }
 
+template <int R16, int T16, int NSB>
+hipError_t launch_s(const void* blocks, int64_t m, int64_t k, const void* x, int64_t n, float* y,
+                    hipStream_t s) {
+  const unsigned gx = static_cast<unsigned>((m + 64 * R16 - 1) / (64 * R16));
+  const unsigned gy = static_cast<unsigned>((n + 16 * T16 - 1) / (16 * T16));
+  const int nsb = static_cast<int>(k / 256);
+  const unsigned gz = static_cast<unsigned>((nsb + NSB - 1) / NSB);
+  if (gz > 1) {
+    const hipError_t e = launch_fill_zero(y, m * n, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_gemm_sb4_s<R16, T16, NSB, true>), dim3(gx, gy, gz), dim3(kThreads), 0, s,
+                       static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
+                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(n));
+  } else {
+    hipLaunchKernelGGL((k_gemm_sb4_s<R16, T16, NSB, false>), dim3(gx, gy, 1), dim3(kThreads), 0, s,
+                       static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
+                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(n));
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm(int fmt, const void* blocks, int64_t m, int64_t k, const void* x, int xt,
                        int64_t n, float* y, hipStream_t s) {
   (void)fmt;
   (void)xt;  // only QBLK_SB4 x QBLK_BF16 reaches this point
-  if (n <= 16) return launch_t<1, 1>(blocks, m, k, x, n, y, s);
-  if (n <= 32) return launch_t<1, 2>(blocks, m, k, x, n, y, s);
+  if (n <= 16) return launch_s<2, 1, 2>(blocks, m, k, x, n, y, s);
+  if (n <= 32) return launch_s<2, 2, 2>(blocks, m, k, x, n, y, s);
   if (n <= 64) return launch_t<1, 4>(blocks, m, k, x, n, y, s);
   return launch_w<4>(blocks, m, k, x, n, y, s);
 }

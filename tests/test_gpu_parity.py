@@ -264,7 +264,9 @@ def test_misaligned_pointer_is_rejected(q):
 
 
 # --------------------------------------------------------------------- GEMM
-@pytest.mark.parametrize("n", [1, 5, 16, 33, 64, 100])
+# token counts chosen to reach every tiling: <= 16, <= 32, <= 64 and wide
+# (one and two 128-token tiles), each with a ragged last tile
+@pytest.mark.parametrize("n", [1, 5, 16, 24, 32, 33, 64, 100, 200])
 def test_gemm_tolerance_small(q, n):
     m, k = 150, 2304
     w = mixed_blocks(m, k, 11)
@@ -273,6 +275,18 @@ def test_gemm_tolerance_small(q, n):
     Y = host(q.gemm(dev(blocks), q.SB4, m, k, dev_bf16(X)))
     Y_ref, B = O.gemm(O.SB4, blocks, m, k, WL.bf16_values(X).astype(np.float64))
     check_products(Y, Y_ref, B, f"gemm n={n}")
+
+
+@pytest.mark.parametrize("n", [3, 40, 130])
+def test_gemm_single_super_block(q, n):
+    # K = 256: one super-block, so every K-split and pipelining path degenerates
+    m, k = 70, 256
+    w = mixed_blocks(m, k, 13)
+    blocks = O.quantize_sb4(w)
+    X = WL.bf16_bits(np.random.default_rng(14).standard_normal((n, k)).astype(np.float32))
+    Y = host(q.gemm(dev(blocks), q.SB4, m, k, dev_bf16(X)))
+    Y_ref, B = O.gemm(O.SB4, blocks, m, k, WL.bf16_values(X).astype(np.float64))
+    check_products(Y, Y_ref, B, f"gemm k=256 n={n}")
 
 
 @pytest.mark.parametrize("shape", ["up", "down"])
