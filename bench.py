@@ -320,6 +320,30 @@ def measure_rows(torch, q, WL, np, dev):
                               frac_mfma_bf16=round(tf / BF16_PEAK_TFLOPS, 4))
             log(f"  {name}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s, {tf:.1f} TFLOP/s")
         del cps
+    # the same product for the other two formats (14336x4096)
+    w, _ = WL.sb4_prefill("up", 16)
+    m, k = w.shape
+    wd = torch.from_numpy(w).to(dev)
+    for fmt, tag in ((q.Q4_0, "q4_0"), (q.SB4_AFFINE, "sb4a")):
+        b0 = q.quantize(wd, fmt)
+        C = n_copies(b0.numel())
+        cps = [b0] + [b0.clone() for _ in range(C - 1)]
+        for n_tok in (16, 64, 512):
+            _, X = WL.sb4_prefill("up", n_tok)
+            Xd = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16)
+            Y = torch.empty((n_tok, m), dtype=torch.float32, device=dev)
+            t = Timer(torch, lambda i: q.gemm(cps[i], fmt, m, k, Xd, out=Y), C)
+            ms = t.run(max(1, 100 // C))
+            flops = 2.0 * m * k * n_tok
+            nb = b0.numel() + X.size * 2 + Y.numel() * 4
+            tf = flops / (ms * 1e-3) / 1e12
+            gbs = nb / (ms * 1e-3) / 1e9
+            name = f"gemm_{tag}_{m}x{k}_n{n_tok}_bf16"
+            rows[name] = dict(us=round(ms * 1e3, 3), bytes=nb, GBps=round(gbs, 1),
+                              frac_hbm=round(gbs / HBM_PEAK_GBS, 4), TFLOPs=round(tf, 2),
+                              frac_mfma_bf16=round(tf / BF16_PEAK_TFLOPS, 4))
+            log(f"  {name}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s, {tf:.1f} TFLOP/s")
+        del cps
     return rows
 
 

@@ -138,7 +138,8 @@ qblk_status_t qblk_gemm(qblk_format_t fmt, const void* blocks, int64_t m, int64_
   QBLK_TRY(check_shape(fmt, m, k));
   if (!dtype_ok(xt)) return QBLK_ERR_DTYPE;
   if (n < 0 || n > kMaxDim) return QBLK_ERR_SHAPE;
-  if (fmt != QBLK_SB4 || xt != QBLK_BF16) return QBLK_ERR_UNSUPPORTED;
+  // the matrix-core kernels take bf16 activations and whole 256-weight groups
+  if (xt != QBLK_BF16 || k % 256 != 0) return QBLK_ERR_UNSUPPORTED;
   const bool out = m > 0 && n > 0;
   QBLK_TRY(check_ptr(blocks, out && k > 0));
   QBLK_TRY(check_ptr(x, out && k > 0));

@@ -74,55 +74,144 @@ __device__ __forceinline__ bf16x8v_t decode_codes(uint32_t q) {
   return __builtin_bit_cast(bf16x8v_t, w);
 }
 
-// The registers a lane needs from one super-block of one weight row:
-// the 8 code dwords of its k-group (one per sub-block) and the header.
+// The registers a lane needs from one 256-weight group of one weight row:
+// the 8 code dwords of its k-group (one per sub-block), the 8 sub-block
+// scales, and (Type 1) the sub-block offsets of sub-blocks g and g+4.
 struct SbRegs {
   uint32_t code[8];
-  float scale[8];  // 16 * S * sc_j
+  float scale[8];  // 16 * (scale of sub-block j): codes decode to (code-8)/16
+  float corr[2];   // Type 1: 8*s_j + a_j for j = g, g+4 (see k_gemm_t)
 };
 
-constexpr int kRaw = 3 + 16;  // header dwords + two u16 per sub-block
+// How each format lays out a 256-weight group (8 sub-blocks of 32):
+//  Type 0   [S16][sc x8][qs x128]              138 B, scale S*sc_j
+//  Q4_0     8 blocks [d16][qs x16]              144 B, scale d_j
+//  Type 1   [Ss16][Sa16][sc x8][ac x8][qs x128] 148 B, scale Ss*sc_j, offset Sa*ac_j
+// Lane k-group g needs code bytes 4g..4g+3 of every sub-block.
+template <int FMT>
+struct Group;
 
-__device__ __forceinline__ void load_sb(const uint8_t* p, int g, uint32_t raw[kRaw]) {
-  // header: dword-aligned 12 bytes covering the 10 header bytes (all inside
-  // the super-block: [p-2, p+10) or [p, p+12))
-  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-  const u32x3_a4 h = *reinterpret_cast<const u32x3_a4*>(a & ~uintptr_t(3));
-  raw[0] = h.x;
-  raw[1] = h.y;
-  raw[2] = h.z;
-  // code bytes 4g..4g+3 of each sub-block (2-byte aligned): two u16 each
+template <>
+struct Group<QBLK_SB4> {
+  static constexpr int GB = 138, RAW = 3 + 16;
+  // header: the dword-aligned 12 bytes holding the 10 header bytes; codes
+  // (2-byte aligned): two u16 per sub-block
+  static __device__ __forceinline__ void load(const uint8_t* p, int g, uint32_t raw[RAW]) {
+    const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
+    const u32x3_a4 h = *reinterpret_cast<const u32x3_a4*>(p - mis);
+    raw[0] = h.x;
+    raw[1] = h.y;
+    raw[2] = h.z;
 #pragma unroll
-  for (int s = 0; s < 8; s++) {
-    const uint8_t* o = p + 10 + 16 * s + 4 * g;
-    raw[3 + 2 * s] = load_u16(o);
-    raw[4 + 2 * s] = load_u16(o + 2);
+    for (int s = 0; s < 8; s++) {
+      const uint8_t* o = p + 10 + 16 * s + 4 * g;
+      raw[3 + 2 * s] = load_u16(o);
+      raw[4 + 2 * s] = load_u16(o + 2);
+    }
   }
+  static __device__ __forceinline__ void finish(const uint8_t* p, int, const uint32_t raw[RAW], SbRegs& r) {
+    const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
+    const uint32_t w0 = __builtin_amdgcn_alignbyte(raw[1], raw[0], sh);  // S16, sc0, sc1
+    const uint32_t w1 = __builtin_amdgcn_alignbyte(raw[2], raw[1], sh);  // sc2..sc5
+    const uint32_t w2 = raw[2] >> (8 * sh);                              // sc6, sc7
+    const float S16 = f16_bits_to_f32(w0 & 0xffffu) * 16.0f;
+    const uint32_t sc03 = (w0 >> 16) | (w1 << 16), sc47 = (w1 >> 16) | (w2 << 16);
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+      r.code[s] = raw[3 + 2 * s] | (raw[4 + 2 * s] << 16);
+      const uint32_t word = s < 4 ? sc03 : sc47;
+      const int8_t c = static_cast<int8_t>((word >> (8 * (s & 3))) & 0xffu);
+      r.scale[s] = S16 * static_cast<float>(c);
+    }
+    r.corr[0] = r.corr[1] = 0.0f;
+  }
+};
+
+template <>
+struct Group<QBLK_Q4_0> {
+  // p is 4-byte aligned (rows are whole multiples of 144 bytes): block j
+  // starts at 18j, 2 bytes past a dword boundary when j is odd.
+  static constexpr int GB = 144, RAW = 8 + 12;
+  static __device__ __forceinline__ void load(const uint8_t* p, int g, uint32_t raw[RAW]) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      raw[j] = *reinterpret_cast<const uint32_t*>(p + ((18 * j) & ~3));  // d16 in the low or high half
+      if (j & 1) {
+        raw[8 + (j >> 1) * 3 + 2] = *reinterpret_cast<const uint32_t*>(p + 18 * j + 2 + 4 * g);  // aligned
+      } else {
+        const u32x2_a4 v = *reinterpret_cast<const u32x2_a4*>(p + 18 * j + 4 * g);  // bytes 2..5 at +2
+        raw[8 + (j >> 1) * 3] = v.x;
+        raw[8 + (j >> 1) * 3 + 1] = v.y;
+      }
+    }
+  }
+  static __device__ __forceinline__ void finish(const uint8_t*, int, const uint32_t raw[RAW], SbRegs& r) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const uint32_t d = (j & 1) ? raw[j] >> 16 : raw[j] & 0xffffu;
+      r.scale[j] = f16_bits_to_f32(d) * 16.0f;
+      r.code[j] = (j & 1) ? raw[8 + (j >> 1) * 3 + 2]
+                          : __builtin_amdgcn_alignbyte(raw[8 + (j >> 1) * 3 + 1], raw[8 + (j >> 1) * 3], 2);
+    }
+    r.corr[0] = r.corr[1] = 0.0f;
+  }
+};
+
+template <>
+struct Group<QBLK_SB4_AFFINE> {
+  // 148-byte groups are dword aligned: header dwords 0..4, codes 4-aligned
+  static constexpr int GB = 148, RAW = 5 + 8;
+  static __device__ __forceinline__ void load(const uint8_t* p, int g, uint32_t raw[RAW]) {
+    const u32x4_a4 h = *reinterpret_cast<const u32x4_a4*>(p);
+    raw[0] = h.x;
+    raw[1] = h.y;
+    raw[2] = h.z;
+    raw[3] = h.w;
+    raw[4] = *reinterpret_cast<const uint32_t*>(p + 16);
+#pragma unroll
+    for (int s = 0; s < 8; s++) raw[5 + s] = *reinterpret_cast<const uint32_t*>(p + 20 + 16 * s + 4 * g);
+  }
+  static __device__ __forceinline__ void finish(const uint8_t*, int g, const uint32_t raw[RAW], SbRegs& r) {
+    const float Ss = f16_bits_to_f32(raw[0] & 0xffffu), Sa = f16_bits_to_f32(raw[0] >> 16);
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+      r.code[s] = raw[5 + s];
+      const int8_t c = static_cast<int8_t>((raw[1 + (s >> 2)] >> (8 * (s & 3))) & 0xffu);
+      r.scale[s] = (Ss * static_cast<float>(c)) * 16.0f;
+    }
+    // w = s*n + a = s*(n-8) + (8s + a): the codes decode to n-8 as for Type 0,
+    // and (8s + a) * sum(x over the sub-block) is added per group
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      const uint32_t sw = raw[1 + q], aw = raw[3 + q];
+      const int8_t c = static_cast<int8_t>((sw >> (8 * g)) & 0xffu);
+      const int8_t o = static_cast<int8_t>((aw >> (8 * g)) & 0xffu);
+      r.corr[q] = __builtin_fmaf(8.0f, Ss * static_cast<float>(c), Sa * static_cast<float>(o));
+    }
+  }
+};
+
+// sum over the 4 lanes of a quad (lanes 4i..4i+3)
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));  // quad_perm 2,3,0,1
+  return v;
 }
 
-__device__ __forceinline__ void finish_sb(const uint8_t* p, const uint32_t raw[kRaw], SbRegs& r) {
-  const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
-  const uint32_t w0 = __builtin_amdgcn_alignbyte(raw[1], raw[0], sh);  // S16, sc0, sc1
-  const uint32_t w1 = __builtin_amdgcn_alignbyte(raw[2], raw[1], sh);  // sc2..sc5
-  const uint32_t w2 = raw[2] >> (8 * sh);                              // sc6, sc7
-  const float S16 = f16_bits_to_f32(w0 & 0xffffu) * 16.0f;
-  const uint32_t sc03 = (w0 >> 16) | (w1 << 16), sc47 = (w1 >> 16) | (w2 << 16);
-#pragma unroll
-  for (int s = 0; s < 8; s++) {
-    r.code[s] = raw[3 + 2 * s] | (raw[4 + 2 * s] << 16);
-    const uint32_t word = s < 4 ? sc03 : sc47;
-    const int8_t c = static_cast<int8_t>((word >> (8 * (s & 3))) & 0xffu);
-    r.scale[s] = S16 * static_cast<float>(c);
-  }
-}
-
-template <int TM, int TN, bool SPLIT>
-__global__ __launch_bounds__(kThreads) void k_gemm_sb4(const uint8_t* __restrict__ W,
-                                                       const uint16_t* __restrict__ X,
-                                                       float* __restrict__ Y, int M, int K, int N,
-                                                       int sb_per_split) {
+// Type 1 also needs sum(x) over every sub-block of every token: the staging
+// threads form it (the 4 quarters of a sub-block sit on 4 adjacent lanes) and
+// the per-group correction sum_j (8 s_j + a_j) sum(x_j) is added with two
+// fp32 16x16x4 matrix ops (sub-blocks 0..3 and 4..7) into the accumulators.
+template <int FMT, int TM, int TN, bool SPLIT>
+__global__ __launch_bounds__(kThreads) void k_gemm_t(const uint8_t* __restrict__ W,
+                                                     const uint16_t* __restrict__ X,
+                                                     float* __restrict__ Y, int M, int K, int N,
+                                                     int sb_per_split) {
+  using G = Group<FMT>;
+  constexpr bool AFFINE = FMT == QBLK_SB4_AFFINE;
   constexpr int NT = 16 * TN;
   __shared__ uint4 xs4[2][NT * kLdsRow / 8];
+  __shared__ float xsum[2][AFFINE ? NT * 8 : 1];  // [token][sub-block]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t mw = static_cast<int64_t>(blockIdx.x) * 64 * TM + wave * 16 * TM;
@@ -130,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_sb4(const uint8_t* __restrict
   const int nsb = K / 256;
   const int b_begin = SPLIT ? blockIdx.z * sb_per_split : 0;
   const int b_end = SPLIT ? min(nsb, b_begin + sb_per_split) : nsb;
-  const int64_t rowbytes = static_cast<int64_t>(nsb) * 138;
+  const int64_t rowbytes = static_cast<int64_t>(nsb) * G::GB;
   const uint8_t* rowp[TM];
 #pragma unroll
   for (int tm = 0; tm < TM; tm++) {
@@ -165,6 +254,17 @@ __global__ __launch_bounds__(kThreads) void k_gemm_sb4(const uint8_t* __restrict
         *reinterpret_cast<uint2*>(row + 8 * g0) = make_uint2(xv[i].x, xv[i].y);
         *reinterpret_cast<uint2*>(row + 8 * (g0 + 1)) = make_uint2(xv[i].z, xv[i].w);
       }
+      if constexpr (AFFINE) {
+        // products with 1.0 are exact; the sums are fp32
+        const bf16x2v_t one = __builtin_bit_cast(bf16x2v_t, 0x3f803f80u);
+        float part = 0.0f;
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].x), one, part, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].y), one, part, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].z), one, part, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].w), one, part, false);
+        part = quad_sum(part);
+        if (c < NT * 32 && (c & 3) == 0) xsum[buf][(c >> 5) * 8 + ((c & 31) >> 2)] = part;
+      }
     }
   };
 
@@ -176,15 +276,15 @@ __global__ __launch_bounds__(kThreads) void k_gemm_sb4(const uint8_t* __restrict
   const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
 
   uint4 xv[(NT * 32 + kThreads - 1) / kThreads];
-  uint32_t raw[TM][kRaw];
+  uint32_t raw[TM][G::RAW];
   SbRegs cur[TM];
   if (b_begin < b_end) {
     load_x(b_begin, xv);
 #pragma unroll
-    for (int tm = 0; tm < TM; tm++) load_sb(rowp[tm] + static_cast<int64_t>(b_begin) * 138, g, raw[tm]);
+    for (int tm = 0; tm < TM; tm++) G::load(rowp[tm] + static_cast<int64_t>(b_begin) * G::GB, g, raw[tm]);
     store_x(0, xv);
 #pragma unroll
-    for (int tm = 0; tm < TM; tm++) finish_sb(rowp[tm] + static_cast<int64_t>(b_begin) * 138, raw[tm], cur[tm]);
+    for (int tm = 0; tm < TM; tm++) G::finish(rowp[tm] + static_cast<int64_t>(b_begin) * G::GB, g, raw[tm], cur[tm]);
   }
 
   for (int b = b_begin; b < b_end; b++) {
@@ -194,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_sb4(const uint8_t* __restrict
     if (more) {
       load_x(b + 1, xv);
 #pragma unroll
-      for (int tm = 0; tm < TM; tm++) load_sb(rowp[tm] + static_cast<int64_t>(b + 1) * 138, g, raw[tm]);
+      for (int tm = 0; tm < TM; tm++) G::load(rowp[tm] + static_cast<int64_t>(b + 1) * G::GB, g, raw[tm]);
     }
     const uint16_t* xs = reinterpret_cast<const uint16_t*>(xs4[buf]);
 #pragma unroll
@@ -225,10 +325,22 @@ __global__ __launch_bounds__(kThreads) void k_gemm_sb4(const uint8_t* __restrict
         for (int tn = 0; tn < TN; tn++)
           asm volatile("" : "+v"(acc[tm][tn].x), "+v"(acc[tm][tn].y), "+v"(acc[tm][tn].z), "+v"(acc[tm][tn].w));
     }
+    if constexpr (AFFINE) {
+      // A = sum(x) [token][sub-block 4q + g], B = (8 s + a) [sub-block 4q + g][row]
+#pragma unroll
+      for (int tn = 0; tn < TN; tn++) {
+        const float* xq = xsum[buf] + (16 * tn + l16) * 8 + g;
+#pragma unroll
+        for (int tm = 0; tm < TM; tm++) {
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[0], cur[tm].corr[0], acc[tm][tn], 0, 0, 0);
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[4], cur[tm].corr[1], acc[tm][tn], 0, 0, 0);
+        }
+      }
+    }
     if (more) {
       store_x(buf ^ 1, xv);
 #pragma unroll
-      for (int tm = 0; tm < TM; tm++) finish_sb(rowp[tm] + static_cast<int64_t>(b + 1) * 138, raw[tm], cur[tm]);
+      for (int tm = 0; tm < TM; tm++) G::finish(rowp[tm] + static_cast<int64_t>(b + 1) * G::GB, g, raw[tm], cur[tm]);
     }
   }
 
@@ -615,7 +727,7 @@ int cu_count_gemm() {
   return n;
 }
 
-template <int TM, int TN>
+template <int FMT, int TM, int TN>
 hipError_t launch_t(const void* blocks, int64_t m, int64_t k, const void* x, int64_t n, float* y,
                     hipStream_t s) {
   const unsigned gx = static_cast<unsigned>((m + 64 * TM - 1) / (64 * TM));
@@ -634,11 +746,11 @@ hipError_t launch_t(const void* blocks, int64_t m, int64_t k, const void* x, int
   if (split > 1) {
     const hipError_t e = launch_fill_zero(y, m * n, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_gemm_sb4<TM, TN, true>), dim3(gx, gy, split), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((k_gemm_t<FMT, TM, TN, true>), dim3(gx, gy, split), dim3(kThreads), 0, s,
                        static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
                        static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), per);
   } else {
-    hipLaunchKernelGGL((k_gemm_sb4<TM, TN, false>), dim3(gx, gy, 1), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((k_gemm_t<FMT, TM, TN, false>), dim3(gx, gy, 1), dim3(kThreads), 0, s,
                        static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
                        static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), nsb);
   }
@@ -701,12 +813,23 @@ hipError_t launch_s(const void* blocks, int64_t m, int64_t k, const void* x, int
 
 hipError_t launch_gemm(int fmt, const void* blocks, int64_t m, int64_t k, const void* x, int xt,
                        int64_t n, float* y, hipStream_t s) {
-  (void)fmt;
-  (void)xt;  // only QBLK_SB4 x QBLK_BF16 reaches this point
-  if (n <= 16) return launch_s<2, 1, 2>(blocks, m, k, x, n, y, s);
-  if (n <= 32) return launch_s<2, 2, 2>(blocks, m, k, x, n, y, s);
-  if (n <= 64) return launch_t<1, 4>(blocks, m, k, x, n, y, s);
-  return launch_w<4>(blocks, m, k, x, n, y, s);
+  (void)xt;  // only BF16 activations reach this point
+  if (fmt == QBLK_SB4) {
+    if (n <= 16) return launch_s<2, 1, 2>(blocks, m, k, x, n, y, s);
+    if (n <= 32) return launch_s<2, 2, 2>(blocks, m, k, x, n, y, s);
+    if (n <= 64) return launch_t<QBLK_SB4, 1, 4>(blocks, m, k, x, n, y, s);
+    return launch_w<4>(blocks, m, k, x, n, y, s);
+  }
+  if (fmt == QBLK_Q4_0) {
+    if (n <= 16) return launch_t<QBLK_Q4_0, 1, 1>(blocks, m, k, x, n, y, s);
+    if (n <= 32) return launch_t<QBLK_Q4_0, 1, 2>(blocks, m, k, x, n, y, s);
+    if (n <= 64) return launch_t<QBLK_Q4_0, 1, 4>(blocks, m, k, x, n, y, s);
+    return launch_t<QBLK_Q4_0, 2, 4>(blocks, m, k, x, n, y, s);
+  }
+  if (n <= 16) return launch_t<QBLK_SB4_AFFINE, 1, 1>(blocks, m, k, x, n, y, s);
+  if (n <= 32) return launch_t<QBLK_SB4_AFFINE, 1, 2>(blocks, m, k, x, n, y, s);
+  if (n <= 64) return launch_t<QBLK_SB4_AFFINE, 1, 4>(blocks, m, k, x, n, y, s);
+  return launch_t<QBLK_SB4_AFFINE, 2, 4>(blocks, m, k, x, n, y, s);
 }
 
 }  // namespace qblk

@@ -142,9 +142,12 @@ qblk_status_t qblk_gemv(qblk_format_t fmt, const void* blocks, int64_t m,
                         qblk_stream_t stream);
 
 /* Small-batch product Y = X W^T: X is n x k row-major (token-major) of type xt,
- * Y is n x m row-major fp32.  QBLK_SB4 with xt = BF16 runs on the bf16 matrix
- * cores; other format/type pairs return QBLK_ERR_UNSUPPORTED.  Same error
- * bound as qblk_gemv, per output element. */
+ * Y is n x m row-major fp32.  All three formats run on the bf16 matrix cores
+ * with xt = BF16; F32/F16 activations, and Q4_0 with k % 256 != 0, return
+ * QBLK_ERR_UNSUPPORTED.  Same error bound as qblk_gemv, per output element.
+ * When k spans many groups and m*n is small the k range is split over the
+ * grid and partial sums are added into Y (zeroed first by this call), so the
+ * summation order, not the bound, varies between tilings. */
 qblk_status_t qblk_gemm(qblk_format_t fmt, const void* blocks, int64_t m,
                         int64_t k, const void* x, qblk_dtype_t xt, int64_t n,
                         float* y, qblk_stream_t stream);

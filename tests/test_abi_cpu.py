@@ -84,10 +84,12 @@ def test_argument_errors(q):
     assert L.qblk_gemv(1, MIS, 1, 256, B, 1, Y, S) == 4
     assert L.qblk_gemv(1, A, 1, 256, MIS, 1, Y, S) == 4
     assert L.qblk_quantize_sb4(A, 0, 1, 256, 0, MIS, S) == 4
-    # GEMM support matrix
-    assert L.qblk_gemm(0, A, 16, 256, B, 2, 16, Y, S) == 5
+    # GEMM support matrix: bf16 activations only; Q4_0 in whole 256-weight groups
     assert L.qblk_gemm(1, A, 16, 256, B, 1, 16, Y, S) == 5
-    assert L.qblk_gemm(2, A, 16, 256, B, 2, 16, Y, S) == 5
+    assert L.qblk_gemm(0, A, 16, 256, B, 0, 16, Y, S) == 5
+    assert L.qblk_gemm(0, A, 16, 288, B, 2, 16, Y, S) == 5
+    assert L.qblk_gemm(2, A, 16, 256, B, 1, 16, Y, S) == 5
+    assert L.qblk_gemm(0, A, 16, 33, B, 2, 16, Y, S) == 2
 
 
 def test_empty_calls_succeed_without_launch(q):

@@ -277,6 +277,38 @@ def test_gemm_tolerance_small(q, n):
     check_products(Y, Y_ref, B, f"gemm n={n}")
 
 
+def gemm_fmt(q, name):
+    """(library format id, oracle format id) for a format name."""
+    return {"q4_0": (q.Q4_0, O.Q4_0), "sb4a": (q.SB4_AFFINE, O.SB4_AFFINE)}[name]
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "sb4a"])
+@pytest.mark.parametrize("n", [1, 16, 24, 40, 64, 100])
+def test_gemm_other_formats(q, fmt, n):
+    # Q4_0 (scale per 32-block) and Type 1 (scale and offset per sub-block)
+    m, k = 150, 2304
+    f, of = gemm_fmt(q, fmt)
+    w = mixed_blocks(m, k, 21)
+    blocks = O.quantize(of, w)
+    X = WL.bf16_bits(np.random.default_rng(22).standard_normal((n, k)).astype(np.float32))
+    Y = host(q.gemm(dev(blocks), f, m, k, dev_bf16(X)))
+    Y_ref, B = O.gemm(of, blocks, m, k, WL.bf16_values(X).astype(np.float64))
+    check_products(Y, Y_ref, B, f"gemm {fmt} n={n}")
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "sb4a"])
+def test_gemm_other_formats_split_k(q, fmt):
+    # long K with few rows: K is split over the grid and summed into Y
+    m, k = 40, 14336
+    f, of = gemm_fmt(q, fmt)
+    w = mixed_blocks(m, k, 23)
+    blocks = O.quantize(of, w)
+    X = WL.bf16_bits(np.random.default_rng(24).standard_normal((20, k)).astype(np.float32))
+    Y = host(q.gemm(dev(blocks), f, m, k, dev_bf16(X)))
+    Y_ref, B = O.gemm(of, blocks, m, k, WL.bf16_values(X).astype(np.float64))
+    check_products(Y, Y_ref, B, f"gemm {fmt} split-K")
+
+
 @pytest.mark.parametrize("n", [3, 40, 130])
 def test_gemm_single_super_block(q, n):
     # K = 256: one super-block, so every K-split and pipelining path degenerates
