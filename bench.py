@@ -92,9 +92,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=200, help="untimed GEMV launches")
     ap.add_argument("--rows", type=int, default=1, help="1: also time the other hot-path steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline budget (0: skip)")
-    ap.add_argument("--mode", choices=("full", "traffic"), default="full",
+    ap.add_argument("--mode", choices=("full", "traffic", "gemm"), default="full",
                     help="traffic: a 256 MiB device copy (counter calibration) then a few "
-                         "headline GEMV launches, for rocprofv3 --pmc runs")
+                         "headline GEMV launches, for rocprofv3 --pmc runs; gemm: three "
+                         "launches of one prefill GEMM (--gemm-shape, --gemm-n), for counters")
+    ap.add_argument("--gemm-shape", choices=("up", "down"), default="up")
+    ap.add_argument("--gemm-n", type=int, default=512)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -115,6 +118,9 @@ def main():
 
     if args.mode == "traffic":
         traffic_run(torch, q, WL, dev)
+        return
+    if args.mode == "gemm":
+        gemm_run(torch, q, WL, np, dev, args.gemm_shape, args.gemm_n)
         return
 
     # ------------------------------------------------------------ headline
@@ -211,6 +217,21 @@ def traffic_run(torch, q, WL, dev):
         q.gemv(cps[(i + 1) % C], q.SB4, M, K, xd, out=y)
     torch.cuda.synchronize()
     log("traffic run done")
+
+
+def gemm_run(torch, q, WL, np, dev, shape, n_tok):
+    """Three launches of the Type 0 prefill GEMM on the seeded workload (one
+    weight copy: for counter runs, not timing)."""
+    w, X = WL.sb4_prefill(shape, n_tok)
+    m, k = w.shape
+    b = q.quantize(torch.from_numpy(w).to(dev), q.SB4)
+    Xd = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16)
+    Y = torch.empty((n_tok, m), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        q.gemm(b, q.SB4, m, k, Xd, out=Y)
+    torch.cuda.synchronize()
+    log(f"gemm run done ({shape}, {m}x{k}, n={n_tok})")
 
 
 # ----------------------------------------------------------------- other rows

@@ -397,8 +397,12 @@ __device__ __forceinline__ void decode16(uint32_t d0, uint32_t d1, bf16x8v_t& lo
 
 constexpr int kRawW = 3 + 8 * 3;  // header dwords + three dwords per sub-block
 
-// Fetch what lane half h needs of one super-block at p: the header (as in
-// load_sb) and, per sub-block, the aligned 12 bytes holding code bytes 8h..8h+7.
+// Fetch what lane half h needs of one super-block at p: the header (dword
+// aligned 12 bytes holding its 10 bytes, never before the row's first byte
+// since row starts are even) and, per sub-block, code bytes 8h..8h+7 at A,
+// from the dwords at A & ~3: three of them for sub-blocks 0..6 (the extra
+// bytes belong to the next sub-block), for sub-block 7 two dwords plus the
+// 2 bytes at A+6, so nothing past the super-block is read.
 __device__ __forceinline__ void load_sb_w(const uint8_t* p, int h, uint32_t raw[kRawW]) {
   // p - (p & 3) keeps the pointer's provenance, so these stay global loads
   const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
@@ -406,14 +410,19 @@ __device__ __forceinline__ void load_sb_w(const uint8_t* p, int h, uint32_t raw[
   raw[0] = hd.x;
   raw[1] = hd.y;
   raw[2] = hd.z;
-  const uint8_t* c = p - mis + ((mis + 10 + 8 * h) & ~3u);
+  const uint8_t* a = p + 10 + 8 * h;                      // code bytes of sub-block 0
+  const uint8_t* c = p - mis + ((mis + 10 + 8 * h) & ~3u);  // a & ~3
 #pragma unroll
-  for (int s = 0; s < 8; s++) {
+  for (int s = 0; s < 7; s++) {
     const u32x3_a4 v = *reinterpret_cast<const u32x3_a4*>(c + 16 * s);
     raw[3 + 3 * s] = v.x;
     raw[4 + 3 * s] = v.y;
     raw[5 + 3 * s] = v.z;
   }
+  const u32x2_a4 v = *reinterpret_cast<const u32x2_a4*>(c + 16 * 7);
+  raw[3 + 3 * 7] = v.x;
+  raw[4 + 3 * 7] = v.y;
+  raw[5 + 3 * 7] = load_u16(a + 16 * 7 + 6);
 }
 
 struct SbRegsW {
@@ -565,20 +574,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_sb4_w(const uint8_t* __res
 // ---------------------------------------------------------------------------
 constexpr int kRawS = 3 + 8 * 2;  // header dwords + an aligned dword pair per sub-block
 
-// Header and the aligned 8 bytes holding code bytes 4g..4g+3 of each sub-block.
+// Header (as in load_sb_w) and, per sub-block, code bytes 4g..4g+3 at A from
+// the dword pair at A & ~3 (sub-blocks 0..6) or, for sub-block 7, the dword
+// at A & ~3 plus the 2 bytes at A+2: nothing past the super-block is read.
 __device__ __forceinline__ void load_sb_s(const uint8_t* p, int g, uint32_t raw[kRawS]) {
   const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
   const u32x3_a4 hd = *reinterpret_cast<const u32x3_a4*>(p - mis);
   raw[0] = hd.x;
   raw[1] = hd.y;
   raw[2] = hd.z;
-  const uint8_t* c = p - mis + ((mis + 10 + 4 * g) & ~3u);
+  const uint8_t* a = p + 10 + 4 * g;
+  const uint8_t* c = p - mis + ((mis + 10 + 4 * g) & ~3u);  // a & ~3
 #pragma unroll
-  for (int s = 0; s < 8; s++) {
+  for (int s = 0; s < 7; s++) {
     const u32x2_a4 v = *reinterpret_cast<const u32x2_a4*>(c + 16 * s);
     raw[3 + 2 * s] = v.x;
     raw[4 + 2 * s] = v.y;
   }
+  raw[3 + 2 * 7] = *reinterpret_cast<const uint32_t*>(c + 16 * 7);
+  raw[4 + 2 * 7] = load_u16(a + 16 * 7 + 2);
 }
 
 __device__ __forceinline__ void finish_sb_s(const uint8_t* p, const uint32_t raw[kRawS], SbRegs& r) {
