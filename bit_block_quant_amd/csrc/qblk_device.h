@@ -59,6 +59,35 @@ __device__ __forceinline__ int code_of(float v, float s, float lo, float hi) {
   return static_cast<int>(t);
 }
 
+// The same codes for 8 values against one scale s, with the division done
+// once: r = 1/s (IEEE; 0 when s = 0).  The rounded product y = v*r is within
+// 2.5 ulp of the IEEE quotient v/s (r and the product each add at most half an
+// ulp of relative error), so when y is more than 2^-14 from every
+// half-integer -- 3 ulp or more while |y| < 256; larger quotients clamp
+// either way -- the quotient rounds (half away from zero) to the integer
+// nearest y, which v_rndne gives.  Values that close to a half-integer take
+// the exact quotient (a rare, wave-uniform branch).
+__device__ __forceinline__ void codes8(const float v[8], float s, float lo, float hi, int n[8]) {
+  const float r = s == 0.0f ? 0.0f : 1.0f / s;
+  float q[8];
+  uint64_t m[8], any = 0;  // per value: the lanes whose product is near a half-integer
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float y = v[i] * r;
+    q[i] = __builtin_rintf(y);
+    m[i] = __builtin_amdgcn_ballot_w64(__builtin_fabsf(y - q[i]) >= 0.5f - 0x1p-14f);  // y - q exact
+    any |= m[i];
+  }
+  if (any) {
+    const uint64_t bit = uint64_t(1) << (threadIdx.x & 63);
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+      if (m[i] & bit) q[i] = rha(qdiv(v[i], s));
+  }
+#pragma unroll
+  for (int i = 0; i < 8; i++) n[i] = static_cast<int>(__builtin_amdgcn_fmed3f(q[i], lo, hi));
+}
+
 // Optimisation barrier: the value is materialised in a VGPR, so a following
 // narrowing conversion cannot be fused with the arithmetic that produced it
 // (a fused v_fma_mix with a +0 addend would turn -0 into +0).

@@ -140,8 +140,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_q4_0(const void* __restrict_
   const uint16_t d16 = f32_to_f16_bits(amax / 7.0f);
   const float d = f16_bits_to_f32(d16);
   int n[8];
+  codes8(v, d, -8.0f, 7.0f, n);
 #pragma unroll
-  for (int i = 0; i < 8; i++) n[i] = code_of(v[i], d, -8.0f, 7.0f) + 8;
+  for (int i = 0; i < 8; i++) n[i] += 8;
   uint32_t w0, w1;
   pack_group(n, w0, w1);
   if (valid) {
@@ -230,8 +231,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_sb4(const void* __restrict__
     for (int i = 0; i < 8; i++) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
     amax = group_max<4>(amax);
     const float d = f16_bits_to_f32(f32_to_f16_bits(amax / 7.0f));
+    codes8(x, d, -8.0f, 7.0f, n);
 #pragma unroll
-    for (int i = 0; i < 8; i++) n[i] = code_of(x[i], d, -8.0f, 7.0f) + 8;
+    for (int i = 0; i < 8; i++) n[i] += 8;
     // second level: the eight fp16 scales -> INT8 under one fp16 super-scale
     float smax = d;
 #pragma unroll
@@ -253,8 +255,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_sb4(const void* __restrict__
     mx = group_max<4>(mx);
     const float s = f16_bits_to_f32(f32_to_f16_bits((mx - mn) / 15.0f));
     const float a = f16_bits_to_f32(f32_to_f16_bits(mn));
+    float xa[8];
 #pragma unroll
-    for (int i = 0; i < 8; i++) n[i] = code_of(x[i] - a, s, 0.0f, 15.0f);
+    for (int i = 0; i < 8; i++) xa[i] = x[i] - a;
+    codes8(xa, s, 0.0f, 15.0f, n);
     float smax = s, amax = __builtin_fabsf(a);
 #pragma unroll
     for (int m = 4; m < 32; m <<= 1) {
@@ -278,6 +282,148 @@ __global__ __launch_bounds__(kThreads) void k_quant_sb4(const void* __restrict__
   if (valid && u < 2) lds_put8(stage, sl * B + (AFFINE ? 20 : 10) + 16 * j + 8 * u, w0, w1);
   __syncthreads();
   const int64_t ns = nsb - sb0 < 8 ? nsb - sb0 : 8;
+  lds_to_global(stage, out + sb0 * B, static_cast<int>(ns * B));
+}
+
+// ------------------------------------------ one 32-weight group per thread
+// The same quantizers with each thread owning a whole 32-weight group (a
+// Q4_0 block or a sub-block): the group's extremes, its scale and its nibble
+// pairs (byte b = code b | code b+16 << 4) need no cross-lane traffic, and
+// the per-group divisions are done once per 32 weights instead of once per 8.
+// A workgroup covers 256 groups (8192 weights): 256 Q4_0 blocks (4608 bytes)
+// or 32 super-blocks (4416 / 4736 bytes), all multiples of 16.
+template <int DT>
+__device__ __forceinline__ void load32(const void* w, int64_t idx, bool valid, float v[32]) {
+#pragma unroll
+  for (int q = 0; q < 4; q++) load8<DT>(w, idx + 8 * q, valid, v + 8 * q);
+}
+
+// the 16 qs bytes of a group from its 32 codes, as 4 words
+__device__ __forceinline__ void pack32(const int n[32], uint32_t qw[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int b = 0; b < 4; b++) x |= static_cast<uint32_t>(n[4 * q + b] | (n[4 * q + b + 16] << 4)) << (8 * b);
+    qw[q] = x;
+  }
+}
+
+__device__ __forceinline__ void lds_put16_a2(uint8_t* lds, int off, const uint32_t qw[4]) {
+  uint16_t* p = reinterpret_cast<uint16_t*>(lds + off);  // off is even
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    p[2 * q] = static_cast<uint16_t>(qw[q]);
+    p[2 * q + 1] = static_cast<uint16_t>(qw[q] >> 16);
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_quant_q4_0_g(const void* __restrict__ w,
+                                                           uint8_t* __restrict__ out,
+                                                           int64_t nblocks) {
+  __shared__ uint4 stage4[kThreads * 18 / 16];
+  uint8_t* stage = reinterpret_cast<uint8_t*>(stage4);
+  const int t = threadIdx.x;
+  const int64_t blk0 = static_cast<int64_t>(blockIdx.x) * kThreads;
+  const bool valid = blk0 + t < nblocks;
+  float v[32];
+  load32<DT>(w, (blk0 + t) * 32, valid, v);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; i++) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+  const uint16_t d16 = f32_to_f16_bits(amax / 7.0f);
+  const float d = f16_bits_to_f32(d16);
+  int n[32];
+#pragma unroll
+  for (int q = 0; q < 4; q++) codes8(v + 8 * q, d, -8.0f, 7.0f, n + 8 * q);
+#pragma unroll
+  for (int i = 0; i < 32; i++) n[i] += 8;
+  uint32_t qw[4];
+  pack32(n, qw);
+  if (valid) {
+    *reinterpret_cast<uint16_t*>(stage + t * 18) = d16;
+    lds_put16_a2(stage, t * 18 + 2, qw);
+  }
+  __syncthreads();
+  const int64_t nb = nblocks - blk0 < kThreads ? nblocks - blk0 : kThreads;
+  lds_to_global(stage, out + blk0 * 18, static_cast<int>(nb * 18));
+}
+
+// Threads 8s..8s+7 own super-block s (0..31) of the workgroup, thread j of
+// the eight owning sub-block j.
+template <int DT, bool AFFINE>
+__global__ __launch_bounds__(kThreads) void k_quant_sb4_g(const void* __restrict__ w,
+                                                          uint8_t* __restrict__ out,
+                                                          int64_t nsb) {
+  constexpr int B = AFFINE ? 148 : 138;
+  constexpr int SBW = kThreads / 8;  // super-blocks per workgroup
+  __shared__ uint4 stage4[SBW * B / 16];
+  uint8_t* stage = reinterpret_cast<uint8_t*>(stage4);
+  const int t = threadIdx.x;
+  const int64_t sb0 = static_cast<int64_t>(blockIdx.x) * SBW;
+  const int sl = t >> 3, j = t & 7;
+  const bool valid = sb0 + sl < nsb;
+  float x[32];
+  load32<DT>(w, (sb0 + sl) * 256 + 32 * j, valid, x);
+  uint8_t* blk = stage + sl * B;
+  int n[32];
+  uint32_t qw[4];
+  if constexpr (!AFFINE) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; i++) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+    const float d = f16_bits_to_f32(f32_to_f16_bits(amax / 7.0f));
+#pragma unroll
+    for (int q = 0; q < 4; q++) codes8(x + 8 * q, d, -8.0f, 7.0f, n + 8 * q);
+#pragma unroll
+    for (int i = 0; i < 32; i++) n[i] += 8;
+    pack32(n, qw);
+    float smax = d;
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) smax = __builtin_fmaxf(smax, __shfl_xor(smax, m, kWave));
+    const uint16_t S16 = f32_to_f16_bits(smax / 127.0f);
+    const int sc = code_of(d, f16_bits_to_f32(S16), -127.0f, 127.0f);
+    if (valid) {
+      if (j == 0) *reinterpret_cast<uint16_t*>(blk) = S16;
+      blk[2 + j] = static_cast<uint8_t>(sc);
+      lds_put16_a2(blk, 10 + 16 * j, qw);
+    }
+  } else {
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 32; i++) {
+      mn = __builtin_fminf(mn, x[i]);
+      mx = __builtin_fmaxf(mx, x[i]);
+    }
+    const float s = f16_bits_to_f32(f32_to_f16_bits((mx - mn) / 15.0f));
+    const float a = f16_bits_to_f32(f32_to_f16_bits(mn));
+#pragma unroll
+    for (int i = 0; i < 32; i++) x[i] = x[i] - a;
+#pragma unroll
+    for (int q = 0; q < 4; q++) codes8(x + 8 * q, s, 0.0f, 15.0f, n + 8 * q);
+    pack32(n, qw);
+    float smax = s, amax = __builtin_fabsf(a);
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) {
+      smax = __builtin_fmaxf(smax, __shfl_xor(smax, m, kWave));
+      amax = __builtin_fmaxf(amax, __shfl_xor(amax, m, kWave));
+    }
+    const uint16_t Ss16 = f32_to_f16_bits(smax / 127.0f);
+    const uint16_t Sa16 = f32_to_f16_bits(amax / 127.0f);
+    const int sc = code_of(s, f16_bits_to_f32(Ss16), -127.0f, 127.0f);
+    const int ac = code_of(a, f16_bits_to_f32(Sa16), -127.0f, 127.0f);
+    if (valid) {
+      if (j == 0) reinterpret_cast<uint32_t*>(blk)[0] = Ss16 | (static_cast<uint32_t>(Sa16) << 16);
+      blk[4 + j] = static_cast<uint8_t>(sc);
+      blk[12 + j] = static_cast<uint8_t>(ac);
+      uint32_t* qd = reinterpret_cast<uint32_t*>(blk + 20 + 16 * j);  // 4-byte aligned
+#pragma unroll
+      for (int q = 0; q < 4; q++) qd[q] = qw[q];
+    }
+  }
+  __syncthreads();
+  const int64_t ns = nsb - sb0 < SBW ? nsb - sb0 : SBW;
   lds_to_global(stage, out + sb0 * B, static_cast<int>(ns * B));
 }
 
@@ -348,11 +494,16 @@ inline unsigned grid_for(int64_t weights) {
 hipError_t launch_quantize_q4_0(const void* w, int wt, int64_t rows, int64_t k, void* blocks,
                                 hipStream_t s) {
   const int64_t nb = rows * k / 32;
-  const unsigned g = grid_for(rows * k);
   uint8_t* out = static_cast<uint8_t*>(blocks);
-  if (wt == QBLK_F32) hipLaunchKernelGGL(k_quant_q4_0<QBLK_F32>, dim3(g), dim3(kThreads), 0, s, w, out, nb);
-  else if (wt == QBLK_F16) hipLaunchKernelGGL(k_quant_q4_0<QBLK_F16>, dim3(g), dim3(kThreads), 0, s, w, out, nb);
-  else hipLaunchKernelGGL(k_quant_q4_0<QBLK_BF16>, dim3(g), dim3(kThreads), 0, s, w, out, nb);
+  if (wt == QBLK_F32) {  // 8 weights per thread: 32-byte coalesced loads
+    const unsigned g = grid_for(rows * k);
+    hipLaunchKernelGGL(k_quant_q4_0<QBLK_F32>, dim3(g), dim3(kThreads), 0, s, w, out, nb);
+    return hipGetLastError();
+  }
+  // 16-bit inputs: one 32-weight block per thread (64-byte loads)
+  const unsigned g = static_cast<unsigned>((nb + kThreads - 1) / kThreads);
+  if (wt == QBLK_F16) hipLaunchKernelGGL(k_quant_q4_0_g<QBLK_F16>, dim3(g), dim3(kThreads), 0, s, w, out, nb);
+  else hipLaunchKernelGGL(k_quant_q4_0_g<QBLK_BF16>, dim3(g), dim3(kThreads), 0, s, w, out, nb);
   return hipGetLastError();
 }
 
@@ -365,10 +516,15 @@ hipError_t launch_quantize_q4_0_ref(const float* w, int64_t rows, int64_t k, voi
 
 template <bool A>
 static void launch_sb4_t(const void* w, int wt, int64_t nsb, uint8_t* out, hipStream_t s) {
-  const unsigned g = static_cast<unsigned>((nsb + 7) / 8);
-  if (wt == QBLK_F32) hipLaunchKernelGGL((k_quant_sb4<QBLK_F32, A>), dim3(g), dim3(kThreads), 0, s, w, out, nsb);
-  else if (wt == QBLK_F16) hipLaunchKernelGGL((k_quant_sb4<QBLK_F16, A>), dim3(g), dim3(kThreads), 0, s, w, out, nsb);
-  else hipLaunchKernelGGL((k_quant_sb4<QBLK_BF16, A>), dim3(g), dim3(kThreads), 0, s, w, out, nsb);
+  if (wt == QBLK_F32) {  // 8 weights per thread: 32-byte coalesced loads
+    const unsigned g = static_cast<unsigned>((nsb + 7) / 8);
+    hipLaunchKernelGGL((k_quant_sb4<QBLK_F32, A>), dim3(g), dim3(kThreads), 0, s, w, out, nsb);
+    return;
+  }
+  // 16-bit inputs: one sub-block per thread (64-byte loads)
+  const unsigned g = static_cast<unsigned>((nsb + kThreads / 8 - 1) / (kThreads / 8));
+  if (wt == QBLK_F16) hipLaunchKernelGGL((k_quant_sb4_g<QBLK_F16, A>), dim3(g), dim3(kThreads), 0, s, w, out, nsb);
+  else hipLaunchKernelGGL((k_quant_sb4_g<QBLK_BF16, A>), dim3(g), dim3(kThreads), 0, s, w, out, nsb);
 }
 
 hipError_t launch_quantize_sb4(const void* w, int wt, int64_t rows, int64_t k, int affine,
