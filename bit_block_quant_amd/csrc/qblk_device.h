@@ -88,6 +88,54 @@ __device__ __forceinline__ void codes8(const float v[8], float s, float lo, floa
   for (int i = 0; i < 8; i++) n[i] = static_cast<int>(__builtin_amdgcn_fmed3f(q[i], lo, hi));
 }
 
+// The clamped codes as floats (same rule as codes8) for N values whose
+// products y = v*r are already formed (v: the exact dividends, used only on
+// the slow path).
+template <int N>
+__device__ __forceinline__ void codes_f(const float v[N], float y[N], float s, float lo, float hi) {
+  uint64_t m[N], any = 0;
+#pragma unroll
+  for (int i = 0; i < N; i++) {
+    const float q = __builtin_rintf(y[i]);
+    m[i] = __builtin_amdgcn_ballot_w64(__builtin_fabsf(y[i] - q) >= 0.5f - 0x1p-14f);
+    any |= m[i];
+    y[i] = q;
+  }
+  if (any) {
+    const uint64_t bit = uint64_t(1) << (threadIdx.x & 63);
+#pragma unroll
+    for (int i = 0; i < N; i++)
+      if (m[i] & bit) y[i] = rha(qdiv(v[i], s));
+  }
+#pragma unroll
+  for (int i = 0; i < N; i++) y[i] = __builtin_amdgcn_fmed3f(y[i], lo, hi);
+}
+
+// fp16 half (lo or hi) of a packed word times m plus c, one rounding
+// (v_fma_mix: the fp16 operand is widened exactly).
+__device__ __forceinline__ float mix_lo(uint32_t h, float m, float c) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(m), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float mix_hi(uint32_t h, float m, float c) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(m), "v"(c));
+  return r;
+}
+
+// 16 qs bytes from 32 clamped codes (as floats): byte b = c[b] + 16*c[b+16] + add
+__device__ __forceinline__ void pack32f(const float c[32], float add, uint32_t qw[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int b = 0; b < 4; b++)
+      x = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(c[4 * q + b + 16], 16.0f, c[4 * q + b]) + add, b, x);
+    qw[q] = x;
+  }
+}
+
 // Optimisation barrier: the value is materialised in a VGPR, so a following
 // narrowing conversion cannot be fused with the arithmetic that produced it
 // (a fused v_fma_mix with a +0 addend would turn -0 into +0).

@@ -292,21 +292,95 @@ __global__ __launch_bounds__(kThreads) void k_quant_sb4(const void* __restrict__
 // the per-group divisions are done once per 32 weights instead of once per 8.
 // A workgroup covers 256 groups (8192 weights): 256 Q4_0 blocks (4608 bytes)
 // or 32 super-blocks (4416 / 4736 bytes), all multiples of 16.
-template <int DT>
-__device__ __forceinline__ void load32(const void* w, int64_t idx, bool valid, float v[32]) {
-#pragma unroll
-  for (int q = 0; q < 4; q++) load8<DT>(w, idx + 8 * q, valid, v + 8 * q);
-}
+// 16-bit inputs stay packed (two per word) until the products: extremes
+// with packed 16-bit max/min, dividends and products with v_fma_mix (fp16)
+// or an exact widening to fp32 (bf16).
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 
-// the 16 qs bytes of a group from its 32 codes, as 4 words
-__device__ __forceinline__ void pack32(const int n[32], uint32_t qw[4]) {
+__device__ __forceinline__ void load_h16(const void* w, int64_t idx, bool valid, uint32_t h[16]) {
 #pragma unroll
   for (int q = 0; q < 4; q++) {
-    uint32_t x = 0;
-#pragma unroll
-    for (int b = 0; b < 4; b++) x |= static_cast<uint32_t>(n[4 * q + b] | (n[4 * q + b + 16] << 4)) << (8 * b);
-    qw[q] = x;
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (valid) u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(w) + idx + 8 * q);
+    h[4 * q] = u.x;
+    h[4 * q + 1] = u.y;
+    h[4 * q + 2] = u.z;
+    h[4 * q + 3] = u.w;
   }
+}
+
+template <int DT>
+__device__ __forceinline__ float widen16(uint32_t bits) {
+  return DT == QBLK_F16 ? f16_bits_to_f32(bits) : bf16_bits_to_f32(bits);
+}
+
+// max |x| of the 32 values: with the sign cleared, finite fp16 and bf16
+// patterns order like unsigned integers
+template <int DT>
+__device__ __forceinline__ float absmax16(const uint32_t h[16]) {
+  u16x2_t m = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; i++) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, h[i] & 0x7fff7fffu));
+  return widen16<DT>(m.x > m.y ? m.x : m.y);
+}
+
+template <int DT>
+__device__ __forceinline__ void minmax16(const uint32_t h[16], float& mn, float& mx) {
+  if constexpr (DT == QBLK_F16) {
+    half2_t lo = __builtin_bit_cast(half2_t, h[0]), hi = lo;
+#pragma unroll
+    for (int i = 1; i < 16; i++) {
+      lo = __builtin_elementwise_min(lo, __builtin_bit_cast(half2_t, h[i]));
+      hi = __builtin_elementwise_max(hi, __builtin_bit_cast(half2_t, h[i]));
+    }
+    mn = __builtin_fminf(static_cast<float>(lo.x), static_cast<float>(lo.y));
+    mx = __builtin_fmaxf(static_cast<float>(hi.x), static_cast<float>(hi.y));
+  } else {
+    mn = mx = widen16<DT>(h[0] & 0xffffu);
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const float a = widen16<DT>(h[i] & 0xffffu), b = widen16<DT>(h[i] >> 16);
+      mn = __builtin_fminf(mn, __builtin_fminf(a, b));
+      mx = __builtin_fmaxf(mx, __builtin_fmaxf(a, b));
+    }
+  }
+}
+
+// Codes of the 32 values (x - a)/s (a = 0: x/s) clamped to [lo, hi], packed
+// as byte b = code b + 16 * code b+16 + add (add = 136 stores code+8 for the
+// signed formats).  Dividend fl(x - a) and product as in codes8.
+template <int DT, bool OFFSET>
+__device__ __forceinline__ void codes16(const uint32_t h[16], float a, float s, float lo, float hi,
+                                        float add, uint32_t qw[4]) {
+  const float r = s == 0.0f ? 0.0f : 1.0f / s;
+  float v[32], y[32];
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    if constexpr (DT == QBLK_F16) {
+      if constexpr (OFFSET) {
+        v[2 * i] = mix_lo(h[i], 1.0f, -a);
+        v[2 * i + 1] = mix_hi(h[i], 1.0f, -a);
+        y[2 * i] = v[2 * i] * r;
+        y[2 * i + 1] = v[2 * i + 1] * r;
+      } else {
+        v[2 * i] = f16_bits_to_f32(h[i] & 0xffffu);  // only read on the slow path
+        v[2 * i + 1] = f16_bits_to_f32(h[i] >> 16);
+        y[2 * i] = mix_lo(h[i], r, 0.0f);
+        y[2 * i + 1] = mix_hi(h[i], r, 0.0f);
+      }
+    } else {
+      v[2 * i] = widen16<DT>(h[i] & 0xffffu);
+      v[2 * i + 1] = widen16<DT>(h[i] >> 16);
+      if constexpr (OFFSET) {
+        v[2 * i] = v[2 * i] - a;
+        v[2 * i + 1] = v[2 * i + 1] - a;
+      }
+      y[2 * i] = v[2 * i] * r;
+      y[2 * i + 1] = v[2 * i + 1] * r;
+    }
+  }
+  codes_f<32>(v, y, s, lo, hi);
+  pack32f(y, add, qw);
 }
 
 __device__ __forceinline__ void lds_put16_a2(uint8_t* lds, int off, const uint32_t qw[4]) {
@@ -327,20 +401,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_q4_0_g(const void* __restric
   const int t = threadIdx.x;
   const int64_t blk0 = static_cast<int64_t>(blockIdx.x) * kThreads;
   const bool valid = blk0 + t < nblocks;
-  float v[32];
-  load32<DT>(w, (blk0 + t) * 32, valid, v);
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; i++) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+  uint32_t h[16];
+  load_h16(w, (blk0 + t) * 32, valid, h);
+  const float amax = absmax16<DT>(h);
   const uint16_t d16 = f32_to_f16_bits(amax / 7.0f);
   const float d = f16_bits_to_f32(d16);
-  int n[32];
-#pragma unroll
-  for (int q = 0; q < 4; q++) codes8(v + 8 * q, d, -8.0f, 7.0f, n + 8 * q);
-#pragma unroll
-  for (int i = 0; i < 32; i++) n[i] += 8;
   uint32_t qw[4];
-  pack32(n, qw);
+  codes16<DT, false>(h, 0.0f, d, -8.0f, 7.0f, 136.0f, qw);
   if (valid) {
     *reinterpret_cast<uint16_t*>(stage + t * 18) = d16;
     lds_put16_a2(stage, t * 18 + 2, qw);
@@ -364,21 +431,14 @@ __global__ __launch_bounds__(kThreads) void k_quant_sb4_g(const void* __restrict
   const int64_t sb0 = static_cast<int64_t>(blockIdx.x) * SBW;
   const int sl = t >> 3, j = t & 7;
   const bool valid = sb0 + sl < nsb;
-  float x[32];
-  load32<DT>(w, (sb0 + sl) * 256 + 32 * j, valid, x);
+  uint32_t h[16];
+  load_h16(w, (sb0 + sl) * 256 + 32 * j, valid, h);
   uint8_t* blk = stage + sl * B;
-  int n[32];
   uint32_t qw[4];
   if constexpr (!AFFINE) {
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; i++) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+    const float amax = absmax16<DT>(h);
     const float d = f16_bits_to_f32(f32_to_f16_bits(amax / 7.0f));
-#pragma unroll
-    for (int q = 0; q < 4; q++) codes8(x + 8 * q, d, -8.0f, 7.0f, n + 8 * q);
-#pragma unroll
-    for (int i = 0; i < 32; i++) n[i] += 8;
-    pack32(n, qw);
+    codes16<DT, false>(h, 0.0f, d, -8.0f, 7.0f, 136.0f, qw);
     float smax = d;
 #pragma unroll
     for (int m = 1; m < 8; m <<= 1) smax = __builtin_fmaxf(smax, __shfl_xor(smax, m, kWave));
@@ -390,19 +450,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_sb4_g(const void* __restrict
       lds_put16_a2(blk, 10 + 16 * j, qw);
     }
   } else {
-    float mn = x[0], mx = x[0];
-#pragma unroll
-    for (int i = 1; i < 32; i++) {
-      mn = __builtin_fminf(mn, x[i]);
-      mx = __builtin_fmaxf(mx, x[i]);
-    }
+    float mn, mx;
+    minmax16<DT>(h, mn, mx);
     const float s = f16_bits_to_f32(f32_to_f16_bits((mx - mn) / 15.0f));
     const float a = f16_bits_to_f32(f32_to_f16_bits(mn));
-#pragma unroll
-    for (int i = 0; i < 32; i++) x[i] = x[i] - a;
-#pragma unroll
-    for (int q = 0; q < 4; q++) codes8(x + 8 * q, s, 0.0f, 15.0f, n + 8 * q);
-    pack32(n, qw);
+    codes16<DT, true>(h, a, s, 0.0f, 15.0f, 0.0f, qw);
     float smax = s, amax = __builtin_fabsf(a);
 #pragma unroll
     for (int m = 1; m < 8; m <<= 1) {
