@@ -3,7 +3,7 @@
 Argument marshalling only: every step runs in the library's HIP kernels.
 PyTorch supplies device memory and the stream; tensors must live on a GPU.
 If the library is not built this module raises on import -- there is no CPU
-fallback.  Build with ``python -m bit_block_quant_amd.build``.
+fallback.  Build with ``python bit_block_quant_amd/build.py`` (or ``__graft_entry__.build()``).
 
     blocks = qblk.quantize(w, qblk.SB4)          # w: (rows, k) f32/f16/bf16
     y      = qblk.gemv(blocks, qblk.SB4, m, k, x) # x: (k,) f32/f16/bf16 -> (m,) f32
@@ -45,7 +45,7 @@ class QblkError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"libqblk.so not found at {LIB_PATH}; build it with `python -m bit_block_quant_amd.build`")
+            f"libqblk.so not found at {LIB_PATH}; build it with `python bit_block_quant_amd/build.py`")
     L = C.CDLL(LIB_PATH)
     p, i64, i32 = C.c_void_p, C.c_int64, C.c_int
     L.qblk_block_bytes.argtypes, L.qblk_block_bytes.restype = [i32], C.c_size_t

@@ -1,6 +1,7 @@
 """Build libqblk.so (the C-ABI library with the gfx950 kernels) in-tree.
 
-    python -m bit_block_quant_amd.build [-v]
+    python bit_block_quant_amd/build.py [-v]     (by path: importing the package
+                                                 loads the library it builds)
 
 hipcc cross-compiles for gfx950 without a GPU present.  Flags:
   -ffp-contract=off            no implicit fused multiply-add: dequantized
