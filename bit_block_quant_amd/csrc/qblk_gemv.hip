@@ -475,9 +475,13 @@ __global__ __launch_bounds__(kThreadsH) void k_gemv_h(const uint8_t* __restrict_
   }
 }
 
-__global__ void k_fill_zero(float* y, int64_t n) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) y[i] = 0.0f;
+// y[0, n) = 0: 16-byte stores (y is 16-byte aligned), a scalar tail.
+__global__ __launch_bounds__(256) void k_fill_zero(float* y, int64_t n) {
+  const int64_t n4 = n >> 2;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n4; i += stride)
+    reinterpret_cast<float4*>(y)[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (blockIdx.x == 0 && threadIdx.x < (n & 3)) y[(n4 << 2) + threadIdx.x] = 0.0f;
 }
 
 constexpr int kRows = 4;
@@ -570,8 +574,11 @@ hipError_t launch_gemv(int fmt, const void* blocks, int64_t m, int64_t k, const 
 
 hipError_t launch_fill_zero(float* y, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_fill_zero, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
-                     y, n);
+  // grid-stride over float4s: at most 8 workgroups per CU
+  int64_t g = ((n >> 2) + 255) / 256;
+  const int64_t cap = static_cast<int64_t>(cu_count()) * 8;
+  g = g < 1 ? 1 : (g > cap ? cap : g);
+  hipLaunchKernelGGL(k_fill_zero, dim3(static_cast<unsigned>(g)), dim3(256), 0, s, y, n);
   return hipGetLastError();
 }
 
