@@ -831,18 +831,18 @@ hipError_t launch_gemm(int fmt, const void* blocks, int64_t m, int64_t k, const 
   if (fmt == QBLK_SB4) {
     if (n <= 16) return launch_s<2, 1, 2>(blocks, m, k, x, n, y, s);
     if (n <= 32) return launch_s<2, 2, 2>(blocks, m, k, x, n, y, s);
-    if (n <= 64) return launch_t<QBLK_SB4, 1, 4>(blocks, m, k, x, n, y, s);
+    if (n <= 64) return launch_t<QBLK_SB4, 2, 4>(blocks, m, k, x, n, y, s);
     return launch_w<4>(blocks, m, k, x, n, y, s);
   }
   if (fmt == QBLK_Q4_0) {
     if (n <= 16) return launch_t<QBLK_Q4_0, 1, 1>(blocks, m, k, x, n, y, s);
     if (n <= 32) return launch_t<QBLK_Q4_0, 1, 2>(blocks, m, k, x, n, y, s);
-    if (n <= 64) return launch_t<QBLK_Q4_0, 1, 4>(blocks, m, k, x, n, y, s);
+    if (n <= 64) return launch_t<QBLK_Q4_0, 2, 4>(blocks, m, k, x, n, y, s);
     return launch_t<QBLK_Q4_0, 2, 4>(blocks, m, k, x, n, y, s);
   }
   if (n <= 16) return launch_t<QBLK_SB4_AFFINE, 1, 1>(blocks, m, k, x, n, y, s);
   if (n <= 32) return launch_t<QBLK_SB4_AFFINE, 1, 2>(blocks, m, k, x, n, y, s);
-  if (n <= 64) return launch_t<QBLK_SB4_AFFINE, 1, 4>(blocks, m, k, x, n, y, s);
+  if (n <= 64) return launch_t<QBLK_SB4_AFFINE, 2, 4>(blocks, m, k, x, n, y, s);
   return launch_t<QBLK_SB4_AFFINE, 2, 4>(blocks, m, k, x, n, y, s);
 }
 
