@@ -395,62 +395,153 @@ __device__ __forceinline__ void decode16(uint32_t d0, uint32_t d1, bf16x8v_t& lo
                                                 pk_bf16(off_i4<0>(bh), off_i4<1>(bh)), pk_bf16(off_i4<2>(bh), off_i4<3>(bh))));
 }
 
-constexpr int kRawW = 3 + 8 * 3;  // header dwords + three dwords per sub-block
-
-// Fetch what lane half h needs of one super-block at p: the header (dword
-// aligned 12 bytes holding its 10 bytes, never before the row's first byte
-// since row starts are even) and, per sub-block, code bytes 8h..8h+7 at A,
-// from the dwords at A & ~3: three of them for sub-blocks 0..6 (the extra
-// bytes belong to the next sub-block), for sub-block 7 two dwords plus the
-// 2 bytes at A+6, so nothing past the super-block is read.
-__device__ __forceinline__ void load_sb_w(const uint8_t* p, int h, uint32_t raw[kRawW]) {
-  // p - (p & 3) keeps the pointer's provenance, so these stay global loads
-  const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
-  const u32x3_a4 hd = *reinterpret_cast<const u32x3_a4*>(p - mis);
-  raw[0] = hd.x;
-  raw[1] = hd.y;
-  raw[2] = hd.z;
-  const uint8_t* a = p + 10 + 8 * h;                      // code bytes of sub-block 0
-  const uint8_t* c = p - mis + ((mis + 10 + 8 * h) & ~3u);  // a & ~3
-#pragma unroll
-  for (int s = 0; s < 7; s++) {
-    const u32x3_a4 v = *reinterpret_cast<const u32x3_a4*>(c + 16 * s);
-    raw[3 + 3 * s] = v.x;
-    raw[4 + 3 * s] = v.y;
-    raw[5 + 3 * s] = v.z;
-  }
-  const u32x2_a4 v = *reinterpret_cast<const u32x2_a4*>(c + 16 * 7);
-  raw[3 + 3 * 7] = v.x;
-  raw[4 + 3 * 7] = v.y;
-  raw[5 + 3 * 7] = load_u16(a + 16 * 7 + 6);
-}
-
+// Per lane half h, the wide kernel needs code bytes 8h..8h+7 of every
+// sub-block of a 256-weight group (16 codes), the 8 sub-block scales and, for
+// Type 1, the offsets of sub-blocks 2q+h (q = 0..3).
 struct SbRegsW {
   uint32_t code[8][2];
-  float scale[8];  // 16 * S * sc_j
+  float scale[8];  // 16 * (scale of sub-block j)
+  float corr[4];   // Type 1: 8*s_j + a_j for j = 2q + h
 };
 
-__device__ __forceinline__ void finish_sb_w(const uint8_t* p, const uint32_t raw[kRawW], SbRegsW& r) {
-  const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
-  const uint32_t w0 = __builtin_amdgcn_alignbyte(raw[1], raw[0], sh);  // S16, sc0, sc1
-  const uint32_t w1 = __builtin_amdgcn_alignbyte(raw[2], raw[1], sh);  // sc2..sc5
-  const uint32_t w2 = raw[2] >> (8 * sh);                              // sc6, sc7
-  const float S16 = f16_bits_to_f32(w0 & 0xffffu) * 16.0f;
-  const uint32_t sc03 = (w0 >> 16) | (w1 << 16), sc47 = (w1 >> 16) | (w2 << 16);
-  // code bytes start at p + 10 (+ 8h): offset (sh + 2) & 3 inside the aligned dwords
-  const uint32_t cs = (sh + 2) & 3u;
-#pragma unroll
-  for (int s = 0; s < 8; s++) {
-    r.code[s][0] = __builtin_amdgcn_alignbyte(raw[4 + 3 * s], raw[3 + 3 * s], cs);
-    r.code[s][1] = __builtin_amdgcn_alignbyte(raw[5 + 3 * s], raw[4 + 3 * s], cs);
-    const uint32_t word = s < 4 ? sc03 : sc47;
-    const int8_t c = static_cast<int8_t>((word >> (8 * (s & 3))) & 0xffu);
-    r.scale[s] = S16 * static_cast<float>(c);
-  }
-}
+template <int FMT>
+struct GroupW;
 
-template <int T32, bool SPLIT>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm_sb4_w(const uint8_t* __restrict__ W,
+template <>
+struct GroupW<QBLK_SB4> {
+  static constexpr int GB = 138, RAW = 3 + 8 * 3;
+  // the header (dword aligned 12 bytes holding its 10 bytes, never before the
+  // row's first byte since row starts are even) and, per sub-block, code
+  // bytes 8h..8h+7 at A from the dwords at A & ~3: three of them for
+  // sub-blocks 0..6 (the extra bytes belong to the next sub-block), for
+  // sub-block 7 two dwords plus the 2 bytes at A+6, so nothing past the
+  // super-block is read
+  static __device__ __forceinline__ void load(const uint8_t* p, int h, uint32_t raw[RAW]) {
+    // p - (p & 3) keeps the pointer's provenance, so these stay global loads
+    const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
+    const u32x3_a4 hd = *reinterpret_cast<const u32x3_a4*>(p - mis);
+    raw[0] = hd.x;
+    raw[1] = hd.y;
+    raw[2] = hd.z;
+    const uint8_t* a = p + 10 + 8 * h;                      // code bytes of sub-block 0
+    const uint8_t* c = p - mis + ((mis + 10 + 8 * h) & ~3u);  // a & ~3
+#pragma unroll
+    for (int s = 0; s < 7; s++) {
+      const u32x3_a4 v = *reinterpret_cast<const u32x3_a4*>(c + 16 * s);
+      raw[3 + 3 * s] = v.x;
+      raw[4 + 3 * s] = v.y;
+      raw[5 + 3 * s] = v.z;
+    }
+    const u32x2_a4 v = *reinterpret_cast<const u32x2_a4*>(c + 16 * 7);
+    raw[3 + 3 * 7] = v.x;
+    raw[4 + 3 * 7] = v.y;
+    raw[5 + 3 * 7] = load_u16(a + 16 * 7 + 6);
+  }
+  static __device__ __forceinline__ void finish(const uint8_t* p, int, const uint32_t raw[RAW], SbRegsW& r) {
+    const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
+    const uint32_t w0 = __builtin_amdgcn_alignbyte(raw[1], raw[0], sh);  // S16, sc0, sc1
+    const uint32_t w1 = __builtin_amdgcn_alignbyte(raw[2], raw[1], sh);  // sc2..sc5
+    const uint32_t w2 = raw[2] >> (8 * sh);                              // sc6, sc7
+    const float S16 = f16_bits_to_f32(w0 & 0xffffu) * 16.0f;
+    const uint32_t sc03 = (w0 >> 16) | (w1 << 16), sc47 = (w1 >> 16) | (w2 << 16);
+    // code bytes start at p + 10 (+ 8h): offset (sh + 2) & 3 inside the aligned dwords
+    const uint32_t cs = (sh + 2) & 3u;
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+      r.code[s][0] = __builtin_amdgcn_alignbyte(raw[4 + 3 * s], raw[3 + 3 * s], cs);
+      r.code[s][1] = __builtin_amdgcn_alignbyte(raw[5 + 3 * s], raw[4 + 3 * s], cs);
+      const uint32_t word = s < 4 ? sc03 : sc47;
+      const int8_t c = static_cast<int8_t>((word >> (8 * (s & 3))) & 0xffu);
+      r.scale[s] = S16 * static_cast<float>(c);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; q++) r.corr[q] = 0.0f;
+  }
+};
+
+template <>
+struct GroupW<QBLK_Q4_0> {
+  // p is 4-byte aligned (rows are whole multiples of 144 bytes).  Block j
+  // starts at 18j: for even j its code bytes 8h.. sit 2 bytes past a dword
+  // boundary (three dwords from 18j+8h, ending at most at byte 128 of the
+  // group), for odd j on one (two dwords, ending at most at byte 144).
+  static constexpr int GB = 144, RAW = 8 + 4 * 3 + 4 * 2;
+  static __device__ __forceinline__ void load(const uint8_t* p, int h, uint32_t raw[RAW]) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      raw[j] = *reinterpret_cast<const uint32_t*>(p + ((18 * j) & ~3));  // d16 in the low or high half
+      uint32_t* r = raw + 8 + (j >> 1) * 5 + (j & 1) * 3;
+      if (j & 1) {
+        const u32x2_a4 v = *reinterpret_cast<const u32x2_a4*>(p + 18 * j + 2 + 8 * h);
+        r[0] = v.x;
+        r[1] = v.y;
+      } else {
+        const u32x3_a4 v = *reinterpret_cast<const u32x3_a4*>(p + 18 * j + 8 * h);
+        r[0] = v.x;
+        r[1] = v.y;
+        r[2] = v.z;
+      }
+    }
+  }
+  static __device__ __forceinline__ void finish(const uint8_t*, int, const uint32_t raw[RAW], SbRegsW& r) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const uint32_t d = (j & 1) ? raw[j] >> 16 : raw[j] & 0xffffu;
+      r.scale[j] = f16_bits_to_f32(d) * 16.0f;
+      const uint32_t* c = raw + 8 + (j >> 1) * 5 + (j & 1) * 3;
+      if (j & 1) {
+        r.code[j][0] = c[0];
+        r.code[j][1] = c[1];
+      } else {
+        r.code[j][0] = __builtin_amdgcn_alignbyte(c[1], c[0], 2);
+        r.code[j][1] = __builtin_amdgcn_alignbyte(c[2], c[1], 2);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; q++) r.corr[q] = 0.0f;
+  }
+};
+
+template <>
+struct GroupW<QBLK_SB4_AFFINE> {
+  // 148-byte groups are dword aligned: header dwords 0..4, codes at 20 + 16j
+  static constexpr int GB = 148, RAW = 5 + 8 * 2;
+  static __device__ __forceinline__ void load(const uint8_t* p, int h, uint32_t raw[RAW]) {
+    const u32x4_a4 hd = *reinterpret_cast<const u32x4_a4*>(p);
+    raw[0] = hd.x;
+    raw[1] = hd.y;
+    raw[2] = hd.z;
+    raw[3] = hd.w;
+    raw[4] = *reinterpret_cast<const uint32_t*>(p + 16);
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+      const u32x2_a4 v = *reinterpret_cast<const u32x2_a4*>(p + 20 + 16 * s + 8 * h);
+      raw[5 + 2 * s] = v.x;
+      raw[6 + 2 * s] = v.y;
+    }
+  }
+  static __device__ __forceinline__ void finish(const uint8_t*, int h, const uint32_t raw[RAW], SbRegsW& r) {
+    const float Ss = f16_bits_to_f32(raw[0] & 0xffffu), Sa = f16_bits_to_f32(raw[0] >> 16);
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+      r.code[s][0] = raw[5 + 2 * s];
+      r.code[s][1] = raw[6 + 2 * s];
+      const int8_t c = static_cast<int8_t>((raw[1 + (s >> 2)] >> (8 * (s & 3))) & 0xffu);
+      r.scale[s] = (Ss * static_cast<float>(c)) * 16.0f;
+    }
+    // w = s*n + a = s*(n-8) + (8s + a), as in Group<QBLK_SB4_AFFINE>
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int sb = 2 * q + h;
+      const int8_t c = static_cast<int8_t>((raw[1 + (sb >> 2)] >> (8 * (sb & 3))) & 0xffu);
+      const int8_t o = static_cast<int8_t>((raw[3 + (sb >> 2)] >> (8 * (sb & 3))) & 0xffu);
+      r.corr[q] = __builtin_fmaf(8.0f, Ss * static_cast<float>(c), Sa * static_cast<float>(o));
+    }
+  }
+};
+
+template <int FMT, int T32, bool SPLIT>
+__global__ __launch_bounds__(kThreads, 2) void k_gemm_w(const uint8_t* __restrict__ W,
                                                           const uint16_t* __restrict__ X,
                                                           float* __restrict__ Y, int M, int K, int N,
                                                           int sb_per_split) {
@@ -458,7 +549,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_sb4_w(const uint8_t* __res
   constexpr int kPieces = NT * 16;         // 16-byte pieces per stage (128 k per token)
   constexpr int kPer = kPieces / kThreads; // pieces moved per thread per stage
   static_assert(kPieces % kThreads == 0, "stage must split evenly over the workgroup");
+  using G = GroupW<FMT>;
+  constexpr bool AFFINE = FMT == QBLK_SB4_AFFINE;
   __shared__ uint4 xs[2][kPieces];
+  __shared__ float xsum[2][AFFINE ? NT * 4 : 1];  // Type 1: sum(x) [token][sub-block of the stage]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j32 = lane & 31, h = lane >> 5;
   const int64_t m = static_cast<int64_t>(blockIdx.x) * 128 + wave * 32 + j32;
@@ -466,7 +560,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_sb4_w(const uint8_t* __res
   const int nsb = K / 256;
   const int b_begin = SPLIT ? blockIdx.z * sb_per_split : 0;
   const int b_end = SPLIT ? min(nsb, b_begin + sb_per_split) : nsb;
-  const int64_t rowbytes = static_cast<int64_t>(nsb) * 138;
+  const int64_t rowbytes = static_cast<int64_t>(nsb) * G::GB;
   const uint8_t* rowp = W + (m < M ? m : M - 1) * rowbytes;
 
   // stage q = 2*b + half: thread t moves pieces t, t+256, ...; piece i of the
@@ -491,6 +585,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_sb4_w(const uint8_t* __res
       const int c = threadIdx.x + i * kThreads;
       const int t = c >> 4, pc = c & 15;
       xs[buf][t * 16 + (pc ^ (t & 15))] = xv[i];
+      if constexpr (AFFINE) {
+        // the 4 pieces of a sub-block sit on 4 adjacent lanes; products with
+        // 1.0 are exact, the sums fp32
+        const bf16x2v_t one = __builtin_bit_cast(bf16x2v_t, 0x3f803f80u);
+        float part = 0.0f;
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].x), one, part, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].y), one, part, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].z), one, part, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].w), one, part, false);
+        part = quad_sum(part);
+        if ((c & 3) == 0) xsum[buf][t * 4 + (pc >> 2)] = part;
+      }
     }
   };
 
@@ -504,13 +610,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_sb4_w(const uint8_t* __res
   for (int r = 0; r < 16; r++) zero[r] = 0.0f;
 
   uint4 xv[kPer];
-  uint32_t raw[kRawW];
+  uint32_t raw[G::RAW];
   SbRegsW cur;
   if (b_begin < b_end) {
     load_x(2 * b_begin, xv);
-    load_sb_w(rowp + static_cast<int64_t>(b_begin) * 138, h, raw);
+    G::load(rowp + static_cast<int64_t>(b_begin) * G::GB, h, raw);
     store_x(0, xv);
-    finish_sb_w(rowp + static_cast<int64_t>(b_begin) * 138, raw, cur);
+    G::finish(rowp + static_cast<int64_t>(b_begin) * G::GB, h, raw, cur);
   }
 
   // Stage hs of super-block b reads buffer hs; the next stage's X is fetched
@@ -523,7 +629,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_sb4_w(const uint8_t* __res
     for (int hs = 0; hs < 2; hs++) {
       __syncthreads();
       load_x(hs == 0 ? 2 * b + 1 : 2 * bn, xv);
-      if (hs == 0) load_sb_w(rowp + static_cast<int64_t>(bn) * 138, h, raw);
+      if (hs == 0) G::load(rowp + static_cast<int64_t>(bn) * G::GB, h, raw);
       const uint4* xb = xs[hs];
 #pragma unroll
       for (int jj = 0; jj < 4; jj++) {
@@ -544,8 +650,20 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_sb4_w(const uint8_t* __res
 #pragma unroll
         for (int tt = 0; tt < T32; tt++) asm volatile("" : "+v"(acc[tt]));
       }
+      if constexpr (AFFINE) {
+        // sum_j (8 s_j + a_j) sum(x_j) over the stage's 4 sub-blocks: two fp32
+        // 32x32x2 matrix ops per tile, A = sum(x) [token][sub-block 2q+h of
+        // the pair], B = (8 s + a) [that sub-block][row]
+#pragma unroll
+        for (int tt = 0; tt < T32; tt++) {
+          const float* xq = xsum[hs] + (32 * tt + j32) * 4 + h;
+#pragma unroll
+          for (int q = 0; q < 2; q++)
+            acc[tt] = __builtin_amdgcn_mfma_f32_32x32x2f32(xq[2 * q], cur.corr[2 * hs + q], acc[tt], 0, 0, 0);
+        }
+      }
       store_x(hs ^ 1, xv);
-      if (hs == 1) finish_sb_w(rowp + static_cast<int64_t>(bn) * 138, raw, cur);
+      if (hs == 1) G::finish(rowp + static_cast<int64_t>(bn) * G::GB, h, raw, cur);
     }
   }
 
@@ -771,7 +889,7 @@ hipError_t launch_t(const void* blocks, int64_t m, int64_t k, const void* x, int
   return hipGetLastError();
 }
 
-template <int T32>
+template <int FMT, int T32>
 hipError_t launch_w(const void* blocks, int64_t m, int64_t k, const void* x, int64_t n, float* y,
                     hipStream_t s) {
   const unsigned gx = static_cast<unsigned>((m + 127) / 128);
@@ -791,11 +909,11 @@ hipError_t launch_w(const void* blocks, int64_t m, int64_t k, const void* x, int
   if (split > 1) {
     const hipError_t e = launch_fill_zero(y, m * n, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_gemm_sb4_w<T32, true>), dim3(gx, gy, split), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((k_gemm_w<FMT, T32, true>), dim3(gx, gy, split), dim3(kThreads), 0, s,
                        static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
                        static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), per);
   } else {
-    hipLaunchKernelGGL((k_gemm_sb4_w<T32, false>), dim3(gx, gy, 1), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((k_gemm_w<FMT, T32, false>), dim3(gx, gy, 1), dim3(kThreads), 0, s,
                        static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
                        static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), nsb);
   }
@@ -832,18 +950,18 @@ hipError_t launch_gemm(int fmt, const void* blocks, int64_t m, int64_t k, const 
     if (n <= 16) return launch_s<2, 1, 2>(blocks, m, k, x, n, y, s);
     if (n <= 32) return launch_s<2, 2, 2>(blocks, m, k, x, n, y, s);
     if (n <= 64) return launch_t<QBLK_SB4, 2, 4>(blocks, m, k, x, n, y, s);
-    return launch_w<4>(blocks, m, k, x, n, y, s);
+    return launch_w<QBLK_SB4, 4>(blocks, m, k, x, n, y, s);
   }
   if (fmt == QBLK_Q4_0) {
     if (n <= 16) return launch_t<QBLK_Q4_0, 1, 1>(blocks, m, k, x, n, y, s);
     if (n <= 32) return launch_t<QBLK_Q4_0, 1, 2>(blocks, m, k, x, n, y, s);
     if (n <= 64) return launch_t<QBLK_Q4_0, 2, 4>(blocks, m, k, x, n, y, s);
-    return launch_t<QBLK_Q4_0, 2, 4>(blocks, m, k, x, n, y, s);
+    return launch_w<QBLK_Q4_0, 4>(blocks, m, k, x, n, y, s);
   }
   if (n <= 16) return launch_t<QBLK_SB4_AFFINE, 1, 1>(blocks, m, k, x, n, y, s);
   if (n <= 32) return launch_t<QBLK_SB4_AFFINE, 1, 2>(blocks, m, k, x, n, y, s);
   if (n <= 64) return launch_t<QBLK_SB4_AFFINE, 2, 4>(blocks, m, k, x, n, y, s);
-  return launch_t<QBLK_SB4_AFFINE, 2, 4>(blocks, m, k, x, n, y, s);
+  return launch_w<QBLK_SB4_AFFINE, 4>(blocks, m, k, x, n, y, s);
 }
 
 }  // namespace qblk

@@ -297,13 +297,14 @@ def test_gemm_other_formats(q, fmt, n):
 
 
 @pytest.mark.parametrize("fmt", ["q4_0", "sb4a"])
-def test_gemm_other_formats_split_k(q, fmt):
+@pytest.mark.parametrize("n", [20, 130])
+def test_gemm_other_formats_split_k(q, fmt, n):
     # long K with few rows: K is split over the grid and summed into Y
     m, k = 40, 14336
     f, of = gemm_fmt(q, fmt)
     w = mixed_blocks(m, k, 23)
     blocks = O.quantize(of, w)
-    X = WL.bf16_bits(np.random.default_rng(24).standard_normal((20, k)).astype(np.float32))
+    X = WL.bf16_bits(np.random.default_rng(24).standard_normal((n, k)).astype(np.float32))
     Y = host(q.gemm(dev(blocks), f, m, k, dev_bf16(X)))
     Y_ref, B = O.gemm(of, blocks, m, k, WL.bf16_values(X).astype(np.float64))
     check_products(Y, Y_ref, B, f"gemm {fmt} split-K")
