@@ -29,6 +29,11 @@ def _db(d):
     return sqlite3.connect(dbs[0])
 
 
+def _pct(ds, p):
+    s = sorted(ds)
+    return s[min(len(s) - 1, int(round(p / 100.0 * (len(s) - 1))))]
+
+
 def trace(d):
     c = _db(d)
     rows = c.execute("select name, start, end from kernels order by start").fetchall()
@@ -38,7 +43,8 @@ def trace(d):
     out = []
     for n, ds in sorted(by.items(), key=lambda kv: -sum(kv[1])):
         out.append(dict(kernel=n, calls=len(ds), total_us=round(sum(ds), 3), avg_us=round(statistics.mean(ds), 3),
-                        median_us=round(statistics.median(ds), 3), min_us=round(min(ds), 3),
+                        median_us=round(statistics.median(ds), 3), p10_us=round(_pct(ds, 10), 3),
+                        p90_us=round(_pct(ds, 90), 3), min_us=round(min(ds), 3),
                         max_us=round(max(ds), 3)))
     return out
 
@@ -81,7 +87,7 @@ if __name__ == "__main__":
     if cmd == "trace":
         for r in trace(sys.argv[2]):
             print(f"{r['calls']:6d}  avg {r['avg_us']:10.3f} us  med {r['median_us']:10.3f}  "
-                  f"min {r['min_us']:10.3f}  max {r['max_us']:10.3f}  total {r['total_us']:12.1f}  {r['kernel'][:110]}")
+                  f"p10 {r['p10_us']:10.3f}  p90 {r['p90_us']:10.3f}  min {r['min_us']:10.3f}  max {r['max_us']:10.3f}  total {r['total_us']:12.1f}  {r['kernel'][:110]}")
     elif cmd == "pmc":
         for k, cs in pmc(sys.argv[2]).items():
             print(k[:110])
