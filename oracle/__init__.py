@@ -13,7 +13,7 @@ import numpy as np
 
 from . import build as _build
 
-Q4_0, SB4, SB4_AFFINE = 0, 1, 2
+Q4_0, SB4, SB4_AFFINE, Q4_K = 0, 1, 2, 3
 F32, F16, BF16 = 0, 1, 2
 
 _lib = None
@@ -38,11 +38,12 @@ def lib():
         L.orc_quantize_q4_0.argtypes = [p, i32, i64, i64, p]
         L.orc_quantize_q4_0_ref.argtypes = [p, i64, i64, p]
         L.orc_quantize_sb4.argtypes = [p, i32, i64, i64, i32, p]
+        L.orc_quantize_q4_k.argtypes = [p, i32, i64, i64, p]
         L.orc_dequant.argtypes = [i32, p, i64, i64, p]
         L.orc_gemv.argtypes = [i32, p, i64, i64, p, p, i64, p, p]
         L.orc_gemm.argtypes = [i32, p, i64, i64, p, i64, p, i64, p, p]
         for f in ("orc_meta_int8", "orc_quantize_q4_0", "orc_quantize_q4_0_ref",
-                  "orc_quantize_sb4", "orc_dequant", "orc_gemv", "orc_gemm"):
+                  "orc_quantize_sb4", "orc_quantize_q4_k", "orc_dequant", "orc_gemv", "orc_gemm"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -138,9 +139,20 @@ def quantize_sb4(w, affine=False):
     return out
 
 
+def quantize_q4_k(w):
+    """Q4_0 chapter 4.6 form: fp16 d, dmin; 6-bit s_j, m_j; 4-bit codes."""
+    arr, tag = _dense(w)
+    rows, k = arr.shape
+    out = np.zeros(packed_bytes(Q4_K, rows, k), dtype=np.uint8)
+    _check(lib().orc_quantize_q4_k(_ptr(arr), tag, rows, k, _ptr(out)), "quantize_q4_k")
+    return out
+
+
 def quantize(fmt, w):
     if fmt == Q4_0:
         return quantize_q4_0(w)
+    if fmt == Q4_K:
+        return quantize_q4_k(w)
     return quantize_sb4(w, affine=(fmt == SB4_AFFINE))
 
 

@@ -27,6 +27,16 @@
  *       fp16 super-offset max|alpha|/127.
  *   R14 dequant operation order: (S*sc)*(n-8) for Type 0 and
  *       (Ss*sc)*n + (Sa*ac) for Type 1, no fused multiply-add.
+ *   R23 Q4_K field order [d16][dmin16][12 bytes of 6-bit fields][qs x128]
+ *       (144 bytes); field i (s_0..s_7, then m_0..m_7) occupies bits
+ *       6i..6i+5 of the 96-bit little-endian integer in bytes 4..15.
+ *   R24 Q4_K sub-block range: lo = min(0, min w), hi = max w; first-level
+ *       scale (hi - lo)/15 and min -lo (>= 0, so m_j is unsigned), in fp32.
+ *   R25 Q4_K second level: d = fp16(max scale / 63), dmin = fp16(max min / 63);
+ *       6-bit codes clamp(rha(v / stored), 0, 63).
+ *   R26 Q4_K 4-bit codes against the rebuilt S_j = d*s_j and M_j = dmin*m_j:
+ *       clamp(rha((w + M_j) / S_j), 0, 15).
+ *   R27 Q4_K dequant fl(S_j*q - M_j) (S_j*q and M_j are exact in fp32).
  */
 #include "qblk_oracle.h"
 
@@ -142,7 +152,7 @@ static uint16_t get_u16(const uint8_t* p) {
 
 int orc_block_elems(int fmt) {
   if (fmt == ORC_Q4_0) return 32;
-  if (fmt == ORC_SB4 || fmt == ORC_SB4_AFFINE) return 256;
+  if (fmt == ORC_SB4 || fmt == ORC_SB4_AFFINE || fmt == ORC_Q4_K) return 256;
   return 0;
 }
 
@@ -154,6 +164,8 @@ int orc_block_bytes(int fmt) {
   if (fmt == ORC_Q4_0) return 2 + 32 / 2;
   if (fmt == ORC_SB4) return 2 + 8 + 256 / 2;
   if (fmt == ORC_SB4_AFFINE) return 2 + 2 + 8 + 8 + 256 / 2;
+  /* Q4_K: fp16 d and dmin, 16 six-bit fields (96 bits), 128 bytes of codes */
+  if (fmt == ORC_Q4_K) return 2 + 2 + 16 * 6 / 8 + 256 / 2;
   return 0;
 }
 
@@ -330,6 +342,72 @@ int orc_quantize_sb4(const void* w, int dtype, int64_t rows, int64_t k,
 }
 
 /* ------------------------------------------------------------------ */
+/* Q4_K form ([Q40] 4.6): one fp16 scale d and one fp16 min-scale dmin */
+/* per super-block, a 6-bit scale s_j and a 6-bit min m_j per 32-weight */
+/* sub-block; a weight is d*s_j*q - dmin*m_j with q in [0, 15].         */
+/* The page names the 6-bit packing without describing it (R23).        */
+/* ------------------------------------------------------------------ */
+static void put_field6(uint8_t* f, int i, int v) {
+  for (int b = 0; b < 6; b++)
+    if ((v >> b) & 1) f[(6 * i + b) / 8] |= (uint8_t)(1u << ((6 * i + b) % 8));
+}
+static int get_field6(const uint8_t* f, int i) {
+  int v = 0;
+  for (int b = 0; b < 6; b++) v |= ((f[(6 * i + b) / 8] >> ((6 * i + b) % 8)) & 1) << b;
+  return v;
+}
+
+static void q4_k_superblock(const float* w, uint8_t* blk) {
+  float sc[8], mn[8];
+  float smax = 0.0f, mmax = 0.0f;
+  for (int j = 0; j < 8; j++) {
+    const float* x = w + 32 * j;
+    float lo = 0.0f, hi = x[0]; /* R24: the range always reaches down to 0 */
+    for (int i = 0; i < 32; i++) {
+      if (x[i] < lo) lo = x[i];
+      if (x[i] > hi) hi = x[i];
+    }
+    sc[j] = (hi - lo) / 15.0f; /* 16 levels, 15 steps */
+    mn[j] = -lo;
+    if (sc[j] > smax) smax = sc[j];
+    if (mn[j] > mmax) mmax = mn[j];
+  }
+  /* R25: the largest scale and the largest min map to the 6-bit top, 63 */
+  const uint16_t d16 = orc_f32_to_f16(smax / 63.0f);
+  const uint16_t m16 = orc_f32_to_f16(mmax / 63.0f);
+  const float D = orc_f16_to_f32(d16), Dm = orc_f16_to_f32(m16);
+  put_u16(blk, d16);
+  put_u16(blk + 2, m16);
+  memset(blk + 4, 0, 12);
+  for (int j = 0; j < 8; j++) {
+    const int s6 = clamp_code(orc_rha(qdiv(sc[j], D)), 0, 63);
+    const int m6 = clamp_code(orc_rha(qdiv(mn[j], Dm)), 0, 63);
+    put_field6(blk + 4, j, s6);
+    put_field6(blk + 4, 8 + j, m6);
+    /* R26: codes against the values the block rebuilds */
+    const float S = D * (float)s6, M = Dm * (float)m6;
+    uint8_t n[32];
+    for (int i = 0; i < 32; i++)
+      n[i] = (uint8_t)clamp_code(orc_rha(qdiv(w[32 * j + i] + M, S)), 0, 15);
+    pack_nibbles(n, blk + 16 + 16 * j);
+  }
+}
+
+int orc_quantize_q4_k(const void* w, int dtype, int64_t rows, int64_t k,
+                      uint8_t* out) {
+  if (!w || !out || rows < 0 || k < 0 || k % 256 != 0) return -1;
+  if (dtype < ORC_F32 || dtype > ORC_BF16) return -1;
+  const int64_t nb = k / 256;
+  float buf[256];
+  for (int64_t r = 0; r < rows; r++)
+    for (int64_t b = 0; b < nb; b++) {
+      for (int i = 0; i < 256; i++) buf[i] = load_elem(w, dtype, r * k + b * 256 + i);
+      q4_k_superblock(buf, out + (r * nb + b) * 144);
+    }
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* dequantization                                                      */
 /* ------------------------------------------------------------------ */
 
@@ -354,6 +432,20 @@ static void dequant_row(int fmt, const uint8_t* row, int64_t k, float* y) {
         float sj = S * (float)(int8_t)blk[2 + j]; /* rebuilt sub-scale */
         for (int i = 0; i < 32; i++)
           y[b * 256 + 32 * j + i] = sj * (float)(nib(blk + 10 + 16 * j, i) - 8);
+      }
+    }
+  } else if (fmt == ORC_Q4_K) {
+    for (int64_t b = 0; b < k / 256; b++) {
+      const uint8_t* blk = row + b * 144;
+      float D = orc_f16_to_f32(get_u16(blk));
+      float Dm = orc_f16_to_f32(get_u16(blk + 2));
+      for (int j = 0; j < 8; j++) {
+        float S = D * (float)get_field6(blk + 4, j);
+        float M = Dm * (float)get_field6(blk + 4, 8 + j);
+        for (int i = 0; i < 32; i++) {
+          float t = S * (float)nib(blk + 16 + 16 * j, i);
+          y[b * 256 + 32 * j + i] = t - M;
+        }
       }
     }
   } else {

@@ -14,7 +14,7 @@
  *   [Q40] "GGUF 量化内幕 第4章 Q4_0：块量化的起点" (sxkj888.cn), sections
  *         4.1.2 (block layout), 4.2.1 (nibble order), 4.2.2 (code range and
  *         the minus-8 offset), 4.3 (dequantization), 4.4 (quantizer), 4.5
- *         (outlier example).
+ *         (outlier example), 4.6 (the Q4_K form: d, dmin, 6-bit s_j and m_j).
  *
  * Conventions (fp32 IEEE arithmetic, no FMA contraction, true division):
  *   h(v)  fp32 -> fp16 bits, round-to-nearest-even, subnormals kept.
@@ -40,6 +40,7 @@ extern "C" {
 #define ORC_Q4_0 0       /* 32 weights, 18 bytes            */
 #define ORC_SB4 1        /* 256 weights, 138 bytes (Type 0) */
 #define ORC_SB4_AFFINE 2 /* 256 weights, 148 bytes (Type 1) */
+#define ORC_Q4_K 3       /* 256 weights, 144 bytes ([Q40] 4.6 form) */
 
 /* element types of dense inputs */
 #define ORC_F32 0
@@ -72,6 +73,11 @@ int orc_quantize_q4_0(const void* w, int dtype, int64_t rows, int64_t k,
                       uint8_t* out);
 int orc_quantize_sb4(const void* w, int dtype, int64_t rows, int64_t k,
                      int affine, uint8_t* out);
+
+/* Q4_K form of [Q40] 4.6: y = d*s_j*q - dmin*m_j (layout and the steps the
+ * page leaves open are the readings R23-R27 listed in qblk_oracle.c). */
+int orc_quantize_q4_k(const void* w, int dtype, int64_t rows, int64_t k,
+                      uint8_t* out);
 
 /* Q4_0 quantizer as [Q40] 4.4 prints it (signed extreme / -8, reciprocal
  * multiply, +8.5 and truncation, upper clamp at 15). */

@@ -41,7 +41,7 @@ static int fail(const char* what) {
 
 int main(void) {
   const int64_t rows = 6, k = 512, n = 3;
-  const int fmts[3] = {ORC_Q4_0, ORC_SB4, ORC_SB4_AFFINE};
+  const int fmts[4] = {ORC_Q4_0, ORC_SB4, ORC_SB4_AFFINE, ORC_Q4_K};
   float* w = malloc(sizeof(float) * rows * k);
   uint16_t* w16 = malloc(sizeof(uint16_t) * rows * k);
   float* back = malloc(sizeof(float) * rows * k);
@@ -58,7 +58,7 @@ int main(void) {
   for (int64_t i = 0; i < k; i++) x[i] = uniform() - 0.5;
   for (int64_t i = 0; i < n * k; i++) X[i] = uniform() - 0.5;
 
-  for (int f = 0; f < 3; f++) {
+  for (int f = 0; f < 4; f++) {
     const int fmt = fmts[f];
     const size_t nbytes = (size_t)(rows * (k / orc_block_elems(fmt)) * orc_block_bytes(fmt));
     uint8_t* b = malloc(nbytes);
@@ -71,8 +71,9 @@ int main(void) {
       } else if (dt == ORC_F16) {
         for (int64_t i = 0; i < rows * k; i++) w16[i] = orc_f32_to_f16(w[i]);
       }
-      const int st = fmt == ORC_Q4_0 ? orc_quantize_q4_0(src, dt, rows, k, b)
-                                     : orc_quantize_sb4(src, dt, rows, k, fmt == ORC_SB4_AFFINE, b);
+      const int st = fmt == ORC_Q4_0   ? orc_quantize_q4_0(src, dt, rows, k, b)
+                     : fmt == ORC_Q4_K ? orc_quantize_q4_k(src, dt, rows, k, b)
+                                       : orc_quantize_sb4(src, dt, rows, k, fmt == ORC_SB4_AFFINE, b);
       if (st != 0) return fail("quantize failed");
     }
     if (orc_dequant(fmt, b, rows, k, back) != 0) return fail("dequant failed");

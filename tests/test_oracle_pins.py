@@ -8,6 +8,11 @@ or brute force over every admissible code.  No GPU is involved.
 Pages:
   K-quants blog   "GGUF K-quants" (hugo-blog-2v1.pages.dev/2025/gguf-k-quants/)
   Q4_0 chapter    "GGUF 量化内幕 第4章 Q4_0：块量化的起点" (sxkj888.cn)
+
+The Q4_K form (chapter section 4.6) has no worked example on the pages: its
+pins are a hand-derived block (tests/golden/q4_k_block.txt), brute force over
+every 6-bit and 4-bit code, the error bound its rebuilt range implies, the
+degenerate blocks and numpy's matmul for the products.
 """
 import decimal
 import os
@@ -447,9 +452,113 @@ def test_degenerate_blocks():
 
 
 # --------------------------------------------------------------------------
+# the Q4_K form (Q4_0 chapter 4.6): y = d*s_j*q - dmin*m_j
+# --------------------------------------------------------------------------
+def q4k_fields(hdr12):
+    """the sixteen 6-bit fields (s_0..s_7, m_0..m_7) of bytes 4..15, field i
+    at bits 6i..6i+5 of the little-endian integer (reading R23)."""
+    v = int.from_bytes(bytes(np.asarray(hdr12, dtype=np.uint8)), "little")
+    return [(v >> (6 * i)) & 63 for i in range(16)]
+
+
+def test_q4_k_hand_derived_block():
+    g = read_golden("q4_k_block.txt")
+    w = np.zeros((1, 256), np.float32)
+    q = np.arange(32) % 16
+    w[0, 0:32] = q * np.float32(63 / 256)
+    w[0, 32:64] = np.float32(-63 / 32) + q * np.float32(0.125)
+    assert O.block_bytes(O.Q4_K) == 144 and O.block_elems(O.Q4_K) == 256
+    blk = O.quantize_q4_k(w)
+    assert list(blk[0:16]) == [int(v) for v in g["header"]]
+    assert list(blk[16:32]) == [int(v) for v in g["codes_sub_block_0"]]
+    assert list(blk[32:48]) == [int(v) for v in g["codes_sub_block_1"]]
+    assert np.all(blk[48:] == 0)
+    y = O.dequant(O.Q4_K, blk, 1, 256)[0]
+    assert np.array_equal(y, w[0])  # every input is on the grid
+    # a hand-built block: d = 1/64, dmin = 1/2, fields from the golden file
+    fields = [int(v) for v in g["block2_fields"]]
+    packed = sum(v << (6 * i) for i, v in enumerate(fields)).to_bytes(12, "little")
+    b2 = np.zeros(144, np.uint8)
+    b2[0:4] = np.array([0x2400, 0x3800], dtype="<u2").view(np.uint8)
+    b2[4:16] = np.frombuffer(packed, dtype=np.uint8)
+    b2[16] = 0xF0  # sub-block 0: weight 0 code 0, weight 16 code 15
+    b2[16 + 32] = 0x08  # sub-block 2, weight 0 code 8
+    b2[16 + 96:16 + 112] = 0x88  # sub-block 6: all codes 8
+    y2 = O.dequant(O.Q4_K, b2, 1, 256)[0]
+    for i, v in zip((0, 16, 64, 65, 192, 223), g["block2_values"]):
+        assert y2[i] == np.float32(v), (i, y2[i], v)
+
+
+def test_brute_force_q4_k_codes():
+    rng = np.random.default_rng(24)
+    w = tiny_blocks(rng, 15, 256)
+    blk = O.quantize_q4_k(w).reshape(-1, 144)
+    for b in range(w.shape[0]):
+        x = w[b].reshape(8, 32)
+        lo = np.minimum(x.min(1), np.float32(0))  # reading R24
+        sc = ((x.max(1) - lo) / np.float32(15)).astype(np.float32)
+        mn = (-lo).astype(np.float32)
+        d16, m16 = (int(v) for v in blk[b, 0:4].view("<u2"))
+        assert d16 == f16(sc.max() / np.float32(63)) and m16 == f16(mn.max() / np.float32(63))
+        D, Dm = np.float32(f16val(d16)), np.float32(f16val(m16))
+        F = q4k_fields(blk[b, 4:16])
+        for j in range(8):
+            assert F[j] == best_code(np.float32(0) if D == 0 else sc[j] / D, 0, 63), (b, j)
+            assert F[8 + j] == best_code(np.float32(0) if Dm == 0 else mn[j] / Dm, 0, 63), (b, j)
+            S, M = D * np.float32(F[j]), Dm * np.float32(F[8 + j])
+            codes = nibbles(blk[b, 16 + 16 * j:32 + 16 * j])
+            for i in range(32):
+                t = np.float32(0) if S == 0 else (x[j, i] + M) / S
+                assert codes[i] == best_code(t, 0, 15), (b, j, i)
+
+
+def test_q4_k_error_bound_and_top_codes():
+    rng = np.random.default_rng(32)
+    w = (rng.standard_normal((8, 1024)) * np.exp(rng.uniform(-6, 0, (8, 1)))).astype(np.float32)
+    w[0, :256] = np.abs(w[0, :256])  # a super-block with no negative weight
+    b = O.quantize_q4_k(w).reshape(8, -1, 144)
+    y = O.dequant(O.Q4_K, b.reshape(-1), 8, 1024).reshape(8, -1, 8, 32)
+    for r in range(8):
+        for s in range(b.shape[1]):
+            D = f16val(int(b[r, s, 0:2].view("<u2")[0]))
+            Dm = f16val(int(b[r, s, 2:4].view("<u2")[0]))
+            F = q4k_fields(b[r, s, 4:16])
+            assert max(F[:8]) == 63  # the widest sub-block takes the top 6-bit code
+            x = w[r, 256 * s:256 * s + 256].reshape(8, 32).astype(np.float64)
+            if x.min() < 0:
+                assert max(F[8:]) == 63
+            else:
+                assert Dm == 0 and max(F[8:]) == 0
+            for j in range(8):
+                S = D * F[j]
+                bound = S / 2 + 15 * D / 2 + Dm / 2
+                err = np.abs(x[j] - y[r, s, j]).max()
+                assert err <= bound * (1 + 1e-5) + 1e-30, (r, s, j)
+
+
+def test_q4_k_degenerate_blocks():
+    w = np.zeros((3, 256), dtype=np.float32)
+    w[1, :] = np.float32(-0.375)  # constant negative: zero scale, the min carries it
+    w[2, :] = np.float32(0.375)   # constant positive: zero min
+    b = O.quantize_q4_k(w).reshape(-1, 144)
+    assert np.all(b[0] == 0)
+    y = O.dequant(O.Q4_K, b.reshape(-1), 3, 256)
+    assert np.all(y[0] == 0)
+    F1 = q4k_fields(b[1, 4:16])
+    assert int(b[1, 0:2].view("<u2")[0]) == 0 and F1[:8] == [0] * 8 and F1[8:] == [63] * 8
+    Dm = f16val(int(b[1, 2:4].view("<u2")[0]))
+    assert np.all(np.abs(y[1] + 0.375) <= Dm / 2)
+    assert np.all(b[1, 16:] == 0)
+    F2 = q4k_fields(b[2, 4:16])
+    assert int(b[2, 2:4].view("<u2")[0]) == 0 and F2[8:] == [0] * 8
+    D = f16val(int(b[2, 0:2].view("<u2")[0]))
+    assert np.all(np.abs(y[2] - 0.375) <= D * 63 / 2 * (1 + 1e-6))
+
+
+# --------------------------------------------------------------------------
 # the fp64 products, against numpy's float64 matmul
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("fmt", [O.Q4_0, O.SB4, O.SB4_AFFINE])
+@pytest.mark.parametrize("fmt", [O.Q4_0, O.SB4, O.SB4_AFFINE, O.Q4_K])
 def test_products_vs_numpy(fmt):
     rng = np.random.default_rng(41 + fmt)
     m, k = 24, 768
