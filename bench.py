@@ -15,8 +15,9 @@ plain device copy reaches on the same GPU.
 
 Also measured (field "rows"): every other step of the hot path at the shapes
 of the synthetic workloads -- quantization (Q4_0, super-block Type 0 and
-Type 1 over a 32-layer 7B-shaped stack from fp16), dequantization, the Q4_0 and
-Type 1 GEMVs and the prefill GEMM (N = 16, 64, 512).
+Type 1 over a 32-layer 7B-shaped stack from fp16, Q4_K), dequantization, the
+Q4_0, Type 1 and Q4_K GEMVs and the prefill GEMM (N = 16, 64, 512) for every
+format.
 
 cpu_baseline: the CPU oracle (oracle/, plain C, fp64 sums) timed on this
 host on the same GEMV workload, on one thread and on every core (row chunks).
@@ -311,6 +312,8 @@ def measure_rows(torch, q, WL, np, dev):
     gemv_row("gemv_q4_0_4096x4096_f16", q.Q4_0, torch.from_numpy(w).to(dev), torch.from_numpy(x).to(dev))
     w, x = WL.q4_0_small()
     gemv_row("gemv_q4_0_256x4096_f32", q.Q4_0, torch.from_numpy(w).to(dev), torch.from_numpy(x).to(dev))
+    w, x = WL.sb4_decode("up")
+    gemv_row("gemv_q4k_11008x4096_f16", q.Q4_K, torch.from_numpy(w).to(dev), torch.from_numpy(x).to(dev))
 
     # quantizers
     def quant_row(name, fmt, w, reps=20):
@@ -326,6 +329,8 @@ def measure_rows(torch, q, WL, np, dev):
     wup = torch.from_numpy(w).to(dev)
     quant_row("quantize_sb4_11008x4096_f32", q.SB4, wup)
     quant_row("quantize_sb4a_11008x4096_f32", q.SB4_AFFINE, wup)
+    quant_row("quantize_q4k_11008x4096_f32", q.Q4_K, wup)
+    quant_row("quantize_q4k_11008x4096_f16", q.Q4_K, wup.half())
 
     # dequant
     b = q.quantize(wup, q.SB4)
@@ -385,11 +390,11 @@ def measure_rows(torch, q, WL, np, dev):
                               frac_mfma_bf16=round(tf / BF16_PEAK_TFLOPS, 4))
             log(f"  {name}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s, {tf:.1f} TFLOP/s")
         del cps
-    # the same product for the other two formats (14336x4096)
+    # the same product for the other formats (14336x4096)
     w, _ = WL.sb4_prefill("up", 16)
     m, k = w.shape
     wd = torch.from_numpy(w).to(dev)
-    for fmt, tag in ((q.Q4_0, "q4_0"), (q.SB4_AFFINE, "sb4a")):
+    for fmt, tag in ((q.Q4_0, "q4_0"), (q.SB4_AFFINE, "sb4a"), (q.Q4_K, "q4k")):
         b0 = q.quantize(wd, fmt)
         C = n_copies(b0.numel())
         cps = [b0] + [b0.clone() for _ in range(C - 1)]

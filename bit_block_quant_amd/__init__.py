@@ -18,9 +18,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqblk.so")
 
-Q4_0, SB4, SB4_AFFINE = 0, 1, 2
+Q4_0, SB4, SB4_AFFINE, Q4_K = 0, 1, 2, 3
 F32, F16, BF16 = 0, 1, 2
-FORMATS = {"q4_0": Q4_0, "sb4": SB4, "sb4_affine": SB4_AFFINE}
+FORMATS = {"q4_0": Q4_0, "sb4": SB4, "sb4_affine": SB4_AFFINE, "q4_k": Q4_K}
 _DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 
 STATUS = {
@@ -31,8 +31,8 @@ STATUS = {
 # every symbol include/qblk.h declares
 EXPORTS = (
     "qblk_block_bytes", "qblk_block_elems", "qblk_packed_bytes", "qblk_quantize_q4_0",
-    "qblk_quantize_q4_0_ref", "qblk_quantize_sb4", "qblk_dequant", "qblk_gemv", "qblk_gemm",
-    "qblk_status_string", "qblk_version",
+    "qblk_quantize_q4_0_ref", "qblk_quantize_sb4", "qblk_quantize_q4_k", "qblk_dequant",
+    "qblk_gemv", "qblk_gemm", "qblk_status_string", "qblk_version",
 )
 
 
@@ -54,11 +54,12 @@ def _load():
     L.qblk_quantize_q4_0.argtypes = [p, i32, i64, i64, p, p]
     L.qblk_quantize_q4_0_ref.argtypes = [p, i32, i64, i64, p, p]
     L.qblk_quantize_sb4.argtypes = [p, i32, i64, i64, i32, p, p]
+    L.qblk_quantize_q4_k.argtypes = [p, i32, i64, i64, p, p]
     L.qblk_dequant.argtypes = [i32, p, i64, i64, p, i32, p]
     L.qblk_gemv.argtypes = [i32, p, i64, i64, p, i32, p, p]
     L.qblk_gemm.argtypes = [i32, p, i64, i64, p, i32, i64, p, p]
-    for f in ("qblk_quantize_q4_0", "qblk_quantize_q4_0_ref", "qblk_quantize_sb4", "qblk_dequant",
-              "qblk_gemv", "qblk_gemm"):
+    for f in ("qblk_quantize_q4_0", "qblk_quantize_q4_0_ref", "qblk_quantize_sb4", "qblk_quantize_q4_k",
+              "qblk_dequant", "qblk_gemv", "qblk_gemm"):
         getattr(L, f).restype = i32
     L.qblk_status_string.argtypes, L.qblk_status_string.restype = [i32], C.c_char_p
     L.qblk_version.argtypes, L.qblk_version.restype = [], C.c_char_p
@@ -120,6 +121,9 @@ def quantize(w, fmt, out=None, stream=None, ref=False):
     if fmt == Q4_0:
         f = _lib.qblk_quantize_q4_0_ref if ref else _lib.qblk_quantize_q4_0
         _check(f(_ptr(w), _dtype(w), rows, k, _ptr(out), _stream(stream)), "qblk_quantize_q4_0")
+    elif fmt == Q4_K:
+        _check(_lib.qblk_quantize_q4_k(_ptr(w), _dtype(w), rows, k, _ptr(out), _stream(stream)),
+               "qblk_quantize_q4_k")
     else:
         _check(_lib.qblk_quantize_sb4(_ptr(w), _dtype(w), rows, k, int(fmt == SB4_AFFINE), _ptr(out),
                                       _stream(stream)), "qblk_quantize_sb4")

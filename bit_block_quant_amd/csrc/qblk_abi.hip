@@ -14,7 +14,8 @@ int elems_of(int fmt) {
   switch (fmt) {
     case QBLK_Q4_0: return 32;
     case QBLK_SB4:
-    case QBLK_SB4_AFFINE: return 256;
+    case QBLK_SB4_AFFINE:
+    case QBLK_Q4_K: return 256;
     default: return 0;
   }
 }
@@ -24,6 +25,7 @@ size_t bytes_of(int fmt) {
     case QBLK_Q4_0: return 18;
     case QBLK_SB4: return 138;
     case QBLK_SB4_AFFINE: return 148;
+    case QBLK_Q4_K: return 144;
     default: return 0;
   }
 }
@@ -105,6 +107,18 @@ qblk_status_t qblk_quantize_sb4(const void* w, qblk_dtype_t wt, int64_t rows, in
   if (!work) return QBLK_OK;
   return from_hip(qblk::launch_quantize_sb4(w, wt, rows, k, affine ? 1 : 0, blocks,
                                             static_cast<hipStream_t>(stream)));
+}
+
+qblk_status_t qblk_quantize_q4_k(const void* w, qblk_dtype_t wt, int64_t rows, int64_t k,
+                                 void* blocks, qblk_stream_t stream) {
+  QBLK_TRY(check_shape(QBLK_Q4_K, rows, k));
+  if (!dtype_ok(wt)) return QBLK_ERR_DTYPE;
+  const bool work = rows > 0 && k > 0;
+  QBLK_TRY(check_ptr(w, work));
+  QBLK_TRY(check_ptr(blocks, work));
+  if (!work) return QBLK_OK;
+  return from_hip(qblk::launch_quantize_q4_k(w, wt, rows, k, blocks,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 qblk_status_t qblk_dequant(qblk_format_t fmt, const void* blocks, int64_t rows, int64_t k,

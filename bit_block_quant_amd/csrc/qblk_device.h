@@ -195,4 +195,16 @@ __device__ __forceinline__ uint32_t load_u16(const uint8_t* p) {
   return *reinterpret_cast<const uint16_t*>(p);
 }
 
+// ---------------------------------------------------------------- Q4_K
+// The 16-byte header of a Q4_K super-block as dwords h0..h3: fp16 d (low half
+// of h0) and dmin (high half), then sixteen 6-bit fields, field i at bit
+// 32 + 6i: the scale s_j is field j (inside h1:h2), the min m_j field 8 + j
+// (inside h2:h3).
+__device__ __forceinline__ uint32_t q4k_scale6(uint32_t h1, uint32_t h2, int j) {
+  return static_cast<uint32_t>(((static_cast<uint64_t>(h2) << 32) | h1) >> (6 * j)) & 63u;
+}
+__device__ __forceinline__ uint32_t q4k_min6(uint32_t h2, uint32_t h3, int j) {
+  return static_cast<uint32_t>(((static_cast<uint64_t>(h3) << 32) | h2) >> (16 + 6 * j)) & 63u;
+}
+
 }  // namespace qblk

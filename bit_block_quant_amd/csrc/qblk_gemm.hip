@@ -1,9 +1,12 @@
 // qblk_gemm.hip -- small-batch (prefill) product Y = X W^T on gfx950 matrix
-// cores, W in super-blocks (Type 0), X bf16 (n x k, token-major), Y fp32 (n x m).
+// cores, W in any of the block formats, X bf16 (n x k, token-major), Y fp32
+// (n x m).
 //
-// What is computed: Y[t,i] = sum_k X[t,k] W[i,k] with W[i,k] = (S*sc_j)*(code-8)
-// ("GGUF K-quants" blog, "套娃" step 5; code offset from "GGUF 量化内幕 第4章
-// Q4_0" 4.2.2).
+// What is computed: Y[t,i] = sum_k X[t,k] W[i,k] with W[i,k] the rebuilt
+// weight: Type 0 (S*sc_j)*(code-8) ("GGUF K-quants" blog, "套娃" step 5; code
+// offset from "GGUF 量化内幕 第4章 Q4_0" 4.2.2), Q4_0 d*(code-8) (chapter 4.3),
+// Type 1 (Ss*sc_j)*code + Sa*ac_j (blog, "套娃"), Q4_K (d*s_j)*code - dmin*m_j
+// (chapter 4.6).  The affine formats are run as s*(code-8) + (8s + offset).
 //
 // One v_mfma_f32_16x16x32_bf16 spans K = 32, exactly one sub-block, so the
 // weight operand holds the exact integers (code - 8)/16 in bf16 and the
@@ -87,6 +90,7 @@ struct SbRegs {
 //  Type 0   [S16][sc x8][qs x128]              138 B, scale S*sc_j
 //  Q4_0     8 blocks [d16][qs x16]              144 B, scale d_j
 //  Type 1   [Ss16][Sa16][sc x8][ac x8][qs x128] 148 B, scale Ss*sc_j, offset Sa*ac_j
+//  Q4_K     [d16][dmin16][6-bit fields x16][qs x128] 144 B, scale d*s_j, offset -dmin*m_j
 // Lane k-group g needs code bytes 4g..4g+3 of every sub-block.
 template <int FMT>
 struct Group;
@@ -191,6 +195,37 @@ struct Group<QBLK_SB4_AFFINE> {
   }
 };
 
+template <>
+struct Group<QBLK_Q4_K> {
+  // 144-byte groups are 16-byte aligned: the header as one dwordx4, codes
+  // (codes 0..15, offset -dmin*m_j) handled like Type 1's
+  static constexpr int GB = 144, RAW = 4 + 8;
+  static __device__ __forceinline__ void load(const uint8_t* p, int g, uint32_t raw[RAW]) {
+    const uint4 h = *reinterpret_cast<const uint4*>(p);
+    raw[0] = h.x;
+    raw[1] = h.y;
+    raw[2] = h.z;
+    raw[3] = h.w;
+#pragma unroll
+    for (int s = 0; s < 8; s++) raw[4 + s] = *reinterpret_cast<const uint32_t*>(p + 16 + 16 * s + 4 * g);
+  }
+  static __device__ __forceinline__ void finish(const uint8_t*, int g, const uint32_t raw[RAW], SbRegs& r) {
+    const float D = f16_bits_to_f32(raw[0] & 0xffffu), Dm = f16_bits_to_f32(raw[0] >> 16);
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+      r.code[s] = raw[4 + s];
+      r.scale[s] = (D * static_cast<float>(q4k_scale6(raw[1], raw[2], s))) * 16.0f;
+    }
+    // w = S*n - M = S*(n-8) + (8S - M), as for Type 1
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      const int sb = 4 * q + g;
+      const float S = D * static_cast<float>(q4k_scale6(raw[1], raw[2], sb));
+      r.corr[q] = __builtin_fmaf(8.0f, S, -(Dm * static_cast<float>(q4k_min6(raw[2], raw[3], sb))));
+    }
+  }
+};
+
 // sum over the 4 lanes of a quad (lanes 4i..4i+3)
 __device__ __forceinline__ float quad_sum(float v) {
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
@@ -208,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_t(const uint8_t* __restrict__
                                                      float* __restrict__ Y, int M, int K, int N,
                                                      int sb_per_split) {
   using G = Group<FMT>;
-  constexpr bool AFFINE = FMT == QBLK_SB4_AFFINE;
+  constexpr bool AFFINE = FMT == QBLK_SB4_AFFINE || FMT == QBLK_Q4_K;
   constexpr int NT = 16 * TN;
   __shared__ uint4 xs4[2][NT * kLdsRow / 8];
   __shared__ float xsum[2][AFFINE ? NT * 8 : 1];  // [token][sub-block]
@@ -540,6 +575,41 @@ struct GroupW<QBLK_SB4_AFFINE> {
   }
 };
 
+template <>
+struct GroupW<QBLK_Q4_K> {
+  // 144-byte groups are 16-byte aligned: header dwordx4, codes at 16 + 16j
+  static constexpr int GB = 144, RAW = 4 + 8 * 2;
+  static __device__ __forceinline__ void load(const uint8_t* p, int h, uint32_t raw[RAW]) {
+    const uint4 hd = *reinterpret_cast<const uint4*>(p);
+    raw[0] = hd.x;
+    raw[1] = hd.y;
+    raw[2] = hd.z;
+    raw[3] = hd.w;
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p + 16 + 16 * s + 8 * h);
+      raw[4 + 2 * s] = v.x;
+      raw[5 + 2 * s] = v.y;
+    }
+  }
+  static __device__ __forceinline__ void finish(const uint8_t*, int h, const uint32_t raw[RAW], SbRegsW& r) {
+    const float D = f16_bits_to_f32(raw[0] & 0xffffu), Dm = f16_bits_to_f32(raw[0] >> 16);
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+      r.code[s][0] = raw[4 + 2 * s];
+      r.code[s][1] = raw[5 + 2 * s];
+      r.scale[s] = (D * static_cast<float>(q4k_scale6(raw[1], raw[2], s))) * 16.0f;
+    }
+    // w = S*n - M = S*(n-8) + (8S - M)
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int sb = 2 * q + h;
+      const float S = D * static_cast<float>(q4k_scale6(raw[1], raw[2], sb));
+      r.corr[q] = __builtin_fmaf(8.0f, S, -(Dm * static_cast<float>(q4k_min6(raw[2], raw[3], sb))));
+    }
+  }
+};
+
 template <int FMT, int T32, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 2) void k_gemm_w(const uint8_t* __restrict__ W,
                                                           const uint16_t* __restrict__ X,
@@ -550,7 +620,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_w(const uint8_t* __restric
   constexpr int kPer = kPieces / kThreads; // pieces moved per thread per stage
   static_assert(kPieces % kThreads == 0, "stage must split evenly over the workgroup");
   using G = GroupW<FMT>;
-  constexpr bool AFFINE = FMT == QBLK_SB4_AFFINE;
+  constexpr bool AFFINE = FMT == QBLK_SB4_AFFINE || FMT == QBLK_Q4_K;
   __shared__ uint4 xs[2][kPieces];
   __shared__ float xsum[2][AFFINE ? NT * 4 : 1];  // Type 1: sum(x) [token][sub-block of the stage]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -957,6 +1027,12 @@ hipError_t launch_gemm(int fmt, const void* blocks, int64_t m, int64_t k, const 
     if (n <= 32) return launch_t<QBLK_Q4_0, 1, 2>(blocks, m, k, x, n, y, s);
     if (n <= 64) return launch_t<QBLK_Q4_0, 2, 4>(blocks, m, k, x, n, y, s);
     return launch_w<QBLK_Q4_0, 4>(blocks, m, k, x, n, y, s);
+  }
+  if (fmt == QBLK_Q4_K) {
+    if (n <= 16) return launch_t<QBLK_Q4_K, 1, 1>(blocks, m, k, x, n, y, s);
+    if (n <= 32) return launch_t<QBLK_Q4_K, 1, 2>(blocks, m, k, x, n, y, s);
+    if (n <= 64) return launch_t<QBLK_Q4_K, 2, 4>(blocks, m, k, x, n, y, s);
+    return launch_w<QBLK_Q4_K, 4>(blocks, m, k, x, n, y, s);
   }
   if (n <= 16) return launch_t<QBLK_SB4_AFFINE, 1, 1>(blocks, m, k, x, n, y, s);
   if (n <= 32) return launch_t<QBLK_SB4_AFFINE, 1, 2>(blocks, m, k, x, n, y, s);

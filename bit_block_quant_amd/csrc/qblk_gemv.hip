@@ -3,7 +3,8 @@
 // What is computed: y[i] = sum_k W[i,k] x[k] where W[i,k] is the block
 // format's rebuilt weight (Q4_0: d*(code-8), "GGUF 量化内幕 第4章 Q4_0" 4.3;
 // super-block Type 0: (S*sc_j)*(code-8) and Type 1: (Ss*sc_j)*code + Sa*ac_j,
-// "GGUF K-quants" blog, "套娃" step 5).  The pages only say that dequantized
+// "GGUF K-quants" blog, "套娃" step 5; Q4_K: (d*s_j)*code - dmin*m_j, Q4_0
+// chapter 4.6).  The pages only say that dequantized
 // weights feed the matrix product; this kernel never materialises W.
 //
 // Work split.  A 32-weight unit (a Q4_0 block or one super-block sub-block)
@@ -21,7 +22,8 @@
 // in the matching order: for code word t (bytes 4t..4t+3 of a unit) the pairs
 // are (x[4t], x[4t+2]), (x[4t+16], x[4t+18]), (x[4t+1], x[4t+3]),
 // (x[4t+17], x[4t+19]).  The unit's fp32 scale multiplies the two partial
-// sums; Type 1 adds offset * sum(x over the unit).
+// sums; Type 1 and Q4_K add offset * sum(x over the unit) (Q4_K's offset is
+// -dmin*m_j).
 // With x in fp32 (or bf16, widened exactly to fp32) the codes are converted
 // with v_cvt_f32_ubyte and accumulated with fp32 fused multiply-adds.
 #include "qblk_device.h"
@@ -49,6 +51,13 @@ template <>
 struct Fmt<QBLK_SB4_AFFINE> {
   static constexpr int E = 256, B = 148;
 };
+template <>
+struct Fmt<QBLK_Q4_K> {
+  static constexpr int E = 256, B = 144;
+};
+
+// formats whose codes are 0..15 plus a per-unit offset
+constexpr bool affine_fmt(int f) { return f == QBLK_SB4_AFFINE || f == QBLK_Q4_K; }
 
 // Scale, offset and the 16 code bytes of unit s of a row.
 template <int FMT>
@@ -66,6 +75,17 @@ __device__ __forceinline__ void load_unit(const uint8_t* row, int s, float& sc, 
     sc = S * static_cast<float>(static_cast<int8_t>(p[2 + j]));
     off = 0.0f;
     load16_a2(p + 10 + 16 * j, q);
+  } else if constexpr (FMT == QBLK_Q4_K) {
+    const int b = s >> 3, j = s & 7;
+    const uint8_t* p = row + static_cast<int64_t>(b) * 144;  // 16-byte aligned
+    const uint4 h = *reinterpret_cast<const uint4*>(p);
+    sc = f16_bits_to_f32(h.x & 0xffffu) * static_cast<float>(q4k_scale6(h.y, h.z, j));
+    off = -(f16_bits_to_f32(h.x >> 16) * static_cast<float>(q4k_min6(h.z, h.w, j)));
+    const uint4 v = *reinterpret_cast<const uint4*>(p + 16 + 16 * j);
+    q[0] = v.x;
+    q[1] = v.y;
+    q[2] = v.z;
+    q[3] = v.w;
   } else {
     const int b = s >> 3, j = s & 7;
     const uint8_t* p = row + static_cast<int64_t>(b) * 148;
@@ -197,7 +217,7 @@ template <int FMT, int XT, int R>
 __global__ __launch_bounds__(kThreads) void k_gemv(const uint8_t* __restrict__ blocks,
                                                    const void* __restrict__ x,
                                                    float* __restrict__ y, int M, int K) {
-  constexpr bool AFFINE = FMT == QBLK_SB4_AFFINE;
+  constexpr bool AFFINE = affine_fmt(FMT);
   constexpr bool XH = XT == QBLK_F16;
   constexpr int KC = XH ? kChunkF16 : kChunkF32;
   extern __shared__ uint4 smem[];
@@ -291,6 +311,7 @@ struct UnitAddr {
   static __device__ __forceinline__ uint32_t codes(int u) {
     if constexpr (FMT == QBLK_Q4_0) return 18u * u + 2u;
     else if constexpr (FMT == QBLK_SB4) return 138u * (u >> 3) + 10u + 16u * (u & 7);
+    else if constexpr (FMT == QBLK_Q4_K) return 144u * (u >> 3) + 16u + 16u * (u & 7);
     else return 148u * (u >> 3) + 20u + 16u * (u & 7);
   }
 };
@@ -302,7 +323,8 @@ __global__ __launch_bounds__(kThreadsH) void k_gemv_h(const uint8_t* __restrict_
                                                       const uint16_t* __restrict__ x,
                                                       float* __restrict__ y, int M, int K,
                                                       int rows_per_wg) {
-  constexpr bool AFFINE = FMT == QBLK_SB4_AFFINE;
+  constexpr bool AFFINE = affine_fmt(FMT);
+  constexpr bool QK = FMT == QBLK_Q4_K;
   constexpr int E = Fmt<FMT>::E, B = Fmt<FMT>::B;
   constexpr int SLOTS = kWavesH / KS;  // rows in flight per workgroup round
   const int S = K >> 5;                // units per row
@@ -316,8 +338,10 @@ __global__ __launch_bounds__(kThreadsH) void k_gemv_h(const uint8_t* __restrict_
   const int64_t rowbytes = static_cast<int64_t>(K / E) * B;
 
   // per (lane, unit): byte offsets inside a row of the codes, the scale
-  // header and the INT8 sub-scale (Type 1: offset 8 bytes further)
+  // header and the INT8 sub-scale (Type 1: offset 8 bytes further); Q4_K
+  // reads its whole 16-byte header and needs the sub-block index
   uint32_t off[UPL], hoff[UPL], coff[UPL];
+  int sbj[UPL];
   bool live[UPL];
 #pragma unroll
   for (int k = 0; k < UPL; k++) {
@@ -326,7 +350,8 @@ __global__ __launch_bounds__(kThreadsH) void k_gemv_h(const uint8_t* __restrict_
     const int u = min(uu, S - 1);
     off[k] = UnitAddr<FMT>::codes(u);
     hoff[k] = FMT == QBLK_Q4_0 ? off[k] - 2u : static_cast<uint32_t>(B) * (u >> 3);
-    coff[k] = hoff[k] + (AFFINE ? 4u : 2u) + (u & 7);
+    coff[k] = hoff[k] + (FMT == QBLK_SB4_AFFINE ? 4u : 2u) + (u & 7);
+    sbj[k] = u & 7;
   }
 
   // (1) x of this lane's units, 32 halves each (issued first)
@@ -343,6 +368,7 @@ __global__ __launch_bounds__(kThreadsH) void k_gemv_h(const uint8_t* __restrict_
   // (2) every weight load of this wave, group by group
   uint32_t q[RMAX][UPL][5];
   int hs[RMAX][UPL], hc[RMAX][UPL], ha[RMAX][UPL];
+  uint4 hk[RMAX][UPL];  // Q4_K headers
   uint32_t rbm[RMAX];  // 2 when the row starts 2 bytes past a dword boundary
 #pragma unroll
   for (int k = 0; k < UPL; k++) {
@@ -351,10 +377,14 @@ __global__ __launch_bounds__(kThreadsH) void k_gemv_h(const uint8_t* __restrict_
       const int r = min(row0 + slot + SLOTS * i, row_end - 1);
       const uint8_t* rb = blocks + static_cast<int64_t>(r) * rowbytes;  // wave-uniform
       rbm[i] = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(rb) & 3u);
-      hs[i][k] = AFFINE ? *reinterpret_cast<const int32_t*>(rb + hoff[k])
-                        : *reinterpret_cast<const uint16_t*>(rb + hoff[k]);
-      if constexpr (FMT != QBLK_Q4_0) hc[i][k] = *reinterpret_cast<const int8_t*>(rb + coff[k]);
-      if constexpr (AFFINE) ha[i][k] = *reinterpret_cast<const int8_t*>(rb + coff[k] + 8);
+      if constexpr (QK) {
+        hk[i][k] = *reinterpret_cast<const uint4*>(rb + hoff[k]);  // 16-byte aligned
+      } else {
+        hs[i][k] = AFFINE ? *reinterpret_cast<const int32_t*>(rb + hoff[k])
+                          : *reinterpret_cast<const uint16_t*>(rb + hoff[k]);
+        if constexpr (FMT != QBLK_Q4_0) hc[i][k] = *reinterpret_cast<const int8_t*>(rb + coff[k]);
+        if constexpr (AFFINE) ha[i][k] = *reinterpret_cast<const int8_t*>(rb + coff[k] + 8);
+      }
       if constexpr (AFFINE) {
         const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(rb + off[k]);  // 4-aligned
         q[i][k][0] = v.x; q[i][k][1] = v.y; q[i][k][2] = v.z; q[i][k][3] = v.w;
@@ -436,11 +466,16 @@ __global__ __launch_bounds__(kThreadsH) void k_gemv_h(const uint8_t* __restrict_
       }
       float sc;
       if constexpr (FMT == QBLK_Q4_0) sc = f16_bits_to_f32(hs[i][k]);
+      else if constexpr (QK)
+        sc = f16_bits_to_f32(hk[i][k].x & 0xffffu) * static_cast<float>(q4k_scale6(hk[i][k].y, hk[i][k].z, sbj[k]));
       else sc = f16_bits_to_f32(hs[i][k] & 0xffff) * static_cast<float>(hc[i][k]);
       sc = live[k] ? sc : 0.0f;  // lanes past the row's last unit add 0
       acc[i] = __builtin_fmaf(sc, __builtin_fmaf(hi, 0.0625f, lo), acc[i]);
       if constexpr (AFFINE) {
-        float oa = f16_bits_to_f32(static_cast<uint32_t>(hs[i][k]) >> 16) * static_cast<float>(ha[i][k]);
+        float oa;
+        if constexpr (QK)
+          oa = -(f16_bits_to_f32(hk[i][k].x >> 16) * static_cast<float>(q4k_min6(hk[i][k].z, hk[i][k].w, sbj[k])));
+        else oa = f16_bits_to_f32(static_cast<uint32_t>(hs[i][k]) >> 16) * static_cast<float>(ha[i][k]);
         oa = live[k] ? oa : 0.0f;
         acc[i] = __builtin_fmaf(oa, sx[k], acc[i]);
       }
@@ -569,6 +604,7 @@ hipError_t launch_gemv(int fmt, const void* blocks, int64_t m, int64_t k, const 
                        float* y, hipStream_t s) {
   if (fmt == QBLK_Q4_0) return launch_fmt<QBLK_Q4_0>(blocks, m, k, x, xt, y, s);
   if (fmt == QBLK_SB4) return launch_fmt<QBLK_SB4>(blocks, m, k, x, xt, y, s);
+  if (fmt == QBLK_Q4_K) return launch_fmt<QBLK_Q4_K>(blocks, m, k, x, xt, y, s);
   return launch_fmt<QBLK_SB4_AFFINE>(blocks, m, k, x, xt, y, s);
 }
 

@@ -16,6 +16,8 @@ hipError_t launch_quantize_q4_0_ref(const float* w, int64_t rows, int64_t k, voi
                                     hipStream_t s);
 hipError_t launch_quantize_sb4(const void* w, int wt, int64_t rows, int64_t k, int affine,
                                void* blocks, hipStream_t s);
+hipError_t launch_quantize_q4_k(const void* w, int wt, int64_t rows, int64_t k, void* blocks,
+                                hipStream_t s);
 hipError_t launch_dequant(int fmt, const void* blocks, int64_t rows, int64_t k, void* out, int ot,
                           hipStream_t s);
 hipError_t launch_gemv(int fmt, const void* blocks, int64_t m, int64_t k, const void* x, int xt,

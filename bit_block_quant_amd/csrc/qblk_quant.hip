@@ -17,6 +17,8 @@
 //   Super-block ("GGUF K-quants" blog, "套娃"): eight sub-block scales stored
 //     as fp16, then quantized to INT8 in [-127, 127] against the fp16
 //     super-scale max/127 (steps 1-4), rebuilt as code*super-scale (step 5).
+//   Q4_K form (Q4_0 chapter 4.6): fp16 d and dmin per super-block, 6-bit
+//     scale s_j and min m_j per sub-block, weight (d*s_j)*code - dmin*m_j.
 #include "qblk_device.h"
 #include "qblk_launch.h"
 
@@ -479,6 +481,135 @@ __global__ __launch_bounds__(kThreads) void k_quant_sb4_g(const void* __restrict
   lds_to_global(stage, out + sb0 * B, static_cast<int>(ns * B));
 }
 
+// ------------------------------------------------------------------ Q4_K
+// Sub-block range lo = min(0, min w), hi = max w; first-level scale
+// (hi - lo)/15 and min -lo; d and dmin are fp16 of the largest of each over
+// 63; the 6-bit codes are taken against the stored d and dmin, the 4-bit codes
+// of (w + M_j)/S_j against the rebuilt S_j = d*s_j and M_j = dmin*m_j (both
+// exact in fp32).  Header dwords: d | dmin << 16, then the sixteen 6-bit
+// fields (s_0..s_7, m_0..m_7) at bits 6i of the next three dwords.  Each lane
+// forms the bits of its own sub-block's two fields; an OR over the lanes of a
+// super-block assembles the words.
+__device__ __forceinline__ void q4k_field_bits(uint32_t s6, uint32_t m6, int j, uint32_t& h1,
+                                               uint32_t& h2, uint32_t& h3) {
+  const uint64_t fs = static_cast<uint64_t>(s6) << (6 * j);  // field bits 0..47
+  const uint64_t fm = static_cast<uint64_t>(m6) << (6 * j);  // field bits 48..95, shifted down 48
+  h1 = static_cast<uint32_t>(fs);
+  h2 = static_cast<uint32_t>(fs >> 32) | (static_cast<uint32_t>(fm) << 16);
+  h3 = static_cast<uint32_t>(fm >> 16);
+}
+
+// The second level of one super-block, given this lane's sub-block scale and
+// min and the OR/max partners at lane distances m0, 2*m0, ... < mend.
+struct Q4kMeta {
+  uint32_t d16, m16, s6, m6;
+  float S, M;
+};
+template <int M0, int MEND>
+__device__ __forceinline__ Q4kMeta q4k_meta(float sc, float mn) {
+  float smax = sc, mmax = mn;
+#pragma unroll
+  for (int m = M0; m < MEND; m <<= 1) {
+    smax = __builtin_fmaxf(smax, __shfl_xor(smax, m, kWave));
+    mmax = __builtin_fmaxf(mmax, __shfl_xor(mmax, m, kWave));
+  }
+  Q4kMeta r;
+  // maxima are >= 0; a zero may carry a sign here, the stored value has none
+  r.d16 = f32_to_f16_bits(smax / 63.0f) & 0x7fffu;
+  r.m16 = f32_to_f16_bits(mmax / 63.0f) & 0x7fffu;
+  const float D = f16_bits_to_f32(r.d16), Dm = f16_bits_to_f32(r.m16);
+  r.s6 = static_cast<uint32_t>(code_of(sc, D, 0.0f, 63.0f));
+  r.m6 = static_cast<uint32_t>(code_of(mn, Dm, 0.0f, 63.0f));
+  r.S = D * static_cast<float>(r.s6);
+  r.M = Dm * static_cast<float>(r.m6);
+  return r;
+}
+
+template <int M0, int MEND>
+__device__ __forceinline__ uint4 q4k_header(const Q4kMeta& q, int j) {
+  uint32_t h1, h2, h3;
+  q4k_field_bits(q.s6, q.m6, j, h1, h2, h3);
+#pragma unroll
+  for (int m = M0; m < MEND; m <<= 1) {
+    h1 |= __shfl_xor(h1, m, kWave);
+    h2 |= __shfl_xor(h2, m, kWave);
+    h3 |= __shfl_xor(h3, m, kWave);
+  }
+  return make_uint4(q.d16 | (q.m16 << 16), h1, h2, h3);
+}
+
+// fp32 input, 8 weights per thread: threads 32s..32s+31 own super-block s,
+// thread v holding weights 8v..8v+7 (sub-block v/4).
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_quant_q4k(const void* __restrict__ w,
+                                                        uint8_t* __restrict__ out, int64_t nsb) {
+  constexpr int B = 144;
+  __shared__ uint4 stage4[8 * B / 16];
+  uint8_t* stage = reinterpret_cast<uint8_t*>(stage4);
+  const int t = threadIdx.x;
+  const int64_t sb0 = static_cast<int64_t>(blockIdx.x) * 8;
+  const int sl = t >> 5, v = t & 31, j = v >> 2, u = v & 3;
+  const bool valid = sb0 + sl < nsb;
+  float x[8];
+  load8<DT>(w, (sb0 + sl) * 256 + v * 8, valid, x);
+  float lo = x[0], hi = x[0];
+#pragma unroll
+  for (int i = 1; i < 8; i++) {
+    lo = __builtin_fminf(lo, x[i]);
+    hi = __builtin_fmaxf(hi, x[i]);
+  }
+  lo = group_min<4>(lo);
+  hi = group_max<4>(hi);
+  lo = lo < 0.0f ? lo : 0.0f;  // the range always reaches down to 0
+  const Q4kMeta q = q4k_meta<4, 32>((hi - lo) / 15.0f, -lo);
+  float xm[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) xm[i] = x[i] + q.M;
+  int n[8];
+  codes8(xm, q.S, 0.0f, 15.0f, n);
+  const uint4 hd = q4k_header<4, 32>(q, j);
+  uint32_t w0, w1;
+  pack_group(n, w0, w1);
+  if (valid) {
+    if (v == 0) *reinterpret_cast<uint4*>(stage + sl * B) = hd;
+    if (u < 2) *reinterpret_cast<uint2*>(stage + sl * B + 16 + 16 * j + 8 * u) = make_uint2(w0, w1);
+  }
+  __syncthreads();
+  const int64_t ns = nsb - sb0 < 8 ? nsb - sb0 : 8;
+  lds_to_global(stage, out + sb0 * B, static_cast<int>(ns * B));
+}
+
+// 16-bit input, one sub-block per thread: threads 8s..8s+7 own super-block s.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_quant_q4k_g(const void* __restrict__ w,
+                                                          uint8_t* __restrict__ out, int64_t nsb) {
+  constexpr int B = 144;
+  constexpr int SBW = kThreads / 8;
+  __shared__ uint4 stage4[SBW * B / 16];
+  uint8_t* stage = reinterpret_cast<uint8_t*>(stage4);
+  const int t = threadIdx.x;
+  const int64_t sb0 = static_cast<int64_t>(blockIdx.x) * SBW;
+  const int sl = t >> 3, j = t & 7;
+  const bool valid = sb0 + sl < nsb;
+  uint32_t h[16];
+  load_h16(w, (sb0 + sl) * 256 + 32 * j, valid, h);
+  float lo, hi;
+  minmax16<DT>(h, lo, hi);
+  lo = lo < 0.0f ? lo : 0.0f;
+  const Q4kMeta q = q4k_meta<1, 8>((hi - lo) / 15.0f, -lo);
+  uint32_t qw[4];
+  codes16<DT, true>(h, -q.M, q.S, 0.0f, 15.0f, 0.0f, qw);  // dividends fl(x + M)
+  const uint4 hd = q4k_header<1, 8>(q, j);
+  if (valid) {
+    uint8_t* blk = stage + sl * B;
+    if (j == 0) *reinterpret_cast<uint4*>(blk) = hd;
+    *reinterpret_cast<uint4*>(blk + 16 + 16 * j) = make_uint4(qw[0], qw[1], qw[2], qw[3]);
+  }
+  __syncthreads();
+  const int64_t ns = nsb - sb0 < SBW ? nsb - sb0 : SBW;
+  lds_to_global(stage, out + sb0 * B, static_cast<int>(ns * B));
+}
+
 // ------------------------------------------------------------- dequantize
 // 4-bit code of weight i (0..7 of this thread's 8) from the staged qs bytes of
 // a 32-weight group: threads u = 0,1 take low nibbles of bytes 8u..8u+7,
@@ -494,7 +625,7 @@ template <int FMT, int OT>
 __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict__ blocks,
                                                       void* __restrict__ out, int64_t nblocks) {
   constexpr int E = FMT == QBLK_Q4_0 ? 32 : 256;
-  constexpr int B = FMT == QBLK_Q4_0 ? 18 : (FMT == QBLK_SB4 ? 138 : 148);
+  constexpr int B = FMT == QBLK_Q4_0 ? 18 : FMT == QBLK_SB4 ? 138 : FMT == QBLK_Q4_K ? 144 : 148;
   constexpr int PER_WG = kWgWeights / E;  // 64 or 8
   __shared__ uint4 stage4[PER_WG * B / 16];
   uint8_t* stage = reinterpret_cast<uint8_t*>(stage4);
@@ -521,6 +652,17 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict_
     group_codes(blk + 10 + 16 * j, u, c);
 #pragma unroll
     for (int i = 0; i < 8; i++) y[i] = sj * static_cast<float>(c[i] - 8);
+  } else if constexpr (FMT == QBLK_Q4_K) {
+    const int j = (t & 31) >> 2;
+    const uint4 hd = *reinterpret_cast<const uint4*>(blk);
+    const float S = f16_bits_to_f32(hd.x & 0xffffu) * static_cast<float>(q4k_scale6(hd.y, hd.z, j));
+    const float M = f16_bits_to_f32(hd.x >> 16) * static_cast<float>(q4k_min6(hd.z, hd.w, j));
+    group_codes(blk + 16 + 16 * j, u, c);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const float p = S * static_cast<float>(c[i]);  // exact
+      y[i] = p - M;
+    }
   } else {
     const int j = (t & 31) >> 2;
     const uint32_t hdr = *reinterpret_cast<const uint32_t*>(blk);
@@ -588,6 +730,21 @@ hipError_t launch_quantize_sb4(const void* w, int wt, int64_t rows, int64_t k, i
   return hipGetLastError();
 }
 
+hipError_t launch_quantize_q4_k(const void* w, int wt, int64_t rows, int64_t k, void* blocks,
+                                hipStream_t s) {
+  const int64_t nsb = rows * k / 256;
+  uint8_t* out = static_cast<uint8_t*>(blocks);
+  if (wt == QBLK_F32) {
+    hipLaunchKernelGGL(k_quant_q4k<QBLK_F32>, dim3(static_cast<unsigned>((nsb + 7) / 8)), dim3(kThreads), 0, s,
+                       w, out, nsb);
+    return hipGetLastError();
+  }
+  const unsigned g = static_cast<unsigned>((nsb + kThreads / 8 - 1) / (kThreads / 8));
+  if (wt == QBLK_F16) hipLaunchKernelGGL(k_quant_q4k_g<QBLK_F16>, dim3(g), dim3(kThreads), 0, s, w, out, nsb);
+  else hipLaunchKernelGGL(k_quant_q4k_g<QBLK_BF16>, dim3(g), dim3(kThreads), 0, s, w, out, nsb);
+  return hipGetLastError();
+}
+
 template <int FMT>
 static void launch_deq_t(const uint8_t* b, int64_t nblk, void* out, int ot, unsigned g, hipStream_t s) {
   if (ot == QBLK_F32) hipLaunchKernelGGL((k_dequant<FMT, QBLK_F32>), dim3(g), dim3(kThreads), 0, s, b, out, nblk);
@@ -601,6 +758,7 @@ hipError_t launch_dequant(int fmt, const void* blocks, int64_t rows, int64_t k, 
   const unsigned g = grid_for(rows * k);
   if (fmt == QBLK_Q4_0) launch_deq_t<QBLK_Q4_0>(b, rows * k / 32, out, ot, g, s);
   else if (fmt == QBLK_SB4) launch_deq_t<QBLK_SB4>(b, rows * k / 256, out, ot, g, s);
+  else if (fmt == QBLK_Q4_K) launch_deq_t<QBLK_Q4_K>(b, rows * k / 256, out, ot, g, s);
   else launch_deq_t<QBLK_SB4_AFFINE>(b, rows * k / 256, out, ot, g, s);
   return hipGetLastError();
 }

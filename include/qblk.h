@@ -32,15 +32,26 @@
  *                    (Same blog, section "套娃": Type 1 blocks also carry an
  *                    offset whose fp16 value is compressed to INT8.)
  *
+ *   QBLK_Q4_K        super-block of 256 weights in 144 bytes (4.5 bit/weight):
+ *                      [d: fp16][dmin: fp16][f: 12 bytes][qs: 8 x 16 bytes]
+ *                    per 32-weight sub-block j a 6-bit scale s_j and a 6-bit
+ *                    min m_j; field i of the sixteen 6-bit fields (s_0..s_7,
+ *                    then m_0..m_7) sits at bits 6i..6i+5 of f read as one
+ *                    little-endian integer; codes 0..15 stored as in Q4_0;
+ *                    a weight is (d * s_j) * code - dmin * m_j.
+ *                    (Q4_0 chapter, section 4.6, which names the 6-bit
+ *                    packing without describing it: the field order is this
+ *                    library's.)
+ *
  * Matrices are dense row-major.  A packed matrix of rows x k weights stores row
  * r, block b at byte (r * k/E + b) * B, with E weights and B bytes per block.
  *
- * Quantization rule (the same for all three formats; both the codes and the
- * INT8 scales are computed against the scale the block STORES, decoded back
- * from fp16): code = clamp(round_half_away(v / s), lo, hi), with IEEE fp32
- * division, a zero scale giving code 0 (Q4_0/Type 0: stored code 8), fp16
- * rounding to nearest even with subnormals kept.  Q4_0 uses s = absmax/7 per
- * 32 weights.  The GPU library reproduces the CPU definition bit for bit.
+ * Quantization rule (the same for all formats; both the codes and the INT8
+ * or 6-bit scales are computed against the scale the block STORES, decoded
+ * back from fp16): code = clamp(round_half_away(v / s), lo, hi), with IEEE
+ * fp32 division, a zero scale giving code 0 (Q4_0/Type 0: stored code 8),
+ * fp16 rounding to nearest even with subnormals kept.  Q4_0 uses s = absmax/7
+ * per 32 weights.  The GPU library reproduces the CPU definition bit for bit.
  *
  * Conventions for every entry point:
  *   - Pointers to data are DEVICE pointers owned by the caller; the library
@@ -74,7 +85,8 @@ extern "C" {
 typedef enum {
   QBLK_Q4_0 = 0,       /* 32 weights, 18 bytes  */
   QBLK_SB4 = 1,        /* 256 weights, 138 bytes */
-  QBLK_SB4_AFFINE = 2  /* 256 weights, 148 bytes */
+  QBLK_SB4_AFFINE = 2, /* 256 weights, 148 bytes */
+  QBLK_Q4_K = 3        /* 256 weights, 144 bytes */
 } qblk_format_t;
 
 typedef enum {
@@ -117,6 +129,16 @@ qblk_status_t qblk_quantize_sb4(const void* w, qblk_dtype_t wt, int64_t rows,
                                 int64_t k, int affine, void* blocks,
                                 qblk_stream_t stream);
 
+/* Quantize w (element type F32, F16 or BF16) into QBLK_Q4_K super-blocks.
+ * Q4_0 chapter, section 4.6 gives the form y = d*s_j*q - dmin*m_j; the steps
+ * it leaves open are taken as: sub-block range lo = min(0, min w), hi = max w;
+ * first-level scale (hi - lo)/15 and min -lo in fp32; d = fp16(max scale/63),
+ * dmin = fp16(max min/63); s_j, m_j = clamp(round_half_away(v / stored), 0, 63);
+ * codes clamp(round_half_away((w + dmin*m_j) / (d*s_j)), 0, 15) with the
+ * rebuilt (exact fp32) d*s_j and dmin*m_j. */
+qblk_status_t qblk_quantize_q4_k(const void* w, qblk_dtype_t wt, int64_t rows,
+                                 int64_t k, void* blocks, qblk_stream_t stream);
+
 /* Q4_0 quantization as the Q4_0 chapter's section 4.4 prints it: the signed
  * value of largest magnitude divided by -8 is the scale, codes are
  * min(15, trunc(w * (1/d) + 8.5)) with the fp32 reciprocal.  Input F32 only
@@ -126,9 +148,10 @@ qblk_status_t qblk_quantize_q4_0_ref(const void* w, qblk_dtype_t wt,
                                      qblk_stream_t stream);
 
 /* Rebuild the weights from blocks into out (rows x k, type ot in {F32, F16,
- * BF16}).  F32 output is the exact fp32 value of the format's formula (Q4_0
- * chapter section 4.3 for Q4_0; K-quants blog step 5 for the super-blocks);
- * F16/BF16 outputs are that value rounded to nearest even. */
+ * BF16}).  F32 output is the fp32 value of the format's formula (Q4_0
+ * chapter section 4.3 for Q4_0; K-quants blog step 5 for the super-blocks;
+ * chapter section 4.6 for Q4_K, one rounding of the exact product minus the
+ * exact min); F16/BF16 outputs are that value rounded to nearest even. */
 qblk_status_t qblk_dequant(qblk_format_t fmt, const void* blocks, int64_t rows,
                            int64_t k, void* out, qblk_dtype_t ot,
                            qblk_stream_t stream);
@@ -142,7 +165,7 @@ qblk_status_t qblk_gemv(qblk_format_t fmt, const void* blocks, int64_t m,
                         qblk_stream_t stream);
 
 /* Small-batch product Y = X W^T: X is n x k row-major (token-major) of type xt,
- * Y is n x m row-major fp32.  All three formats run on the bf16 matrix cores
+ * Y is n x m row-major fp32.  All four formats run on the bf16 matrix cores
  * with xt = BF16; F32/F16 activations, and Q4_0 with k % 256 != 0, return
  * QBLK_ERR_UNSUPPORTED.  Same error bound as qblk_gemv, per output element.
  * When k spans many groups and m*n is small the k range is split over the

@@ -25,7 +25,8 @@ def q():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for f in ("qblk_quantize_q4_0", "qblk_quantize_sb4", "qblk_dequant", "qblk_gemv", "qblk_gemm"):
+    for f in ("qblk_quantize_q4_0", "qblk_quantize_sb4", "qblk_quantize_q4_k", "qblk_dequant", "qblk_gemv",
+              "qblk_gemm"):
         assert f in names
 
 
@@ -37,8 +38,9 @@ def test_library_exports_every_declared_symbol(q):
 
 
 def test_geometry(q):
-    assert [q.block_bytes(f) for f in (q.Q4_0, q.SB4, q.SB4_AFFINE)] == [18, 138, 148]
-    assert [q.block_elems(f) for f in (q.Q4_0, q.SB4, q.SB4_AFFINE)] == [32, 256, 256]
+    assert [q.block_bytes(f) for f in (q.Q4_0, q.SB4, q.SB4_AFFINE, q.Q4_K)] == [18, 138, 148, 144]
+    assert [q.block_elems(f) for f in (q.Q4_0, q.SB4, q.SB4_AFFINE, q.Q4_K)] == [32, 256, 256, 256]
+    assert q.packed_bytes(q.Q4_K, 11008, 4096) == 11008 * 16 * 144
     assert q.block_bytes(9) == 0 and q.block_elems(9) == 0
     assert q.packed_bytes(q.SB4, 11008, 4096) == 24305664
     assert q.packed_bytes(q.Q4_0, 4096, 4096) == 9437184
@@ -76,6 +78,10 @@ def test_argument_errors(q):
     assert L.qblk_gemv(1, A, 1, 256, B, 5, Y, S) == 3
     assert L.qblk_quantize_q4_0(A, 3, 1, 32, B, S) == 3
     assert L.qblk_quantize_q4_0_ref(A, 1, 1, 32, B, S) == 3
+    assert L.qblk_quantize_q4_k(A, 3, 1, 256, B, S) == 3
+    assert L.qblk_quantize_q4_k(A, 0, 1, 32, B, S) == 2
+    assert L.qblk_quantize_q4_k(A, 0, 1, 256, MIS, S) == 4
+    assert L.qblk_dequant(4, A, 1, 256, B, 0, S) == 7
     # null and misaligned pointers
     assert L.qblk_quantize_q4_0(NUL, 0, 1, 32, B, S) == 1
     assert L.qblk_dequant(0, A, 1, 32, NUL, 0, S) == 1
@@ -96,6 +102,7 @@ def test_empty_calls_succeed_without_launch(q):
     L = q.lib()
     assert L.qblk_quantize_q4_0(NUL, 0, 0, 32, NUL, S) == 0
     assert L.qblk_quantize_sb4(NUL, 1, 5, 0, 1, NUL, S) == 0
+    assert L.qblk_quantize_q4_k(NUL, 2, 0, 256, NUL, S) == 0
     assert L.qblk_dequant(2, NUL, 0, 256, NUL, 2, S) == 0
     assert L.qblk_gemv(1, NUL, 0, 256, NUL, 1, NUL, S) == 0
     assert L.qblk_gemm(1, NUL, 0, 256, NUL, 2, 8, NUL, S) == 0

@@ -15,8 +15,8 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-5
-FMTS = [O.Q4_0, O.SB4, O.SB4_AFFINE]
-NAMES = {O.Q4_0: "q4_0", O.SB4: "sb4", O.SB4_AFFINE: "sb4a"}
+FMTS = [O.Q4_0, O.SB4, O.SB4_AFFINE, O.Q4_K]
+NAMES = {O.Q4_0: "q4_0", O.SB4: "sb4", O.SB4_AFFINE: "sb4a", O.Q4_K: "q4k"}
 
 
 @pytest.fixture(scope="module")
@@ -112,6 +112,24 @@ def test_quantize_extreme_f16_inputs(q):
         assert np.array_equal(got, O.quantize(fmt, w)), NAMES[fmt]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_quantize_q4_k_one_sided_ranges_and_signed_zeros(q, dtype):
+    # sub-blocks with no negative weight (min 0), none positive, negative
+    # zeros only, a mix of +0 and -0, and single nonzero entries
+    rng = np.random.default_rng(15)
+    w = np.abs(rng.standard_normal((6, 2048)).astype(np.float32)) * 0.03
+    w[1] = -w[1]
+    w[2] = -0.0
+    w[3, ::2] = -0.0
+    w[3, 1::2] = 0.0
+    w[4] = 0.0
+    w[4, ::37] = -rng.uniform(0.01, 1.0, w[4, ::37].size)
+    w[5, :1024] = -0.0
+    d, h = gpu_input(w, dtype)
+    got = host(q.quantize(d, q.Q4_K))
+    assert np.array_equal(got, O.quantize_q4_k(h))
+
+
 def test_quantize_q4_0_reference_mode(q):
     w = mixed_blocks(8, 4096, 3)
     vals = np.array([0.01 * (i - 15) / 15 for i in range(31)] + [10.0], np.float32)
@@ -140,7 +158,7 @@ def random_blocks(fmt, nblk, seed):
     rng = np.random.default_rng(seed)
     nb = O.block_bytes(fmt)
     b = rng.integers(0, 256, (nblk, nb), dtype=np.uint8)
-    nscale = 1 if fmt != O.SB4_AFFINE else 2
+    nscale = 2 if fmt in (O.SB4_AFFINE, O.Q4_K) else 1
     s = rng.integers(0, 0x7C00, (nblk, nscale)).astype(np.uint16)  # finite, incl. subnormal
     s |= (rng.integers(0, 2, (nblk, nscale)) << 15).astype(np.uint16)
     b[:, : 2 * nscale] = s.view(np.uint8).reshape(nblk, 2 * nscale)
@@ -238,6 +256,17 @@ def test_gemv_sb4_decode_config(q, shape):
     check_products(y, y_ref, bound, f"sb4 {m}x{k} f16")
 
 
+def test_gemv_q4_k_decode_shape(q):
+    w, x = WL.sb4_decode("up")
+    m, k = w.shape
+    blocks = O.quantize_q4_k(w)
+    bd = q.quantize(dev(w), q.Q4_K)
+    assert np.array_equal(host(bd), blocks)
+    y = host(q.gemv(bd, q.Q4_K, m, k, dev(x)))
+    y_ref, bound = O.gemv(O.Q4_K, blocks, m, k, x.astype(np.float64))
+    check_products(y, y_ref, bound, f"q4k {m}x{k} f16")
+
+
 def test_gemv_stack_matrices(q):
     for layer, p in ((0, 0), (0, 4), (31, 6)):
         w, x = WL.sb4a_stack_matrix(layer, p)
@@ -279,13 +308,13 @@ def test_gemm_tolerance_small(q, n):
 
 def gemm_fmt(q, name):
     """(library format id, oracle format id) for a format name."""
-    return {"q4_0": (q.Q4_0, O.Q4_0), "sb4a": (q.SB4_AFFINE, O.SB4_AFFINE)}[name]
+    return {"q4_0": (q.Q4_0, O.Q4_0), "sb4a": (q.SB4_AFFINE, O.SB4_AFFINE), "q4k": (q.Q4_K, O.Q4_K)}[name]
 
 
-@pytest.mark.parametrize("fmt", ["q4_0", "sb4a"])
+@pytest.mark.parametrize("fmt", ["q4_0", "sb4a", "q4k"])
 @pytest.mark.parametrize("n", [1, 16, 24, 40, 64, 100])
 def test_gemm_other_formats(q, fmt, n):
-    # Q4_0 (scale per 32-block) and Type 1 (scale and offset per sub-block)
+    # Q4_0 (scale per 32-block), Type 1 and Q4_K (scale and offset per sub-block)
     m, k = 150, 2304
     f, of = gemm_fmt(q, fmt)
     w = mixed_blocks(m, k, 21)
@@ -296,7 +325,7 @@ def test_gemm_other_formats(q, fmt, n):
     check_products(Y, Y_ref, B, f"gemm {fmt} n={n}")
 
 
-@pytest.mark.parametrize("fmt", ["q4_0", "sb4a"])
+@pytest.mark.parametrize("fmt", ["q4_0", "sb4a", "q4k"])
 @pytest.mark.parametrize("n", [20, 130])
 def test_gemm_other_formats_split_k(q, fmt, n):
     # long K with few rows: K is split over the grid and summed into Y
@@ -335,3 +364,17 @@ def test_gemm_prefill_config(q, shape, n):
     rows = np.concatenate([rows, [0, m - 1]])
     Y_ref, B = O.gemm(O.SB4, blocks, m, k, WL.bf16_values(X).astype(np.float64), rows=rows)
     check_products(Y[:, rows], Y_ref, B, f"gemm {shape} n={n}")
+
+
+@pytest.mark.parametrize("n", [16, 64, 512])
+def test_gemm_q4_k_prefill_shape(q, n):
+    w, X = WL.sb4_prefill("up", n)
+    m, k = w.shape
+    blocks = O.quantize_q4_k(w)
+    bd = q.quantize(dev(w), q.Q4_K)
+    assert np.array_equal(host(bd), blocks)
+    Y = host(q.gemm(bd, q.Q4_K, m, k, dev_bf16(X)))
+    rows = np.random.default_rng(n + 1).choice(m, size=64 if n == 512 else 256, replace=False)
+    rows = np.concatenate([rows, [0, m - 1]])
+    Y_ref, B = O.gemm(O.Q4_K, blocks, m, k, WL.bf16_values(X).astype(np.float64), rows=rows)
+    check_products(Y[:, rows], Y_ref, B, f"gemm q4k n={n}")
