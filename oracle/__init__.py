@@ -13,7 +13,7 @@ import numpy as np
 
 from . import build as _build
 
-Q4_0, SB4, SB4_AFFINE, Q4_K = 0, 1, 2, 3
+Q4_0, SB4, SB4_AFFINE, Q4_K, W4G128 = 0, 1, 2, 3, 4
 F32, F16, BF16 = 0, 1, 2
 
 _lib = None
@@ -39,11 +39,15 @@ def lib():
         L.orc_quantize_q4_0_ref.argtypes = [p, i64, i64, p]
         L.orc_quantize_sb4.argtypes = [p, i32, i64, i64, i32, p]
         L.orc_quantize_q4_k.argtypes = [p, i32, i64, i64, p]
+        L.orc_quantize_w4g128.argtypes = [p, i32, i64, i64, p]
+        L.orc_quantize_act_i8.argtypes = [p, i32, i64, i64, p, p]
+        L.orc_gemm_w4a8.argtypes = [p, i64, i64, p, p, i64, p, i64, p, p]
         L.orc_dequant.argtypes = [i32, p, i64, i64, p]
         L.orc_gemv.argtypes = [i32, p, i64, i64, p, p, i64, p, p]
         L.orc_gemm.argtypes = [i32, p, i64, i64, p, i64, p, i64, p, p]
         for f in ("orc_meta_int8", "orc_quantize_q4_0", "orc_quantize_q4_0_ref",
-                  "orc_quantize_sb4", "orc_quantize_q4_k", "orc_dequant", "orc_gemv", "orc_gemm"):
+                  "orc_quantize_sb4", "orc_quantize_q4_k", "orc_quantize_w4g128",
+                  "orc_quantize_act_i8", "orc_gemm_w4a8", "orc_dequant", "orc_gemv", "orc_gemm"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -148,9 +152,51 @@ def quantize_q4_k(w):
     return out
 
 
+def quantize_w4g128(w):
+    """TurboQuant article 2.1: per-row symmetric groups of 128, 4-bit (planar layout)."""
+    arr, tag = _dense(w)
+    rows, k = arr.shape
+    out = np.zeros(packed_bytes(W4G128, rows, k), dtype=np.uint8)
+    _check(lib().orc_quantize_w4g128(_ptr(arr), tag, rows, k, _ptr(out)), "quantize_w4g128")
+    return out
+
+
+def quantize_act_i8(x):
+    """TurboQuant article 2.2: 8-bit activations, one symmetric scale per row (token).
+    Returns (xq int8 n x k, scale float32 n)."""
+    arr, tag = _dense(x)
+    n, k = arr.shape
+    xq = np.zeros((n, k), dtype=np.int8)
+    sc = np.zeros(n, dtype=np.float32)
+    _check(lib().orc_quantize_act_i8(_ptr(arr), tag, n, k, _ptr(xq), _ptr(sc)), "quantize_act_i8")
+    return xq, sc
+
+
+def gemm_w4a8(blocks, m, k, xq, scale, rows=None):
+    """fp64 Y (n x nrows) of the rebuilt weights times the rebuilt activations, and the bound."""
+    b = np.ascontiguousarray(blocks, dtype=np.uint8)
+    q = np.ascontiguousarray(xq, dtype=np.int8)
+    s = np.ascontiguousarray(scale, dtype=np.float32)
+    n = q.shape[0]
+    assert q.shape[1] == k and s.size == n
+    if rows is None:
+        idx, nr = None, m
+    else:
+        idx = np.ascontiguousarray(rows, dtype=np.int64)
+        nr = idx.size
+    Y = np.zeros((n, nr), dtype=np.float64)
+    B = np.zeros((n, nr), dtype=np.float64)
+    _check(lib().orc_gemm_w4a8(_ptr(b), m, k, _ptr(q), _ptr(s), n,
+                               _ptr(idx) if idx is not None else None, nr, _ptr(Y), _ptr(B)),
+           "gemm_w4a8")
+    return Y, B
+
+
 def quantize(fmt, w):
     if fmt == Q4_0:
         return quantize_q4_0(w)
+    if fmt == W4G128:
+        return quantize_w4g128(w)
     if fmt == Q4_K:
         return quantize_q4_k(w)
     return quantize_sb4(w, affine=(fmt == SB4_AFFINE))

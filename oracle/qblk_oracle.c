@@ -37,6 +37,16 @@
  *   R26 Q4_K 4-bit codes against the rebuilt S_j = d*s_j and M_j = dmin*m_j:
  *       clamp(rha((w + M_j) / S_j), 0, 15).
  *   R27 Q4_K dequant fl(S_j*q - M_j) (S_j*q and M_j are exact in fp32).
+ *   R28 group-128 W4 layout (the TurboQuant article gives none): planar, the
+ *       code plane (rows x k/2 bytes; byte j of group g holds weight 128g+j
+ *       in its low nibble and weight 128g+64+j in its high nibble) followed
+ *       by the fp16 scale plane (rows x k/128, row-major).
+ *   R29 group-128 W4 rule: symmetric, d = fp16(absmax/7) per group, code
+ *       clamp(rha(w/d), -8, 7) stored +8 (R1 with groups of 128).
+ *   R30 8-bit activations: one symmetric scale per token (row of X),
+ *       s = absmax/127 kept in fp32, codes clamp(rha(x/s), -127, 127).
+ *   R31 the W4A8 product is that of the rebuilt weights and the rebuilt
+ *       activations s*xq (fp64 sums here).
  */
 #include "qblk_oracle.h"
 
@@ -152,6 +162,7 @@ static uint16_t get_u16(const uint8_t* p) {
 
 int orc_block_elems(int fmt) {
   if (fmt == ORC_Q4_0) return 32;
+  if (fmt == ORC_W4G128) return 128;
   if (fmt == ORC_SB4 || fmt == ORC_SB4_AFFINE || fmt == ORC_Q4_K) return 256;
   return 0;
 }
@@ -166,6 +177,8 @@ int orc_block_bytes(int fmt) {
   if (fmt == ORC_SB4_AFFINE) return 2 + 2 + 8 + 8 + 256 / 2;
   /* Q4_K: fp16 d and dmin, 16 six-bit fields (96 bits), 128 bytes of codes */
   if (fmt == ORC_Q4_K) return 2 + 2 + 16 * 6 / 8 + 256 / 2;
+  /* group-128 W4: 64 code bytes and one fp16 scale, in two planes (R28) */
+  if (fmt == ORC_W4G128) return 128 / 2 + 2;
   return 0;
 }
 
@@ -408,6 +421,58 @@ int orc_quantize_q4_k(const void* w, int dtype, int64_t rows, int64_t k,
 }
 
 /* ------------------------------------------------------------------ */
+/* Group-128 W4 weights with 8-bit activations (TurboQuant article,    */
+/* sections 2.1-2.2): per row, groups of 128 weights share one scale   */
+/* from their own maximum and map to 4-bit integers; activations are  */
+/* 8-bit.  Readings R28-R31.                                           */
+/* ------------------------------------------------------------------ */
+int orc_quantize_w4g128(const void* w, int dtype, int64_t rows, int64_t k,
+                        uint8_t* out) {
+  if (!w || !out || rows < 0 || k < 0 || k % 128 != 0) return -1;
+  if (dtype < ORC_F32 || dtype > ORC_BF16) return -1;
+  const int64_t ng = k / 128;
+  uint8_t* scales = out + rows * (k / 2);
+  for (int64_t r = 0; r < rows; r++)
+    for (int64_t g = 0; g < ng; g++) {
+      float x[128];
+      float amax = 0.0f;
+      for (int i = 0; i < 128; i++) {
+        x[i] = load_elem(w, dtype, r * k + g * 128 + i);
+        if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
+      }
+      /* symmetric: the largest magnitude maps to 7, the codes span [-8, 7] */
+      const uint16_t d16 = orc_f32_to_f16(amax / 7.0f);
+      const float d = orc_f16_to_f32(d16);
+      uint8_t* qs = out + r * (k / 2) + g * 64;
+      for (int j = 0; j < 64; j++) {
+        const int lo = clamp_code(orc_rha(qdiv(x[j], d)), -8, 7) + 8;
+        const int hi = clamp_code(orc_rha(qdiv(x[64 + j], d)), -8, 7) + 8;
+        qs[j] = (uint8_t)(lo | (hi << 4));
+      }
+      put_u16(scales + (r * ng + g) * 2, d16);
+    }
+  return 0;
+}
+
+int orc_quantize_act_i8(const void* x, int dtype, int64_t n, int64_t k,
+                        int8_t* xq, float* scale) {
+  if (!x || !xq || !scale || n < 0 || k < 0) return -1;
+  if (dtype < ORC_F32 || dtype > ORC_BF16) return -1;
+  for (int64_t t = 0; t < n; t++) {
+    float amax = 0.0f;
+    for (int64_t i = 0; i < k; i++) {
+      const float v = fabsf(load_elem(x, dtype, t * k + i));
+      if (v > amax) amax = v;
+    }
+    const float s = amax / 127.0f; /* INT8 levels -127 .. 127 */
+    for (int64_t i = 0; i < k; i++)
+      xq[t * k + i] = (int8_t)clamp_code(orc_rha(qdiv(load_elem(x, dtype, t * k + i), s)), -127, 127);
+    scale[t] = s;
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* dequantization                                                      */
 /* ------------------------------------------------------------------ */
 
@@ -416,9 +481,24 @@ static int nib(const uint8_t* qs, int i) {
   return i < 16 ? (qs[i] & 0x0F) : ((qs[i - 16] >> 4) & 0x0F);
 }
 
-/* one row of k weights -> fp32 values */
-static void dequant_row(int fmt, const uint8_t* row, int64_t k, float* y) {
-  if (fmt == ORC_Q4_0) {
+static int64_t row_bytes(int fmt, int64_t k);
+
+/* row r of an m x k packed matrix -> k fp32 values */
+static void dequant_row(int fmt, const uint8_t* blocks, int64_t m, int64_t k,
+                        int64_t r, float* y) {
+  const uint8_t* row = blocks + r * row_bytes(fmt, k);
+  if (fmt == ORC_W4G128) {
+    const uint8_t* codes = blocks + r * (k / 2);
+    const uint8_t* scales = blocks + m * (k / 2) + r * (k / 128) * 2;
+    for (int64_t g = 0; g < k / 128; g++) {
+      const float d = orc_f16_to_f32(get_u16(scales + 2 * g));
+      for (int j = 0; j < 64; j++) {
+        const uint8_t b = codes[g * 64 + j];
+        y[g * 128 + j] = d * (float)((b & 0x0F) - 8);
+        y[g * 128 + 64 + j] = d * (float)((b >> 4) - 8);
+      }
+    }
+  } else if (fmt == ORC_Q4_0) {
     for (int64_t b = 0; b < k / 32; b++) {
       const uint8_t* blk = row + b * 18;
       float d = orc_f16_to_f32(get_u16(blk));
@@ -470,6 +550,8 @@ static int fmt_ok(int fmt, int64_t k) {
   return e > 0 && k >= 0 && k % e == 0;
 }
 
+/* bytes of one row in the packed stream (for the planar group-128 format,
+ * only rows of the same plane are this far apart) */
 static int64_t row_bytes(int fmt, int64_t k) {
   return k / orc_block_elems(fmt) * orc_block_bytes(fmt);
 }
@@ -478,7 +560,7 @@ int orc_dequant(int fmt, const uint8_t* blocks, int64_t rows, int64_t k,
                 float* out) {
   if (!blocks || !out || rows < 0 || !fmt_ok(fmt, k)) return -1;
   for (int64_t r = 0; r < rows; r++)
-    dequant_row(fmt, blocks + r * row_bytes(fmt, k), k, out + r * k);
+    dequant_row(fmt, blocks, rows, k, r, out + r * k);
   return 0;
 }
 
@@ -498,7 +580,7 @@ int orc_gemv(int fmt, const uint8_t* blocks, int64_t m, int64_t k,
       free(w);
       return -1;
     }
-    dequant_row(fmt, blocks + r * row_bytes(fmt, k), k, w);
+    dequant_row(fmt, blocks, m, k, r, w);
     double acc = 0.0, b = 0.0;
     for (int64_t c = 0; c < k; c++) {
       double p = (double)w[c] * x[c];
@@ -525,12 +607,45 @@ int orc_gemm(int fmt, const uint8_t* blocks, int64_t m, int64_t k,
       free(w);
       return -1;
     }
-    dequant_row(fmt, blocks + r * row_bytes(fmt, k), k, w);
+    dequant_row(fmt, blocks, m, k, r, w);
     for (int64_t t = 0; t < n; t++) {
       const double* xr = X + t * k;
       double acc = 0.0, b = 0.0;
       for (int64_t c = 0; c < k; c++) {
         double p = (double)w[c] * xr[c];
+        acc += p;
+        b += fabs(p);
+      }
+      Y[t * nrows + i] = acc;
+      if (bound) bound[t * nrows + i] = b;
+    }
+  }
+  free(w);
+  return 0;
+}
+
+/* W4A8 product (R31): Y[t, i] = sum_k W[row_i, k] * (scale[t] * xq[t, k]),
+ * fp64 sums over the fp32 rebuilt weights and the fp32 rebuilt activations
+ * (scale * code is exact in fp64). */
+int orc_gemm_w4a8(const uint8_t* blocks, int64_t m, int64_t k,
+                  const int8_t* xq, const float* scale, int64_t n,
+                  const int64_t* row_idx, int64_t nrows, double* Y,
+                  double* bound) {
+  if (!blocks || !xq || !scale || !Y || m < 0 || n < 0 || !fmt_ok(ORC_W4G128, k)) return -1;
+  if (!row_idx) nrows = m;
+  float* w = (float*)malloc(sizeof(float) * (size_t)(k > 0 ? k : 1));
+  if (!w) return -2;
+  for (int64_t i = 0; i < nrows; i++) {
+    int64_t r = row_idx ? row_idx[i] : i;
+    if (r < 0 || r >= m) {
+      free(w);
+      return -1;
+    }
+    dequant_row(ORC_W4G128, blocks, m, k, r, w);
+    for (int64_t t = 0; t < n; t++) {
+      double acc = 0.0, b = 0.0;
+      for (int64_t c = 0; c < k; c++) {
+        double p = (double)w[c] * ((double)scale[t] * (double)xq[t * k + c]);
         acc += p;
         b += fabs(p);
       }

@@ -15,6 +15,8 @@
  *         4.1.2 (block layout), 4.2.1 (nibble order), 4.2.2 (code range and
  *         the minus-8 offset), 4.3 (dequantization), 4.4 (quantizer), 4.5
  *         (outlier example), 4.6 (the Q4_K form: d, dmin, 6-bit s_j and m_j).
+ *   [TQ]  the TurboQuant W4A8 article (codechina.net), sections 2.1 (per-row
+ *         symmetric groups of 128 weights, 4-bit) and 2.2 (8-bit activations).
  *
  * Conventions (fp32 IEEE arithmetic, no FMA contraction, true division):
  *   h(v)  fp32 -> fp16 bits, round-to-nearest-even, subnormals kept.
@@ -41,6 +43,7 @@ extern "C" {
 #define ORC_SB4 1        /* 256 weights, 138 bytes (Type 0) */
 #define ORC_SB4_AFFINE 2 /* 256 weights, 148 bytes (Type 1) */
 #define ORC_Q4_K 3       /* 256 weights, 144 bytes ([Q40] 4.6 form) */
+#define ORC_W4G128 4     /* 128 weights: 64 code bytes + fp16 scale, two planes ([TQ]) */
 
 /* element types of dense inputs */
 #define ORC_F32 0
@@ -68,7 +71,8 @@ int orc_meta_int8(const float* s, int n, float S_forced, int8_t* codes,
                   uint16_t* S16, float* S_used);
 
 /* Quantize a dense rows x k matrix (dtype ORC_F32/F16/BF16, row-major) into
- * the packed block stream (row r, block b at (r*k/elems + b)*block_bytes). */
+ * the packed block stream (row r, block b at (r*k/elems + b)*block_bytes;
+ * the group-128 W4 format is planar instead, see R28). */
 int orc_quantize_q4_0(const void* w, int dtype, int64_t rows, int64_t k,
                       uint8_t* out);
 int orc_quantize_sb4(const void* w, int dtype, int64_t rows, int64_t k,
@@ -78,6 +82,19 @@ int orc_quantize_sb4(const void* w, int dtype, int64_t rows, int64_t k,
  * page leaves open are the readings R23-R27 listed in qblk_oracle.c). */
 int orc_quantize_q4_k(const void* w, int dtype, int64_t rows, int64_t k,
                       uint8_t* out);
+
+/* [TQ] group-128 symmetric 4-bit weights (readings R28-R29 in qblk_oracle.c)
+ * and per-token symmetric 8-bit activations (R30): xq is n x k int8, scale
+ * has n fp32 entries.  gemm_w4a8 is the product of the rebuilt operands
+ * (R31), fp64 sums, rows as in orc_gemm. */
+int orc_quantize_w4g128(const void* w, int dtype, int64_t rows, int64_t k,
+                        uint8_t* out);
+int orc_quantize_act_i8(const void* x, int dtype, int64_t n, int64_t k,
+                        int8_t* xq, float* scale);
+int orc_gemm_w4a8(const uint8_t* blocks, int64_t m, int64_t k,
+                  const int8_t* xq, const float* scale, int64_t n,
+                  const int64_t* row_idx, int64_t nrows, double* Y,
+                  double* bound);
 
 /* Q4_0 quantizer as [Q40] 4.4 prints it (signed extreme / -8, reciprocal
  * multiply, +8.5 and truncation, upper clamp at 15). */

@@ -96,6 +96,29 @@ int main(void) {
     free(b2);
   }
   {
+    /* group-128 W4 weights (two planes at exact sizes) and int8 activations */
+    const size_t wb = (size_t)(rows * k / 2 + rows * (k / 128) * 2);
+    uint8_t* b = malloc(wb);
+    int8_t* xq = malloc((size_t)(n * k));
+    float* xs = malloc(sizeof(float) * (size_t)n);
+    if (!b || !xq || !xs) return fail("out of memory");
+    if (orc_quantize_w4g128(w, ORC_F32, rows, k, b) != 0) return fail("quantize_w4g128 failed");
+    if (orc_quantize_w4g128(w16, ORC_F16, rows, k, b) != 0) return fail("quantize_w4g128 f16 failed");
+    if (orc_dequant(ORC_W4G128, b, rows, k, back) != 0) return fail("w4g128 dequant failed");
+    float* Xf = malloc(sizeof(float) * (size_t)(n * k));
+    if (!Xf) return fail("out of memory");
+    for (int64_t i = 0; i < n * k; i++) Xf[i] = (float)X[i];
+    if (orc_quantize_act_i8(Xf, ORC_F32, n, k, xq, xs) != 0) return fail("quantize_act_i8 failed");
+    if (orc_gemm_w4a8(b, rows, k, xq, xs, n, NULL, rows, Y, Yb) != 0) return fail("gemm_w4a8 failed");
+    const int64_t sel[2] = {rows - 1, 1};
+    if (orc_gemm_w4a8(b, rows, k, xq, xs, n, sel, 2, Y, Yb) != 0) return fail("sampled gemm_w4a8 failed");
+    if (orc_gemv(ORC_W4G128, b, rows, k, x, NULL, rows, y, yb) != 0) return fail("w4g128 gemv failed");
+    free(Xf);
+    free(b);
+    free(xq);
+    free(xs);
+  }
+  {
     const float s[8] = {0.10f, 0.14f, 0.11f, 0.18f, 0.08f, 0.16f, 0.13f, 0.09f};
     int8_t codes[8];
     uint16_t S16 = 0;

@@ -8,11 +8,14 @@ or brute force over every admissible code.  No GPU is involved.
 Pages:
   K-quants blog   "GGUF K-quants" (hugo-blog-2v1.pages.dev/2025/gguf-k-quants/)
   Q4_0 chapter    "GGUF 量化内幕 第4章 Q4_0：块量化的起点" (sxkj888.cn)
+  TurboQuant article  the W4A8 page (codechina.net), sections 2.1 and 2.2
 
 The Q4_K form (chapter section 4.6) has no worked example on the pages: its
 pins are a hand-derived block (tests/golden/q4_k_block.txt), brute force over
 every 6-bit and 4-bit code, the error bound its rebuilt range implies, the
-degenerate blocks and numpy's matmul for the products.
+degenerate blocks and numpy's matmul for the products.  The group-128 W4A8
+scheme (TurboQuant article) is pinned the same way, and its product against
+an exact integer-and-rational evaluation.
 """
 import decimal
 import os
@@ -556,9 +559,118 @@ def test_q4_k_degenerate_blocks():
 
 
 # --------------------------------------------------------------------------
+# group-128 W4 weights and 8-bit activations (TurboQuant article 2.1, 2.2)
+# --------------------------------------------------------------------------
+def w4_planes(blocks, rows, k):
+    """(codes rows x k/2, fp16 scale bits rows x k/128) of the planar layout (R28)."""
+    b = np.asarray(blocks, dtype=np.uint8)
+    codes = b[: rows * k // 2].reshape(rows, k // 2)
+    scales = b[rows * k // 2:].copy().view("<u2").reshape(rows, k // 128)
+    return codes, scales
+
+
+def test_w4g128_hand_built_planes():
+    rows, k = 2, 256
+    b = np.zeros(rows * k // 2 + rows * (k // 128) * 2, np.uint8)
+    assert b.size == O.packed_bytes(O.W4G128, rows, k) == 2 * 2 * 66
+    codes = b[:256].reshape(2, 128)
+    codes[0, 0] = 0xF0     # row 0 group 0: weight 0 code 0 (-8), weight 64 code 15 (+7)
+    codes[0, 64 + 5] = 0x9A  # row 0 group 1: weight 128+5 code 10 (+2), weight 128+69 code 9 (+1)
+    codes[1, :] = 0x88     # row 1: all codes 8 (0)
+    codes[1, 127] = 0x08   # row 1 group 1: weight 128+63 code 8, weight 255 code 0 (-8)
+    b[256:264] = np.array([0x3800, 0x2400, 0x3C00, 0xBC00], dtype="<u2").view(np.uint8)  # 0.5, 1/64, 1, -1
+    y = O.dequant(O.W4G128, b, rows, k)
+    assert y[0, 0] == -4.0 and y[0, 64] == 3.5
+    assert y[0, 128 + 5] == 2 / 64 and y[0, 128 + 69] == 1 / 64
+    assert y[0, 1] == -4.0  # byte 1 is 0x00: codes 0 -> -8 * 0.5
+    assert y[1, 191] == 0.0 and y[1, 255] == 8.0  # -1 * -8
+    assert np.count_nonzero(y[1]) == 1
+
+
+def test_brute_force_w4g128_codes():
+    rng = np.random.default_rng(25)
+    w = tiny_blocks(rng, 12, 128).reshape(3, 512)
+    b = O.quantize_w4g128(w)
+    codes, scales = w4_planes(b, 3, 512)
+    for r in range(3):
+        for g in range(4):
+            x = w[r, 128 * g:128 * g + 128]
+            assert scales[r, g] == f16(np.float32(np.abs(x).max()) / np.float32(7.0))
+            d = np.float32(f16val(int(scales[r, g])))
+            byte = codes[r, 64 * g:64 * g + 64].astype(np.int64)
+            n = np.concatenate([byte & 15, byte >> 4])
+            for i in range(128):
+                t = np.float32(0.0) if d == 0 else x[i] / d
+                assert n[i] - 8 == best_code(t, -8, 7), (r, g, i)
+
+
+def test_brute_force_act_i8():
+    rng = np.random.default_rng(26)
+    x = tiny_blocks(rng, 6, 300)
+    x[5] = 0.0
+    xq, s = O.quantize_act_i8(x)
+    for t in range(6):
+        assert s[t] == np.float32(np.abs(x[t]).max()) / np.float32(127.0)
+        for i in range(300):
+            q = np.float32(0.0) if s[t] == 0 else x[t, i] / s[t]
+            assert xq[t, i] == best_code(q, -127, 127), (t, i)
+        if s[t] > 0:
+            assert np.abs(xq[t]).max() == 127  # the largest magnitude takes the top level
+    assert np.all(xq[5] == 0)
+    # 16-bit inputs read exactly as their fp32 values
+    h = x[:5].astype(np.float16)
+    xq16, s16 = O.quantize_act_i8(h)
+    xq32, s32 = O.quantize_act_i8(h.astype(np.float32))
+    assert np.array_equal(xq16, xq32) and np.array_equal(s16, s32)
+
+
+def test_w4a8_product_is_the_exact_rational_sum():
+    # sum over groups of d_g * s_t * (integer dot of codes-8 and xq): exact
+    # rationals, against the oracle's fp64 per-element sums
+    rng = np.random.default_rng(27)
+    m, k, n = 5, 384, 3
+    w = (rng.standard_normal((m, k)) * 0.05).astype(np.float32)
+    x = rng.standard_normal((n, k)).astype(np.float32)
+    b = O.quantize_w4g128(w)
+    xq, s = O.quantize_act_i8(x)
+    Y, B = O.gemm_w4a8(b, m, k, xq, s)
+    codes, scales = w4_planes(b, m, k)
+    for i in range(m):
+        for t in range(n):
+            exact = Fraction(0)
+            for g in range(k // 128):
+                byte = codes[i, 64 * g:64 * g + 64].astype(np.int64)
+                nn = np.concatenate([byte & 15, byte >> 4]) - 8
+                dot = int(np.dot(nn, xq[t, 128 * g:128 * g + 128].astype(np.int64)))
+                exact += Fraction(f16val(int(scales[i, g]))) * dot
+            exact *= Fraction(float(s[t]))
+            assert abs(Fraction(float(Y[t, i])) - exact) <= Fraction(1e-15) * Fraction(float(B[t, i]))
+    W = O.dequant(O.W4G128, b, m, k).astype(np.float64)
+    Xr = s[:, None].astype(np.float64) * xq
+    assert np.allclose(Y, Xr @ W.T, rtol=0, atol=1e-12 * B.max())
+    rows = np.array([4, 0])
+    Y2, _ = O.gemm_w4a8(b, m, k, xq, s, rows=rows)
+    assert np.array_equal(Y2, Y[:, rows])
+
+
+def test_w4g128_idempotent_and_degenerate():
+    rng = np.random.default_rng(28)
+    w = (rng.standard_normal((4, 1024)) * 0.02).astype(np.float32)
+    w[3] = 0.0
+    b = O.quantize_w4g128(w)
+    b2 = O.quantize_w4g128(O.dequant(O.W4G128, b, 4, 1024))
+    assert np.array_equal(b, b2)
+    codes, scales = w4_planes(b, 4, 1024)
+    assert np.all(codes[3] == 0x88) and np.all(scales[3] == 0)
+    y = O.dequant(O.W4G128, b, 4, 1024)
+    d = np.repeat(scales.view(np.float16).astype(np.float64), 128, axis=1)
+    assert np.all(np.abs(w - y) <= d / 2 * (1 + 2.0 ** -22) + 1e-30)
+
+
+# --------------------------------------------------------------------------
 # the fp64 products, against numpy's float64 matmul
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("fmt", [O.Q4_0, O.SB4, O.SB4_AFFINE, O.Q4_K])
+@pytest.mark.parametrize("fmt", [O.Q4_0, O.SB4, O.SB4_AFFINE, O.Q4_K, O.W4G128])
 def test_products_vs_numpy(fmt):
     rng = np.random.default_rng(41 + fmt)
     m, k = 24, 768
