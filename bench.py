@@ -414,6 +414,67 @@ def measure_rows(torch, q, WL, np, dev):
                               frac_mfma_bf16=round(tf / BF16_PEAK_TFLOPS, 4))
             log(f"  {name}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s, {tf:.1f} TFLOP/s")
         del cps
+
+    # group-128 W4 weights with 8-bit activations
+    rows.update(w4a8_rows(torch, q, WL, np, dev))
+    return rows
+
+
+INT8_PEAK_TOPS = 5000.0
+
+
+def w4a8_rows(torch, q, WL, np, dev):
+    rows = {}
+
+    def row(name, ms, nbytes, ops=None):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        r = dict(us=round(ms * 1e3, 3), bytes=nbytes, GBps=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+        msg = f"  {name}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s"
+        if ops:
+            tops = ops / (ms * 1e-3) / 1e12
+            r.update(TOPs=round(tops, 2), frac_mfma_int8=round(tops / INT8_PEAK_TOPS, 4))
+            msg += f", {tops:.1f} TOP/s"
+        rows[name] = r
+        log(msg)
+
+    # weight quantization and one-token product at the decode shape
+    w, x = WL.sb4_decode("up")
+    m, k = w.shape
+    wd = torch.from_numpy(w).to(dev)
+    out = torch.empty(q.packed_bytes(q.W4G128, m, k), dtype=torch.uint8, device=dev)
+    t = Timer(torch, lambda i: q.quantize(wd, q.W4G128, out=out), 1)
+    row(f"quantize_w4g128_{m}x{k}_f32", t.run(20), wd.numel() * 4 + out.numel())
+    b0 = out.clone()
+    del wd, out
+    xd = torch.from_numpy(x).to(dev).view(1, k)
+    xq, xs = q.quantize_act_i8(xd)
+    C = n_copies(b0.numel())
+    cps = [b0] + [b0.clone() for _ in range(C - 1)]
+    y = torch.empty((1, m), dtype=torch.float32, device=dev)
+    t = Timer(torch, lambda i: q.gemm_w4a8(cps[i], m, k, xq, xs, out=y), C)
+    row(f"gemv_w4a8_{m}x{k}_i8", t.run(max(1, 400 // C)), b0.numel() + k + 4 + 4 * m)
+    t = Timer(torch, lambda i: q.quantize_act_i8(xd, out=xq, scale=xs), 1)
+    row(f"quantize_act_i8_1x{k}_f16", t.run(50), k * 2 + k + 4)
+    del cps
+
+    # prefill shape: int8 activations from bf16, then the product
+    w, _ = WL.sb4_prefill("up", 16)
+    m, k = w.shape
+    b0 = q.quantize(torch.from_numpy(w).to(dev), q.W4G128)
+    C = n_copies(b0.numel())
+    cps = [b0] + [b0.clone() for _ in range(C - 1)]
+    for n_tok in (16, 64, 512):
+        _, X = WL.sb4_prefill("up", n_tok)
+        Xd = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16)
+        xq, xs = q.quantize_act_i8(Xd)
+        if n_tok == 512:
+            t = Timer(torch, lambda i: q.quantize_act_i8(Xd, out=xq, scale=xs), 1)
+            row(f"quantize_act_i8_{n_tok}x{k}_bf16", t.run(50), n_tok * k * 3 + 4 * n_tok)
+        Y = torch.empty((n_tok, m), dtype=torch.float32, device=dev)
+        t = Timer(torch, lambda i: q.gemm_w4a8(cps[i], m, k, xq, xs, out=Y), C)
+        row(f"gemm_w4a8_{m}x{k}_n{n_tok}_i8", t.run(max(1, 100 // C)),
+            b0.numel() + n_tok * k + 4 * n_tok + 4 * n_tok * m, ops=2.0 * m * k * n_tok)
+    del cps
     return rows
 
 

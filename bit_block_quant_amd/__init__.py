@@ -9,6 +9,8 @@ fallback.  Build with ``python bit_block_quant_amd/build.py`` (or ``__graft_entr
     y      = qblk.gemv(blocks, qblk.SB4, m, k, x) # x: (k,) f32/f16/bf16 -> (m,) f32
     Y      = qblk.gemm(blocks, qblk.SB4, m, k, X) # X: (n, k) bf16 -> (n, m) f32
     W      = qblk.dequant(blocks, qblk.SB4, m, k, torch.float32)
+    xq, s  = qblk.quantize_act_i8(X)             # W4A8: int8 tokens + fp32 scales
+    Y      = qblk.gemm_w4a8(qblk.quantize(w, qblk.W4G128), m, k, xq, s)
 """
 import ctypes as C
 import os
@@ -18,9 +20,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqblk.so")
 
-Q4_0, SB4, SB4_AFFINE, Q4_K = 0, 1, 2, 3
+Q4_0, SB4, SB4_AFFINE, Q4_K, W4G128 = 0, 1, 2, 3, 4
 F32, F16, BF16 = 0, 1, 2
-FORMATS = {"q4_0": Q4_0, "sb4": SB4, "sb4_affine": SB4_AFFINE, "q4_k": Q4_K}
+FORMATS = {"q4_0": Q4_0, "sb4": SB4, "sb4_affine": SB4_AFFINE, "q4_k": Q4_K, "w4g128": W4G128}
 _DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 
 STATUS = {
@@ -31,8 +33,9 @@ STATUS = {
 # every symbol include/qblk.h declares
 EXPORTS = (
     "qblk_block_bytes", "qblk_block_elems", "qblk_packed_bytes", "qblk_quantize_q4_0",
-    "qblk_quantize_q4_0_ref", "qblk_quantize_sb4", "qblk_quantize_q4_k", "qblk_dequant",
-    "qblk_gemv", "qblk_gemm", "qblk_status_string", "qblk_version",
+    "qblk_quantize_q4_0_ref", "qblk_quantize_sb4", "qblk_quantize_q4_k", "qblk_quantize_w4g128",
+    "qblk_quantize_act_i8", "qblk_dequant", "qblk_gemv", "qblk_gemm", "qblk_gemm_w4a8",
+    "qblk_status_string", "qblk_version",
 )
 
 
@@ -55,11 +58,15 @@ def _load():
     L.qblk_quantize_q4_0_ref.argtypes = [p, i32, i64, i64, p, p]
     L.qblk_quantize_sb4.argtypes = [p, i32, i64, i64, i32, p, p]
     L.qblk_quantize_q4_k.argtypes = [p, i32, i64, i64, p, p]
+    L.qblk_quantize_w4g128.argtypes = [p, i32, i64, i64, p, p]
+    L.qblk_quantize_act_i8.argtypes = [p, i32, i64, i64, p, p, p]
+    L.qblk_gemm_w4a8.argtypes = [p, i64, i64, p, p, i64, p, p]
     L.qblk_dequant.argtypes = [i32, p, i64, i64, p, i32, p]
     L.qblk_gemv.argtypes = [i32, p, i64, i64, p, i32, p, p]
     L.qblk_gemm.argtypes = [i32, p, i64, i64, p, i32, i64, p, p]
     for f in ("qblk_quantize_q4_0", "qblk_quantize_q4_0_ref", "qblk_quantize_sb4", "qblk_quantize_q4_k",
-              "qblk_dequant", "qblk_gemv", "qblk_gemm"):
+              "qblk_quantize_w4g128", "qblk_quantize_act_i8", "qblk_dequant", "qblk_gemv", "qblk_gemm",
+              "qblk_gemm_w4a8"):
         getattr(L, f).restype = i32
     L.qblk_status_string.argtypes, L.qblk_status_string.restype = [i32], C.c_char_p
     L.qblk_version.argtypes, L.qblk_version.restype = [], C.c_char_p
@@ -124,6 +131,9 @@ def quantize(w, fmt, out=None, stream=None, ref=False):
     elif fmt == Q4_K:
         _check(_lib.qblk_quantize_q4_k(_ptr(w), _dtype(w), rows, k, _ptr(out), _stream(stream)),
                "qblk_quantize_q4_k")
+    elif fmt == W4G128:
+        _check(_lib.qblk_quantize_w4g128(_ptr(w), _dtype(w), rows, k, _ptr(out), _stream(stream)),
+               "qblk_quantize_w4g128")
     else:
         _check(_lib.qblk_quantize_sb4(_ptr(w), _dtype(w), rows, k, int(fmt == SB4_AFFINE), _ptr(out),
                                       _stream(stream)), "qblk_quantize_sb4")
@@ -152,4 +162,26 @@ def gemm(blocks, fmt, m, k, X, out=None, stream=None):
         out = torch.empty((n, m), dtype=torch.float32, device=X.device)
     _check(_lib.qblk_gemm(fmt, _ptr(blocks), m, k, _ptr(X), _dtype(X), n, _ptr(out),
                           _stream(stream)), "qblk_gemm")
+    return out
+
+
+def quantize_act_i8(x, out=None, scale=None, stream=None):
+    """8-bit activations: (n, k) f32/f16/bf16 -> (int8 codes (n, k), fp32 scales (n,))."""
+    n, k = x.shape
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.int8, device=x.device)
+    if scale is None:
+        scale = torch.empty(n, dtype=torch.float32, device=x.device)
+    _check(_lib.qblk_quantize_act_i8(_ptr(x), _dtype(x), n, k, _ptr(out), _ptr(scale), _stream(stream)),
+           "qblk_quantize_act_i8")
+    return out, scale
+
+
+def gemm_w4a8(blocks, m, k, xq, scale, out=None, stream=None):
+    """Y (n, m) fp32 = the W4A8 product of QBLK_W4G128 blocks and int8 activations."""
+    n = xq.shape[0]
+    if out is None:
+        out = torch.empty((n, m), dtype=torch.float32, device=xq.device)
+    _check(_lib.qblk_gemm_w4a8(_ptr(blocks), m, k, _ptr(xq), _ptr(scale), n, _ptr(out), _stream(stream)),
+           "qblk_gemm_w4a8")
     return out

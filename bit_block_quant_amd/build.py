@@ -21,7 +21,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqblk.so")
-SOURCES = ["qblk_abi.hip", "qblk_quant.hip", "qblk_gemv.hip", "qblk_gemm.hip"]
+SOURCES = ["qblk_abi.hip", "qblk_quant.hip", "qblk_gemv.hip", "qblk_gemm.hip", "qblk_w4a8.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -13,6 +13,7 @@ constexpr int64_t kMaxBytes = int64_t(1) << 40;
 int elems_of(int fmt) {
   switch (fmt) {
     case QBLK_Q4_0: return 32;
+    case QBLK_W4G128: return 128;
     case QBLK_SB4:
     case QBLK_SB4_AFFINE:
     case QBLK_Q4_K: return 256;
@@ -26,6 +27,7 @@ size_t bytes_of(int fmt) {
     case QBLK_SB4: return 138;
     case QBLK_SB4_AFFINE: return 148;
     case QBLK_Q4_K: return 144;
+    case QBLK_W4G128: return 66;  // 64 code bytes + a 2-byte scale, in two planes
     default: return 0;
   }
 }
@@ -121,6 +123,45 @@ qblk_status_t qblk_quantize_q4_k(const void* w, qblk_dtype_t wt, int64_t rows, i
                                              static_cast<hipStream_t>(stream)));
 }
 
+qblk_status_t qblk_quantize_w4g128(const void* w, qblk_dtype_t wt, int64_t rows, int64_t k,
+                                   void* blocks, qblk_stream_t stream) {
+  QBLK_TRY(check_shape(QBLK_W4G128, rows, k));
+  if (!dtype_ok(wt)) return QBLK_ERR_DTYPE;
+  const bool work = rows > 0 && k > 0;
+  QBLK_TRY(check_ptr(w, work));
+  QBLK_TRY(check_ptr(blocks, work));
+  if (!work) return QBLK_OK;
+  return from_hip(qblk::launch_quantize_w4g128(w, wt, rows, k, blocks,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+qblk_status_t qblk_quantize_act_i8(const void* x, qblk_dtype_t xt, int64_t n, int64_t k,
+                                   int8_t* xq, float* scale, qblk_stream_t stream) {
+  if (n < 0 || k < 0 || n > kMaxDim || k > kMaxDim || k % 8 != 0) return QBLK_ERR_SHAPE;
+  if (!dtype_ok(xt)) return QBLK_ERR_DTYPE;
+  QBLK_TRY(check_ptr(x, n > 0 && k > 0));
+  QBLK_TRY(check_ptr(xq, n > 0 && k > 0));
+  QBLK_TRY(check_ptr(scale, n > 0));
+  if (n == 0) return QBLK_OK;
+  return from_hip(qblk::launch_quantize_act_i8(x, xt, n, k, xq, scale,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+qblk_status_t qblk_gemm_w4a8(const void* blocks, int64_t m, int64_t k, const int8_t* xq,
+                             const float* scale, int64_t n, float* y, qblk_stream_t stream) {
+  QBLK_TRY(check_shape(QBLK_W4G128, m, k));
+  if (n < 0 || n > kMaxDim) return QBLK_ERR_SHAPE;
+  const bool out = m > 0 && n > 0;
+  QBLK_TRY(check_ptr(blocks, out && k > 0));
+  QBLK_TRY(check_ptr(xq, out && k > 0));
+  QBLK_TRY(check_ptr(scale, out && k > 0));
+  QBLK_TRY(check_ptr(y, out));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!out) return QBLK_OK;
+  if (k == 0) return from_hip(qblk::launch_fill_zero(y, m * n, s));
+  return from_hip(qblk::launch_gemm_w4a8(blocks, m, k, xq, scale, n, y, s));
+}
+
 qblk_status_t qblk_dequant(qblk_format_t fmt, const void* blocks, int64_t rows, int64_t k,
                            void* out, qblk_dtype_t ot, qblk_stream_t stream) {
   QBLK_TRY(check_shape(fmt, rows, k));
@@ -137,6 +178,7 @@ qblk_status_t qblk_gemv(qblk_format_t fmt, const void* blocks, int64_t m, int64_
                         const void* x, qblk_dtype_t xt, float* y, qblk_stream_t stream) {
   QBLK_TRY(check_shape(fmt, m, k));
   if (!dtype_ok(xt)) return QBLK_ERR_DTYPE;
+  if (fmt == QBLK_W4G128) return QBLK_ERR_UNSUPPORTED;  // its product is qblk_gemm_w4a8
   QBLK_TRY(check_ptr(blocks, m > 0 && k > 0));
   QBLK_TRY(check_ptr(x, m > 0 && k > 0));
   QBLK_TRY(check_ptr(y, m > 0));
@@ -153,7 +195,7 @@ qblk_status_t qblk_gemm(qblk_format_t fmt, const void* blocks, int64_t m, int64_
   if (!dtype_ok(xt)) return QBLK_ERR_DTYPE;
   if (n < 0 || n > kMaxDim) return QBLK_ERR_SHAPE;
   // the matrix-core kernels take bf16 activations and whole 256-weight groups
-  if (xt != QBLK_BF16 || k % 256 != 0) return QBLK_ERR_UNSUPPORTED;
+  if (xt != QBLK_BF16 || k % 256 != 0 || fmt == QBLK_W4G128) return QBLK_ERR_UNSUPPORTED;
   const bool out = m > 0 && n > 0;
   QBLK_TRY(check_ptr(blocks, out && k > 0));
   QBLK_TRY(check_ptr(x, out && k > 0));

@@ -610,6 +610,94 @@ __global__ __launch_bounds__(kThreads) void k_quant_q4k_g(const void* __restrict
   lds_to_global(stage, out + sb0 * B, static_cast<int>(ns * B));
 }
 
+// ------------------------------------------- group-128 W4 and int8 activations
+// TurboQuant article, sections 2.1-2.2: per row, groups of 128 weights with
+// one symmetric scale from their own maximum, 4-bit codes; 8-bit activations.
+// Weight layout (planar): the code plane (byte j of group G holds weight
+// 128G+j in its low nibble and 128G+64+j in its high nibble, codes stored +8)
+// followed by the fp16 scale plane, one entry per group.  The flat group
+// index G = row * k/128 + g addresses both planes.  A workgroup takes 16
+// groups, 16 threads per group with 8 weights each: thread u < 8 holds
+// weights 8u..8u+7 (low nibbles of bytes 8u..8u+7), thread u + 8 the weights
+// 64 further (their high nibbles).
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_quant_w4g128(const void* __restrict__ w,
+                                                           uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scales,
+                                                           int64_t ngroups) {
+  const int t = threadIdx.x;
+  const int64_t G = static_cast<int64_t>(blockIdx.x) * (kThreads / 16) + (t >> 4);
+  const int u = t & 15;
+  const bool valid = G < ngroups;
+  float v[8];
+  load8<DT>(w, G * 128 + u * 8, valid, v);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+  amax = group_max<16>(amax);
+  const uint16_t d16 = f32_to_f16_bits(amax / 7.0f);
+  int n[8];
+  codes8(v, f16_bits_to_f32(d16), -8.0f, 7.0f, n);
+  const uint32_t a0 = (n[0] + 8) | ((n[1] + 8) << 8) | ((n[2] + 8) << 16) | ((n[3] + 8) << 24);
+  const uint32_t a1 = (n[4] + 8) | ((n[5] + 8) << 8) | ((n[6] + 8) << 16) | ((n[7] + 8) << 24);
+  const uint32_t b0 = __shfl_xor(a0, 8, kWave), b1 = __shfl_xor(a1, 8, kWave);
+  if (valid && u < 8) *reinterpret_cast<uint2*>(codes + G * 64 + 8 * u) = make_uint2(a0 | (b0 << 4), a1 | (b1 << 4));
+  if (valid && u == 0) *reinterpret_cast<uint16_t*>(scales + 2 * G) = d16;
+}
+
+template <int OT>
+__global__ __launch_bounds__(kThreads) void k_dequant_w4g128(const uint8_t* __restrict__ codes,
+                                                             const uint8_t* __restrict__ scales,
+                                                             void* __restrict__ out, int64_t ngroups) {
+  const int t = threadIdx.x;
+  const int64_t G = static_cast<int64_t>(blockIdx.x) * (kThreads / 16) + (t >> 4);
+  const int u = t & 15;
+  if (G >= ngroups) return;
+  const float d = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(scales + 2 * G));
+  const uint2 c = *reinterpret_cast<const uint2*>(codes + G * 64 + 8 * (u & 7));
+  const int sh = (u >> 3) * 4;  // high nibbles for the upper 64 weights
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    y[i] = d * static_cast<float>(static_cast<int>((c.x >> (8 * i + sh)) & 15u) - 8);
+    y[4 + i] = d * static_cast<float>(static_cast<int>((c.y >> (8 * i + sh)) & 15u) - 8);
+  }
+  store8<OT>(out, G * 128 + 8 * u, y);
+}
+
+// One workgroup per token (row of X): the row's largest magnitude, then
+// codes clamp(round_half_away(x / s), -127, 127) with s = max/127 (fp32).
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_quant_act_i8(const void* __restrict__ x,
+                                                           int8_t* __restrict__ xq,
+                                                           float* __restrict__ scale, int64_t k) {
+  __shared__ float red[kThreads / kWave];
+  const int64_t row = blockIdx.x;
+  float amax = 0.0f;
+  for (int64_t i = threadIdx.x * 8; i < k; i += kThreads * 8) {
+    float v[8];
+    load8<DT>(x, row * k + i, true, v);
+#pragma unroll
+    for (int j = 0; j < 8; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, m, kWave));
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = amax;
+  __syncthreads();
+  amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+  const float s = amax / 127.0f;
+  if (threadIdx.x == 0) scale[row] = s;
+  for (int64_t i = threadIdx.x * 8; i < k; i += kThreads * 8) {
+    float v[8];
+    load8<DT>(x, row * k + i, true, v);
+    int n[8];
+    codes8(v, s, -127.0f, 127.0f, n);
+    const uint32_t a0 = (n[0] & 0xff) | ((n[1] & 0xff) << 8) | ((n[2] & 0xff) << 16) | (static_cast<uint32_t>(n[3]) << 24);
+    const uint32_t a1 = (n[4] & 0xff) | ((n[5] & 0xff) << 8) | ((n[6] & 0xff) << 16) | (static_cast<uint32_t>(n[7]) << 24);
+    *reinterpret_cast<uint2*>(xq + row * k + i) = make_uint2(a0, a1);
+  }
+}
+
 // ------------------------------------------------------------- dequantize
 // 4-bit code of weight i (0..7 of this thread's 8) from the staged qs bytes of
 // a 32-weight group: threads u = 0,1 take low nibbles of bytes 8u..8u+7,
@@ -730,6 +818,27 @@ hipError_t launch_quantize_sb4(const void* w, int wt, int64_t rows, int64_t k, i
   return hipGetLastError();
 }
 
+hipError_t launch_quantize_w4g128(const void* w, int wt, int64_t rows, int64_t k, void* blocks,
+                                  hipStream_t s) {
+  const int64_t ng = rows * k / 128;
+  uint8_t* codes = static_cast<uint8_t*>(blocks);
+  uint8_t* scales = codes + rows * k / 2;
+  const unsigned g = static_cast<unsigned>((ng + kThreads / 16 - 1) / (kThreads / 16));
+  if (wt == QBLK_F32) hipLaunchKernelGGL(k_quant_w4g128<QBLK_F32>, dim3(g), dim3(kThreads), 0, s, w, codes, scales, ng);
+  else if (wt == QBLK_F16) hipLaunchKernelGGL(k_quant_w4g128<QBLK_F16>, dim3(g), dim3(kThreads), 0, s, w, codes, scales, ng);
+  else hipLaunchKernelGGL(k_quant_w4g128<QBLK_BF16>, dim3(g), dim3(kThreads), 0, s, w, codes, scales, ng);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_act_i8(const void* x, int xt, int64_t n, int64_t k, int8_t* xq, float* scale,
+                                  hipStream_t s) {
+  const dim3 g(static_cast<unsigned>(n));
+  if (xt == QBLK_F32) hipLaunchKernelGGL(k_quant_act_i8<QBLK_F32>, g, dim3(kThreads), 0, s, x, xq, scale, k);
+  else if (xt == QBLK_F16) hipLaunchKernelGGL(k_quant_act_i8<QBLK_F16>, g, dim3(kThreads), 0, s, x, xq, scale, k);
+  else hipLaunchKernelGGL(k_quant_act_i8<QBLK_BF16>, g, dim3(kThreads), 0, s, x, xq, scale, k);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_q4_k(const void* w, int wt, int64_t rows, int64_t k, void* blocks,
                                 hipStream_t s) {
   const int64_t nsb = rows * k / 256;
@@ -755,6 +864,15 @@ static void launch_deq_t(const uint8_t* b, int64_t nblk, void* out, int ot, unsi
 hipError_t launch_dequant(int fmt, const void* blocks, int64_t rows, int64_t k, void* out, int ot,
                           hipStream_t s) {
   const uint8_t* b = static_cast<const uint8_t*>(blocks);
+  if (fmt == QBLK_W4G128) {
+    const int64_t ng = rows * k / 128;
+    const uint8_t* sc = b + rows * k / 2;
+    const unsigned g = static_cast<unsigned>((ng + kThreads / 16 - 1) / (kThreads / 16));
+    if (ot == QBLK_F32) hipLaunchKernelGGL(k_dequant_w4g128<QBLK_F32>, dim3(g), dim3(kThreads), 0, s, b, sc, out, ng);
+    else if (ot == QBLK_F16) hipLaunchKernelGGL(k_dequant_w4g128<QBLK_F16>, dim3(g), dim3(kThreads), 0, s, b, sc, out, ng);
+    else hipLaunchKernelGGL(k_dequant_w4g128<QBLK_BF16>, dim3(g), dim3(kThreads), 0, s, b, sc, out, ng);
+    return hipGetLastError();
+  }
   const unsigned g = grid_for(rows * k);
   if (fmt == QBLK_Q4_0) launch_deq_t<QBLK_Q4_0>(b, rows * k / 32, out, ot, g, s);
   else if (fmt == QBLK_SB4) launch_deq_t<QBLK_SB4>(b, rows * k / 256, out, ot, g, s);

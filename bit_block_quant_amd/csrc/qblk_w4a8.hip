@@ -1,0 +1,404 @@
+// qblk_w4a8.hip -- products of group-128 4-bit weights with 8-bit activations
+// on gfx950 (the W4A8 scheme of the TurboQuant article, sections 2.1-2.2).
+//
+// What is computed: Y[t,i] = s_t * sum_g d[i,g] * sum_{k in g} (code-8) * xq[t,k]
+// -- the product of the rebuilt weights d*(code-8) and the rebuilt activations
+// s_t*xq.  The inner sums are integers, formed exactly in int32 (v_dot4_i32_i8
+// for one token, int8 matrix ops for several); each group's sum is then
+// scaled by its fp16 weight scale in fp32, and the token scale is applied
+// once at the end.  The codes enter the integer products as they are stored
+// (0..15); the -8 offset is the integer -8 * sum(xq) over the same k range,
+// formed once per token and k range and used as the starting value.
+//
+// Weight layout (planar): the code plane, k/2 bytes per row, byte j of group
+// g holding weight 128g+j (low nibble) and 128g+64+j (high nibble), then the
+// fp16 scale plane, k/128 entries per row.
+#include "qblk_device.h"
+#include "qblk_launch.h"
+
+namespace qblk {
+namespace {
+
+constexpr uint32_t kLo4 = 0x0F0F0F0Fu;
+constexpr uint32_t kOnes8 = 0x01010101u;
+
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+  return __builtin_amdgcn_sdot4(static_cast<int>(a), static_cast<int>(b), c, false);
+}
+
+int cu_count_w4() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
+// ===================================================================
+// One token: every load of a wave issued up front.
+//
+// The rows are split evenly over 16-wave workgroups (one per CU); wave w takes
+// rows w, w+16, w+32 of its slice.  A code row is a run of 16-byte chunks of
+// 32 weights; lane l takes chunks l, l+64, ... (UPL of them), so it sees the
+// same activations in every row: chunk c (group c/4, quarter c%4) pairs its
+// low nibbles with xq[128g+16q .. +16] and its high nibbles with the 16 bytes
+// 64 further on.  Per chunk: 8 v_dot4 and 8 masks; per (chunk, row) one fp32
+// multiply-add with the group's scale (four lanes share a group).
+// ===================================================================
+constexpr int kWavesV = 16;
+
+template <int RMAX, int UPL>
+__global__ __launch_bounds__(kWavesV * kWave) void k_gemv_w4a8(const uint8_t* __restrict__ codes,
+                                                              const uint16_t* __restrict__ scales,
+                                                              const int8_t* __restrict__ xq,
+                                                              const float* __restrict__ xs,
+                                                              float* __restrict__ y, int M, int K,
+                                                              int rows_per_wg) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int row0 = blockIdx.x * rows_per_wg;
+  const int row_end = min(M, row0 + rows_per_wg);
+  if (row0 + wave >= row_end) return;
+  const int C = K >> 5;   // chunks per row
+  const int NG = K >> 7;  // groups per row
+  const int64_t rowbytes = K >> 1;
+
+  // (1) the lane's activations, issued first
+  uint4 xl[UPL], xh[UPL];
+  int cc[UPL];
+  bool live[UPL];
+#pragma unroll
+  for (int i = 0; i < UPL; i++) {
+    const int c = lane + 64 * i;
+    live[i] = c < C;
+    cc[i] = min(c, C - 1);
+    const int8_t* p = xq + 128 * (cc[i] >> 2) + 16 * (cc[i] & 3);
+    xl[i] = *reinterpret_cast<const uint4*>(p);
+    xh[i] = *reinterpret_cast<const uint4*>(p + 64);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // (2) codes and scales of every (chunk, row), chunk-major
+  uint4 cw[RMAX][UPL];
+  uint32_t sc[RMAX][UPL];
+#pragma unroll
+  for (int i = 0; i < UPL; i++) {
+#pragma unroll
+    for (int r = 0; r < RMAX; r++) {
+      const int row = min(row0 + wave + kWavesV * r, row_end - 1);
+      cw[r][i] = *reinterpret_cast<const uint4*>(codes + row * rowbytes + 16 * cc[i]);
+      sc[r][i] = scales[static_cast<int64_t>(row) * NG + (cc[i] >> 2)];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // nothing may touch the activations before the weight loads are issued
+#pragma unroll
+  for (int i = 0; i < UPL; i++)
+    asm volatile("" : "+v"(xl[i].x), "+v"(xl[i].y), "+v"(xl[i].z), "+v"(xl[i].w), "+v"(xh[i].x), "+v"(xh[i].y),
+                 "+v"(xh[i].z), "+v"(xh[i].w)::"memory");
+
+  // (3) -8 * sum(xq) over each chunk's 32 activations
+  int corr[UPL];
+#pragma unroll
+  for (int i = 0; i < UPL; i++) {
+    int s = dot4(xl[i].x, kOnes8, 0);
+    s = dot4(xl[i].y, kOnes8, s);
+    s = dot4(xl[i].z, kOnes8, s);
+    s = dot4(xl[i].w, kOnes8, s);
+    s = dot4(xh[i].x, kOnes8, s);
+    s = dot4(xh[i].y, kOnes8, s);
+    s = dot4(xh[i].z, kOnes8, s);
+    s = dot4(xh[i].w, kOnes8, s);
+    corr[i] = -8 * s;
+  }
+
+  // (4) products
+  float acc[RMAX];
+#pragma unroll
+  for (int r = 0; r < RMAX; r++) acc[r] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < UPL; i++) {
+#pragma unroll
+    for (int r = 0; r < RMAX; r++) {
+      const uint4 c = cw[r][i];
+      int a = corr[i];
+      a = dot4(c.x & kLo4, xl[i].x, a);
+      a = dot4((c.x >> 4) & kLo4, xh[i].x, a);
+      a = dot4(c.y & kLo4, xl[i].y, a);
+      a = dot4((c.y >> 4) & kLo4, xh[i].y, a);
+      a = dot4(c.z & kLo4, xl[i].z, a);
+      a = dot4((c.z >> 4) & kLo4, xh[i].z, a);
+      a = dot4(c.w & kLo4, xl[i].w, a);
+      a = dot4((c.w >> 4) & kLo4, xh[i].w, a);
+      const float d = live[i] ? f16_bits_to_f32(sc[r][i]) : 0.0f;
+      acc[r] = __builtin_fmaf(d, static_cast<float>(a), acc[r]);
+    }
+  }
+  const float st = xs[0];
+#pragma unroll
+  for (int r = 0; r < RMAX; r++) {
+    const float v = wave_sum_dpp(acc[r]);
+    const int row = row0 + wave + kWavesV * r;
+    if (lane == kWave - 1 && row < row_end) y[row] = v * st;
+  }
+}
+
+// ===================================================================
+// Several tokens: v_mfma_i32_16x16x64_i8.
+//
+// Operand layout: lane l holds row (l % 16) of A and column (l % 16) of B,
+// each with 16 int8 k values of its lane group (l / 16); lane l receives
+// D[4*(l/16) + r][l % 16], r = 0..3.  Only A and B sharing the k assignment
+// matters: for step s (0, 1) of a 128-weight group, lane group g takes code
+// bytes j0..j0+7, j0 = 8*(4s + g): weights j0..j0+7 (low nibbles) and
+// 64+j0..64+j0+7 (high nibbles), and the same 16 activations.  A = X (tokens),
+// B = W^T (weight rows), so a lane's four outputs share one weight row and
+// one scale per group.  The integer accumulator of a group starts at
+// -8 * sum(xq) of its token over the group (staged with X).
+//
+// A workgroup of 4 waves owns 64*TM weight rows (16*TM per wave) and 16*TN
+// tokens.  X is staged one group (128 k) at a time in LDS, double-buffered:
+// token row = 8 pieces of 16 bytes in operand order (piece 4s+g = the 16
+// activations above), rows 144 bytes apart so 8 lanes reading one piece of 8
+// consecutive tokens hit distinct banks.  When the M x N tiling leaves too
+// few workgroups, the groups are split over a third grid dimension and the
+// partial products are added into Y (zeroed first).
+// ===================================================================
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kThreadsM = 256;
+constexpr int kXRow = 144;  // bytes per staged token row
+
+template <int TM, int TN, bool SPLIT>
+__global__ __launch_bounds__(kThreadsM) void k_gemm_w4a8(const uint8_t* __restrict__ codes,
+                                                         const uint16_t* __restrict__ scales,
+                                                         const int8_t* __restrict__ xq,
+                                                         const float* __restrict__ xs,
+                                                         float* __restrict__ Y, int M, int K, int N,
+                                                         int groups_per_split) {
+  constexpr int NT = 16 * TN;
+  constexpr int XCH = NT * 8;                                  // 16-byte X chunks per stage
+  constexpr int XPT = (XCH + kThreadsM - 1) / kThreadsM;       // per thread
+  __shared__ uint4 xs4[2][NT * kXRow / 16];
+  __shared__ i32x4_t xcor4[2][NT / 4];                         // -8 * sum(xq) per token
+  int* const xcor0 = reinterpret_cast<int*>(xcor4[0]);
+  int* const xcor1 = reinterpret_cast<int*>(xcor4[1]);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int NG = K >> 7;
+  const int64_t rowbytes = K >> 1;
+  const int64_t mw = static_cast<int64_t>(blockIdx.x) * 64 * TM + wave * 16 * TM;
+  const int n0 = blockIdx.y * NT;
+  const int g_begin = SPLIT ? blockIdx.z * groups_per_split : 0;
+  const int g_end = SPLIT ? min(NG, g_begin + groups_per_split) : NG;
+  int64_t rowi[TM];
+#pragma unroll
+  for (int tm = 0; tm < TM; tm++) {
+    const int64_t m = mw + 16 * tm + l16;
+    rowi[tm] = m < M ? m : M - 1;
+  }
+
+  auto load_x = [&](int G, uint4 xv[XPT]) {
+#pragma unroll
+    for (int i = 0; i < XPT; i++) {
+      const int c = threadIdx.x + i * kThreadsM;
+      const int tok = c >> 3, cc = c & 7;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (c < XCH && n0 + tok < N)
+        v = *reinterpret_cast<const uint4*>(xq + static_cast<int64_t>(n0 + tok) * K + 128 * G + 16 * cc);
+      xv[i] = v;
+    }
+  };
+  auto store_x = [&](int buf, const uint4 xv[XPT]) {
+    uint8_t* xsb = reinterpret_cast<uint8_t*>(xs4[buf]);
+#pragma unroll
+    for (int i = 0; i < XPT; i++) {
+      const int c = threadIdx.x + i * kThreadsM;
+      const int tok = c >> 3, cc = c & 7;
+      // activations 16cc..16cc+15 of the group: pieces 2(cc&3) and 2(cc&3)+1,
+      // first halves (cc < 4) or second halves (cc >= 4)
+      if (c < XCH) {
+        uint8_t* row = xsb + tok * kXRow + 32 * (cc & 3) + 8 * (cc >> 2);
+        *reinterpret_cast<uint2*>(row) = make_uint2(xv[i].x, xv[i].y);
+        *reinterpret_cast<uint2*>(row + 16) = make_uint2(xv[i].z, xv[i].w);
+      }
+      int s = dot4(xv[i].x, kOnes8, 0);
+      s = dot4(xv[i].y, kOnes8, s);
+      s = dot4(xv[i].z, kOnes8, s);
+      s = dot4(xv[i].w, kOnes8, s);
+      // the 8 chunks of a token sit on 8 adjacent lanes
+      s += __shfl_xor(s, 1, kWave);
+      s += __shfl_xor(s, 2, kWave);
+      s += __shfl_xor(s, 4, kWave);
+      if (c < XCH && cc == 0) (buf ? xcor1 : xcor0)[tok] = -8 * s;
+    }
+  };
+  auto load_w = [&](int G, uint2 cw[TM][2], uint32_t sc[TM]) {
+#pragma unroll
+    for (int tm = 0; tm < TM; tm++) {
+      const uint8_t* p = codes + rowi[tm] * rowbytes + 64 * G + 8 * g;
+      cw[tm][0] = *reinterpret_cast<const uint2*>(p);
+      cw[tm][1] = *reinterpret_cast<const uint2*>(p + 32);
+      sc[tm] = scales[rowi[tm] * NG + G];
+    }
+  };
+
+  float4_t acc[TM][TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; tm++)
+#pragma unroll
+    for (int tn = 0; tn < TN; tn++) acc[tm][tn] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  uint4 xv[XPT];
+  uint2 cw[TM][2];
+  uint32_t sc[TM];
+  i32x4_t Bop[TM][2];
+  float dsc[TM];
+  auto decode = [&]() {
+#pragma unroll
+    for (int tm = 0; tm < TM; tm++) {
+#pragma unroll
+      for (int s = 0; s < 2; s++) {
+        const uint2 c = cw[tm][s];
+        Bop[tm][s] = i32x4_t{static_cast<int>(c.x & kLo4), static_cast<int>(c.y & kLo4),
+                             static_cast<int>((c.x >> 4) & kLo4), static_cast<int>((c.y >> 4) & kLo4)};
+      }
+      dsc[tm] = f16_bits_to_f32(sc[tm]);
+    }
+  };
+  if (g_begin < g_end) {
+    load_x(g_begin, xv);
+    load_w(g_begin, cw, sc);
+    store_x(0, xv);
+    decode();
+  }
+
+  for (int G = g_begin; G < g_end; G++) {
+    const int buf = (G - g_begin) & 1;
+    __syncthreads();
+    const bool more = G + 1 < g_end;
+    if (more) {
+      load_x(G + 1, xv);
+      load_w(G + 1, cw, sc);
+    }
+    const uint8_t* xsb = reinterpret_cast<const uint8_t*>(xs4[buf]);
+#pragma unroll
+    for (int tn = 0; tn < TN; tn++) {
+      const i32x4_t A0 = *reinterpret_cast<const i32x4_t*>(xsb + (16 * tn + l16) * kXRow + 16 * g);
+      const i32x4_t A1 = *reinterpret_cast<const i32x4_t*>(xsb + (16 * tn + l16) * kXRow + 16 * (4 + g));
+      const i32x4_t C0 = xcor4[buf][4 * tn + g];  // tokens 16tn + 4g .. +3
+#pragma unroll
+      for (int tm = 0; tm < TM; tm++) {
+        i32x4_t D = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, Bop[tm][0], C0, 0, 0, 0);
+        D = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, Bop[tm][1], D, 0, 0, 0);
+        float4_t& a = acc[tm][tn];
+        a.x = __builtin_fmaf(dsc[tm], static_cast<float>(D.x), a.x);
+        a.y = __builtin_fmaf(dsc[tm], static_cast<float>(D.y), a.y);
+        a.z = __builtin_fmaf(dsc[tm], static_cast<float>(D.z), a.z);
+        a.w = __builtin_fmaf(dsc[tm], static_cast<float>(D.w), a.w);
+      }
+    }
+    if (more) {
+      store_x(buf ^ 1, xv);
+      decode();
+    }
+  }
+
+#pragma unroll
+  for (int tn = 0; tn < TN; tn++) {
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int n = n0 + 16 * tn + 4 * g + r;
+      if (n >= N) continue;
+      const float st = xs[n];
+#pragma unroll
+      for (int tm = 0; tm < TM; tm++) {
+        const int64_t m = mw + 16 * tm + l16;
+        if (m >= M) continue;
+        const float v = (r == 0 ? acc[tm][tn].x : r == 1 ? acc[tm][tn].y : r == 2 ? acc[tm][tn].z : acc[tm][tn].w) * st;
+        float* dst = Y + static_cast<int64_t>(n) * M + m;
+        if constexpr (SPLIT) atomicAdd(dst, v);
+        else *dst = v;
+      }
+    }
+  }
+}
+
+template <int RMAX, int UPL>
+hipError_t launch_v_t(const uint8_t* codes, const uint16_t* scales, int64_t m, int64_t k, const int8_t* xq,
+                      const float* xs, float* y, int rpw, hipStream_t s) {
+  const unsigned grid = static_cast<unsigned>((m + rpw - 1) / rpw);
+  hipLaunchKernelGGL((k_gemv_w4a8<RMAX, UPL>), dim3(grid), dim3(kWavesV * kWave), 0, s, codes, scales, xq, xs, y,
+                     static_cast<int>(m), static_cast<int>(k), rpw);
+  return hipGetLastError();
+}
+
+// chunks per lane (UPL) from k, then rows per wave (RMAX) from the rows per
+// workgroup, capped so that a lane's loads fit its 128 registers (16 waves of
+// a workgroup share a SIMD four at a time): RMAX * UPL <= 15, RMAX <= 3.
+template <int UPL>
+hipError_t launch_v_u(const uint8_t* codes, const uint16_t* scales, int64_t m, int64_t k, const int8_t* xq,
+                      const float* xs, float* y, hipStream_t s) {
+  constexpr int kRcap = UPL <= 5 ? 3 : (UPL == 6 ? 2 : 1);
+  int64_t per = (m + cu_count_w4() - 1) / cu_count_w4();  // an even share of the rows over the CUs
+  per = per < kWavesV ? kWavesV : (per > kRcap * kWavesV ? kRcap * kWavesV : per);
+  const int rpw = static_cast<int>(per);
+  const int rmax = (rpw + kWavesV - 1) / kWavesV;
+  if (rmax == 1 || kRcap == 1) return launch_v_t<1, UPL>(codes, scales, m, k, xq, xs, y, rpw, s);
+  if (rmax == 2 || kRcap == 2) return launch_v_t<(kRcap >= 2 ? 2 : 1), UPL>(codes, scales, m, k, xq, xs, y, rpw, s);
+  return launch_v_t<(kRcap >= 3 ? 3 : 1), UPL>(codes, scales, m, k, xq, xs, y, rpw, s);
+}
+
+hipError_t launch_v(const uint8_t* codes, const uint16_t* scales, int64_t m, int64_t k, const int8_t* xq,
+                    const float* xs, float* y, hipStream_t s) {
+  switch (static_cast<int>((k / 32 + 63) / 64)) {
+    case 1: return launch_v_u<1>(codes, scales, m, k, xq, xs, y, s);
+    case 2: return launch_v_u<2>(codes, scales, m, k, xq, xs, y, s);
+    case 3: return launch_v_u<3>(codes, scales, m, k, xq, xs, y, s);
+    case 4: return launch_v_u<4>(codes, scales, m, k, xq, xs, y, s);
+    case 5: return launch_v_u<5>(codes, scales, m, k, xq, xs, y, s);
+    case 6: return launch_v_u<6>(codes, scales, m, k, xq, xs, y, s);
+    case 7: return launch_v_u<7>(codes, scales, m, k, xq, xs, y, s);
+    default: return launch_v_u<8>(codes, scales, m, k, xq, xs, y, s);
+  }
+}
+
+template <int TM, int TN>
+hipError_t launch_m(const uint8_t* codes, const uint16_t* scales, int64_t m, int64_t k, const int8_t* xq,
+                    const float* xs, int64_t n, float* y, hipStream_t s) {
+  const unsigned gx = static_cast<unsigned>((m + 64 * TM - 1) / (64 * TM));
+  const unsigned gy = static_cast<unsigned>((n + 16 * TN - 1) / (16 * TN));
+  const int ng = static_cast<int>(k / 128);
+  const int64_t tiles = static_cast<int64_t>(gx) * gy;
+  const int64_t want = 2 * static_cast<int64_t>(cu_count_w4());
+  if (tiles < want && ng > 1) {
+    int split = static_cast<int>((want + tiles - 1) / tiles);
+    split = split > ng ? ng : split;
+    const int per = (ng + split - 1) / split;
+    const unsigned gz = static_cast<unsigned>((ng + per - 1) / per);
+    const hipError_t e = launch_fill_zero(y, m * n, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_gemm_w4a8<TM, TN, true>), dim3(gx, gy, gz), dim3(kThreadsM), 0, s, codes, scales, xq, xs,
+                       y, static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), per);
+  } else {
+    hipLaunchKernelGGL((k_gemm_w4a8<TM, TN, false>), dim3(gx, gy, 1), dim3(kThreadsM), 0, s, codes, scales, xq, xs,
+                       y, static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), ng);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_w4a8(const void* blocks, int64_t m, int64_t k, const int8_t* xq, const float* xs,
+                            int64_t n, float* y, hipStream_t s) {
+  const uint8_t* codes = static_cast<const uint8_t*>(blocks);
+  const uint16_t* scales = reinterpret_cast<const uint16_t*>(codes + m * k / 2);
+  if (n == 1 && k <= 8 * 64 * 32) return launch_v(codes, scales, m, k, xq, xs, y, s);
+  if (n <= 16) return launch_m<1, 1>(codes, scales, m, k, xq, xs, n, y, s);
+  if (n <= 64) return launch_m<2, 4>(codes, scales, m, k, xq, xs, n, y, s);
+  return launch_m<4, 4>(codes, scales, m, k, xq, xs, n, y, s);
+}
+
+}  // namespace qblk

@@ -43,8 +43,21 @@
  *                    packing without describing it: the field order is this
  *                    library's.)
  *
+ *   QBLK_W4G128      groups of 128 weights along a row, one fp16 scale each
+ *                    (66 bytes per group, 4.125 bit/weight), stored as two
+ *                    planes: first the codes, k/2 bytes per row (byte j of
+ *                    group g holds weight 128g+j in its low nibble and weight
+ *                    128g+64+j in its high nibble, codes stored +8), then the
+ *                    scales, k/128 fp16 values per row.  Symmetric: scale
+ *                    d = absmax/7, a weight is d * (code - 8).  Products take
+ *                    8-bit activations (qblk_quantize_act_i8, qblk_gemm_w4a8).
+ *                    (TurboQuant W4A8 article (codechina.net), sections 2.1
+ *                    and 2.2; the layout is this library's, the page gives
+ *                    none.)
+ *
  * Matrices are dense row-major.  A packed matrix of rows x k weights stores row
- * r, block b at byte (r * k/E + b) * B, with E weights and B bytes per block.
+ * r, block b at byte (r * k/E + b) * B, with E weights and B bytes per block
+ * (QBLK_W4G128: the two planes above, rows * k/E * B bytes in all).
  *
  * Quantization rule (the same for all formats; both the codes and the INT8
  * or 6-bit scales are computed against the scale the block STORES, decoded
@@ -86,7 +99,8 @@ typedef enum {
   QBLK_Q4_0 = 0,       /* 32 weights, 18 bytes  */
   QBLK_SB4 = 1,        /* 256 weights, 138 bytes */
   QBLK_SB4_AFFINE = 2, /* 256 weights, 148 bytes */
-  QBLK_Q4_K = 3        /* 256 weights, 144 bytes */
+  QBLK_Q4_K = 3,       /* 256 weights, 144 bytes */
+  QBLK_W4G128 = 4      /* 128 weights, 66 bytes (two planes) */
 } qblk_format_t;
 
 typedef enum {
@@ -138,6 +152,37 @@ qblk_status_t qblk_quantize_sb4(const void* w, qblk_dtype_t wt, int64_t rows,
  * rebuilt (exact fp32) d*s_j and dmin*m_j. */
 qblk_status_t qblk_quantize_q4_k(const void* w, qblk_dtype_t wt, int64_t rows,
                                  int64_t k, void* blocks, qblk_stream_t stream);
+
+/* Quantize w (element type F32, F16 or BF16, k a multiple of 128) into
+ * QBLK_W4G128 groups: per row, each group of 128 weights takes the scale
+ * d = fp16(max|w| / 7) and codes clamp(round_half_away(w / d), -8, 7) + 8
+ * against the stored d (TurboQuant article, section 2.1: per-row symmetric
+ * groups of 128, scale from the group's own maximum, 4-bit integers). */
+qblk_status_t qblk_quantize_w4g128(const void* w, qblk_dtype_t wt, int64_t rows,
+                                   int64_t k, void* blocks, qblk_stream_t stream);
+
+/* 8-bit activations (TurboQuant article, section 2.2, which leaves the
+ * activation scaling open): for each of the n rows (tokens) of x (n x k,
+ * type xt, k a multiple of 8), one symmetric scale s = max|x| / 127 kept in
+ * fp32 (scale[t], n floats) and codes xq = clamp(round_half_away(x / s),
+ * -127, 127) (n x k int8, row-major); a zero row gives s = 0 and codes 0. */
+qblk_status_t qblk_quantize_act_i8(const void* x, qblk_dtype_t xt, int64_t n,
+                                   int64_t k, int8_t* xq, float* scale,
+                                   qblk_stream_t stream);
+
+/* W4A8 product Y = X W^T with W (m x k) in QBLK_W4G128 and X given as the
+ * int8 codes xq (n x k) and token scales (n floats) of
+ * qblk_quantize_act_i8: Y[t,i] = scale[t] * sum_g d[i,g] *
+ * sum_{k in g} (code - 8) * xq[t,k], Y n x m fp32 row-major.  The integer
+ * sums are exact; Y is within 2e-5 * sum_k |W[i,k] * scale[t] * xq[t,k]| of
+ * the exact product of the rebuilt weights and activations.  n = 1 runs a
+ * batch-1 kernel (k <= 16384); otherwise int8 matrix cores, with the k range
+ * split over the grid (partial sums added into Y, zeroed first by this call)
+ * when m*n is small.  qblk_gemv and qblk_gemm return QBLK_ERR_UNSUPPORTED
+ * for QBLK_W4G128. */
+qblk_status_t qblk_gemm_w4a8(const void* blocks, int64_t m, int64_t k,
+                             const int8_t* xq, const float* scale, int64_t n,
+                             float* y, qblk_stream_t stream);
 
 /* Q4_0 quantization as the Q4_0 chapter's section 4.4 prints it: the signed
  * value of largest magnitude divided by -8 is the scale, codes are

@@ -41,6 +41,9 @@ def test_geometry(q):
     assert [q.block_bytes(f) for f in (q.Q4_0, q.SB4, q.SB4_AFFINE, q.Q4_K)] == [18, 138, 148, 144]
     assert [q.block_elems(f) for f in (q.Q4_0, q.SB4, q.SB4_AFFINE, q.Q4_K)] == [32, 256, 256, 256]
     assert q.packed_bytes(q.Q4_K, 11008, 4096) == 11008 * 16 * 144
+    assert q.block_bytes(q.W4G128) == 66 and q.block_elems(q.W4G128) == 128
+    assert q.packed_bytes(q.W4G128, 11008, 4096) == 11008 * 4096 // 2 + 11008 * 32 * 2
+    assert q.packed_bytes(q.W4G128, 3, 192) == 0
     assert q.block_bytes(9) == 0 and q.block_elems(9) == 0
     assert q.packed_bytes(q.SB4, 11008, 4096) == 24305664
     assert q.packed_bytes(q.Q4_0, 4096, 4096) == 9437184
@@ -81,7 +84,16 @@ def test_argument_errors(q):
     assert L.qblk_quantize_q4_k(A, 3, 1, 256, B, S) == 3
     assert L.qblk_quantize_q4_k(A, 0, 1, 32, B, S) == 2
     assert L.qblk_quantize_q4_k(A, 0, 1, 256, MIS, S) == 4
-    assert L.qblk_dequant(4, A, 1, 256, B, 0, S) == 7
+    assert L.qblk_dequant(5, A, 1, 256, B, 0, S) == 7
+    assert L.qblk_quantize_w4g128(A, 0, 1, 192, B, S) == 2
+    assert L.qblk_quantize_w4g128(A, 4, 1, 128, B, S) == 3
+    assert L.qblk_quantize_act_i8(A, 0, 2, 12, B, Y, S) == 2
+    assert L.qblk_quantize_act_i8(A, 0, 2, 16, B, MIS, S) == 4
+    assert L.qblk_gemm_w4a8(A, 4, 192, B, Y, 2, Y, S) == 2
+    assert L.qblk_gemm_w4a8(A, 4, 128, B, NUL, 2, Y, S) == 1
+    # group-128 weights multiply only 8-bit activations
+    assert L.qblk_gemv(4, A, 4, 128, B, 1, Y, S) == 5
+    assert L.qblk_gemm(4, A, 4, 256, B, 2, 4, Y, S) == 5
     # null and misaligned pointers
     assert L.qblk_quantize_q4_0(NUL, 0, 1, 32, B, S) == 1
     assert L.qblk_dequant(0, A, 1, 32, NUL, 0, S) == 1
@@ -103,6 +115,8 @@ def test_empty_calls_succeed_without_launch(q):
     assert L.qblk_quantize_q4_0(NUL, 0, 0, 32, NUL, S) == 0
     assert L.qblk_quantize_sb4(NUL, 1, 5, 0, 1, NUL, S) == 0
     assert L.qblk_quantize_q4_k(NUL, 2, 0, 256, NUL, S) == 0
+    assert L.qblk_quantize_act_i8(NUL, 1, 0, 256, NUL, NUL, S) == 0
+    assert L.qblk_gemm_w4a8(NUL, 0, 256, NUL, NUL, 4, NUL, S) == 0
     assert L.qblk_dequant(2, NUL, 0, 256, NUL, 2, S) == 0
     assert L.qblk_gemv(1, NUL, 0, 256, NUL, 1, NUL, S) == 0
     assert L.qblk_gemm(1, NUL, 0, 256, NUL, 2, 8, NUL, S) == 0

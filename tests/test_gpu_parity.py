@@ -378,3 +378,106 @@ def test_gemm_q4_k_prefill_shape(q, n):
     rows = np.concatenate([rows, [0, m - 1]])
     Y_ref, B = O.gemm(O.Q4_K, blocks, m, k, WL.bf16_values(X).astype(np.float64), rows=rows)
     check_products(Y[:, rows], Y_ref, B, f"gemm q4k n={n}")
+
+
+# ------------------------------------------- group-128 W4 weights, int8 activations
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_quantize_w4g128_bit_exact(q, dtype):
+    # 16 x 2304: 288 groups (18 workgroups); near-tie rows exercise the exact branch
+    for w in (mixed_blocks(16, 2304, 31), near_ties(7, 2304, 32)):
+        d, h = gpu_input(w, dtype)
+        got = host(q.quantize(d, q.W4G128))
+        assert np.array_equal(got, O.quantize_w4g128(h)), f"first mismatch at byte {np.argmax(got != O.quantize_w4g128(h))}"
+
+
+@pytest.mark.parametrize("ot", ["f32", "f16", "bf16"])
+def test_dequant_w4g128_bit_exact(q, ot):
+    rows, k = 5, 128 * 11
+    rng = np.random.default_rng(33)
+    codes = rng.integers(0, 256, rows * k // 2, dtype=np.uint8)
+    sc = rng.integers(0, 0x7C00, rows * k // 128).astype(np.uint16)
+    sc |= (rng.integers(0, 2, sc.size) << 15).astype(np.uint16)
+    for blocks in (np.concatenate([codes, sc.view(np.uint8)]), O.quantize_w4g128(mixed_blocks(rows, k, 34))):
+        dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[ot]
+        got = q.dequant(dev(blocks), q.W4G128, rows, k, dt)
+        ref = O.dequant(O.W4G128, blocks, rows, k)
+        if ot == "f32":
+            assert np.array_equal(host(got).view(np.uint32), ref.view(np.uint32))
+        elif ot == "f16":
+            assert np.array_equal(host(got).view(np.uint16), ref.astype(np.float16).view(np.uint16))
+        else:
+            refb = torch.from_numpy(ref).to(torch.bfloat16).view(torch.int16).numpy()
+            assert np.array_equal(host(got.view(torch.int16)), refb)
+
+
+def act_rows(n, k, seed):
+    """Token rows: gaussian, heavy-tailed, exact ties of the int8 grid, zeros."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, k)).astype(np.float32)
+    if n > 1:
+        x[1] = rng.standard_t(2, k)
+    if n > 2:  # max 127 * 2^-4: every multiple of 2^-5 is a tie or a grid point
+        x[2] = (rng.integers(-254, 255, k) / 2.0) * 2.0 ** -4
+        x[2, 0] = 127 * 2.0 ** -4
+    if n > 3:
+        x[3] = 0.0
+    return x
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_quantize_act_i8_bit_exact(q, dtype):
+    x = act_rows(6, 2304, 35)
+    d, h = gpu_input(x, dtype)
+    xq, s = q.quantize_act_i8(d)
+    xq_ref, s_ref = O.quantize_act_i8(h)
+    assert np.array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(host(xq), xq_ref)
+
+
+def w4a8_case(q, m, k, n, seed, rows=None):
+    w = mixed_blocks(m, k, seed)
+    blocks = O.quantize_w4g128(w)
+    x = act_rows(n, k, seed + 1)
+    xq_ref, s_ref = O.quantize_act_i8(x)
+    xq, s = q.quantize_act_i8(dev(x))
+    assert np.array_equal(host(xq), xq_ref) and np.array_equal(host(s), s_ref)
+    Y = host(q.gemm_w4a8(dev(blocks), m, k, xq, s))
+    Y_ref, B = O.gemm_w4a8(blocks, m, k, xq_ref, s_ref, rows=rows)
+    check_products(Y if rows is None else Y[:, rows], Y_ref, B, f"w4a8 {m}x{k} n={n}")
+
+
+# one token: chunks per lane 1..8 (k = 128 .. 16384) and 1..3 rows per wave;
+# k = 16512 takes the matrix-core path with n = 1
+@pytest.mark.parametrize("shape", [(37, 128), (150, 2304), (300, 4096), (11008, 4096), (77, 11008),
+                                   (600, 14336), (40, 16384), (20, 16512)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_gemv_w4a8(q, shape):
+    m, k = shape
+    w4a8_case(q, m, k, 1, 36)
+
+
+@pytest.mark.parametrize("n", [2, 5, 16, 24, 40, 64, 100, 200])
+def test_gemm_w4a8(q, n):
+    w4a8_case(q, 150, 2304, n, 37)
+
+
+@pytest.mark.parametrize("n", [3, 20, 130])
+def test_gemm_w4a8_split_k(q, n):
+    w4a8_case(q, 40, 14336, n, 38)
+
+
+@pytest.mark.parametrize("n", [16, 64, 512])
+def test_gemm_w4a8_prefill_shape(q, n):
+    w, X = WL.sb4_prefill("up", n)
+    m, k = w.shape
+    blocks = O.quantize_w4g128(w)
+    bd = q.quantize(dev(w), q.W4G128)
+    assert np.array_equal(host(bd), blocks)
+    x = WL.bf16_values(X).astype(np.float32)
+    xq_ref, s_ref = O.quantize_act_i8(x)
+    xq, s = q.quantize_act_i8(dev_bf16(X))
+    assert np.array_equal(host(xq), xq_ref) and np.array_equal(host(s), s_ref)
+    Y = host(q.gemm_w4a8(bd, m, k, xq, s))
+    rows = np.random.default_rng(n + 2).choice(m, size=64 if n == 512 else 256, replace=False)
+    rows = np.concatenate([rows, [0, m - 1]])
+    Y_ref, B = O.gemm_w4a8(blocks, m, k, xq_ref, s_ref, rows=rows)
+    check_products(Y[:, rows], Y_ref, B, f"w4a8 prefill n={n}")
