@@ -4,7 +4,8 @@
 // What is computed: Y[t,i] = s_t * sum_g d[i,g] * sum_{k in g} (code-8) * xq[t,k]
 // -- the product of the rebuilt weights d*(code-8) and the rebuilt activations
 // s_t*xq.  The inner sums are integers, formed exactly in int32 (v_dot4_i32_i8
-// for one token, int8 matrix ops for several); each group's sum is then
+// for one token, int8 matrix ops -- 16x16x64 tiles up to 16 tokens, 32x32x32
+// wide tiles beyond -- for several); each group's sum is then
 // scaled by its fp16 weight scale in fp32, and the token scale is applied
 // once at the end.  The codes enter the integer products as they are stored
 // (0..15); the -8 offset is the integer -8 * sum(xq) over the same k range,
@@ -326,6 +327,174 @@ __global__ __launch_bounds__(kThreadsM) void k_gemm_w4a8(const uint8_t* __restri
   }
 }
 
+// ===================================================================
+// Many tokens: v_mfma_i32_32x32x32_i8, wide tiles.
+//
+// Operand layout: lane l holds row (l % 32) of A and column (l % 32) of B,
+// each with 16 int8 k values of its half (l / 32); lane l receives
+// D[8*(r/4) + 4*(l/32) + r%4][l % 32], r = 0..15.  For step s (0..3) of a
+// 128-weight group, half h takes code bytes j0..j0+7, j0 = 32h + 8s -- so a
+// lane reads 32 contiguous code bytes per group -- i.e. weights j0..j0+7
+// (low nibbles) and 64+j0..64+j0+7 (high nibbles), and the same activations.
+// A = X (tokens), B = W^T, so all 16 outputs of a lane share one weight row
+// and one scale per group; the integer accumulator starts at -8*sum(xq) of
+// each output's token (16 values, four 16-byte LDS reads).
+//
+// A workgroup of 4 waves owns 128 weight rows (32 per wave) and 32*T32
+// tokens.  X is staged SG groups at a time in LDS, double-buffered: per token
+// and group 8 pieces of 16 bytes in operand order (piece 4h + s), token rows
+// 128*SG + 16 bytes apart, so the 16 lanes of one read phase (16 consecutive
+// tokens, one piece) hit 16 different 4-bank groups.
+// ===================================================================
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int T32, int SG, bool SPLIT>
+__global__ __launch_bounds__(256, 2) void k_gemm_w4a8_w(const uint8_t* __restrict__ codes,
+                                                       const uint16_t* __restrict__ scales,
+                                                       const int8_t* __restrict__ xq,
+                                                       const float* __restrict__ xs,
+                                                       float* __restrict__ Y, int M, int K, int N,
+                                                       int stages_per_split) {
+  constexpr int NT = 32 * T32;
+  constexpr int XROW = 128 * SG + 16;
+  constexpr int XCH = NT * 8 * SG;
+  constexpr int XPT = XCH / 256;
+  static_assert(XCH % 256 == 0, "X chunks per thread");
+  __shared__ uint4 xs4[2][NT * XROW / 16];
+  __shared__ i32x4_t xcor4[2][SG][NT / 4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int NG = K >> 7;
+  const int NS = NG / SG;
+  const int64_t rowbytes = K >> 1;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 128 + wave * 32 + l32;
+  const int64_t rowc = row < M ? row : M - 1;
+  const int n0 = blockIdx.y * NT;
+  const int s_begin = SPLIT ? blockIdx.z * stages_per_split : 0;
+  const int s_end = SPLIT ? min(NS, s_begin + stages_per_split) : NS;
+
+  auto load_x = [&](int st, uint4 xv[XPT]) {
+#pragma unroll
+    for (int i = 0; i < XPT; i++) {
+      const int c = threadIdx.x + i * 256;
+      const int tok = c / (8 * SG), rem = c % (8 * SG);
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (n0 + tok < N)
+        v = *reinterpret_cast<const uint4*>(xq + static_cast<int64_t>(n0 + tok) * K + 128 * SG * st + 16 * rem);
+      xv[i] = v;
+    }
+  };
+  auto store_x = [&](int buf, const uint4 xv[XPT]) {
+    uint8_t* xsb = reinterpret_cast<uint8_t*>(xs4[buf]);
+#pragma unroll
+    for (int i = 0; i < XPT; i++) {
+      const int c = threadIdx.x + i * 256;
+      const int tok = c / (8 * SG), rem = c % (8 * SG);
+      const int grp = rem >> 3, cc = rem & 7;
+      // activations 16cc..16cc+15 (mod 64) of group grp: pieces p0 = 4h' + 2(cc&1)
+      // and p0 + 1 with h' = (cc&3)/2; first halves for cc < 4, second halves after
+      const int p0 = 4 * ((cc & 3) >> 1) + 2 * (cc & 1);
+      uint8_t* r = xsb + tok * XROW + 128 * grp + 16 * p0 + 8 * (cc >> 2);
+      *reinterpret_cast<uint2*>(r) = make_uint2(xv[i].x, xv[i].y);
+      *reinterpret_cast<uint2*>(r + 16) = make_uint2(xv[i].z, xv[i].w);
+      int s = dot4(xv[i].x, kOnes8, 0);
+      s = dot4(xv[i].y, kOnes8, s);
+      s = dot4(xv[i].z, kOnes8, s);
+      s = dot4(xv[i].w, kOnes8, s);
+      s += __shfl_xor(s, 1, kWave);
+      s += __shfl_xor(s, 2, kWave);
+      s += __shfl_xor(s, 4, kWave);
+      if (cc == 0) reinterpret_cast<int*>(xcor4[buf][grp])[tok] = -8 * s;
+    }
+  };
+  auto load_w = [&](int st, uint4 raw[SG][2], uint32_t sc[SG]) {
+#pragma unroll
+    for (int grp = 0; grp < SG; grp++) {
+      const int G = SG * st + grp;
+      const uint4* p = reinterpret_cast<const uint4*>(codes + rowc * rowbytes + 64 * G + 32 * h);
+      raw[grp][0] = p[0];
+      raw[grp][1] = p[1];
+      sc[grp] = scales[rowc * NG + G];
+    }
+  };
+
+  f32x16_t acc[T32];
+#pragma unroll
+  for (int t = 0; t < T32; t++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[t][r] = 0.0f;
+
+  uint4 xv[XPT];
+  uint4 raw[SG][2], nraw[SG][2];
+  uint32_t sc[SG], nsc[SG];
+  if (s_begin < s_end) {
+    load_x(s_begin, xv);
+    load_w(s_begin, raw, sc);
+    store_x(0, xv);
+  }
+  for (int st = s_begin; st < s_end; st++) {
+    const int buf = (st - s_begin) & 1;
+    __syncthreads();
+    const bool more = st + 1 < s_end;
+    if (more) {
+      load_x(st + 1, xv);
+      load_w(st + 1, nraw, nsc);
+    }
+    const uint8_t* xsb = reinterpret_cast<const uint8_t*>(xs4[buf]);
+#pragma unroll
+    for (int grp = 0; grp < SG; grp++) {
+      const float d = f16_bits_to_f32(sc[grp]);
+      const uint32_t w[8] = {raw[grp][0].x, raw[grp][0].y, raw[grp][0].z, raw[grp][0].w,
+                             raw[grp][1].x, raw[grp][1].y, raw[grp][1].z, raw[grp][1].w};
+      i32x4_t B[4];
+#pragma unroll
+      for (int s = 0; s < 4; s++)
+        B[s] = i32x4_t{static_cast<int>(w[2 * s] & kLo4), static_cast<int>(w[2 * s + 1] & kLo4),
+                       static_cast<int>((w[2 * s] >> 4) & kLo4), static_cast<int>((w[2 * s + 1] >> 4) & kLo4)};
+#pragma unroll
+      for (int t = 0; t < T32; t++) {
+        const i32x4_t* xc = xcor4[buf][grp] + 8 * t + h;
+        const i32x4_t c0 = xc[0], c1 = xc[2], c2 = xc[4], c3 = xc[6];
+        i32x16_t D = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w,
+                      c2.x, c2.y, c2.z, c2.w, c3.x, c3.y, c3.z, c3.w};
+        const uint8_t* ar = xsb + (32 * t + l32) * XROW + 128 * grp + 64 * h;
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+          const i32x4_t A = *reinterpret_cast<const i32x4_t*>(ar + 16 * s);
+          D = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B[s], D, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[t][r] = __builtin_fmaf(d, static_cast<float>(D[r]), acc[t][r]);
+      }
+    }
+    if (more) {
+      store_x(buf ^ 1, xv);
+#pragma unroll
+      for (int grp = 0; grp < SG; grp++) {
+        raw[grp][0] = nraw[grp][0];
+        raw[grp][1] = nraw[grp][1];
+        sc[grp] = nsc[grp];
+      }
+    }
+  }
+
+  if (row >= M) return;
+#pragma unroll
+  for (int t = 0; t < T32; t++) {
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int n = n0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (n < N) {
+        float* dst = Y + static_cast<int64_t>(n) * M + row;
+        const float v = acc[t][r] * xs[n];
+        if constexpr (SPLIT) atomicAdd(dst, v);
+        else *dst = v;
+      }
+    }
+  }
+}
+
 template <int RMAX, int UPL>
 hipError_t launch_v_t(const uint8_t* codes, const uint16_t* scales, int64_t m, int64_t k, const int8_t* xq,
                       const float* xs, float* y, int rpw, hipStream_t s) {
@@ -389,6 +558,29 @@ hipError_t launch_m(const uint8_t* codes, const uint16_t* scales, int64_t m, int
   return hipGetLastError();
 }
 
+template <int T32, int SG>
+hipError_t launch_w(const uint8_t* codes, const uint16_t* scales, int64_t m, int64_t k, const int8_t* xq,
+                    const float* xs, int64_t n, float* y, int64_t want_tiles, hipStream_t s) {
+  const unsigned gx = static_cast<unsigned>((m + 127) / 128);
+  const unsigned gy = static_cast<unsigned>((n + 32 * T32 - 1) / (32 * T32));
+  const int ns = static_cast<int>(k / 128 / SG);
+  const int64_t tiles = static_cast<int64_t>(gx) * gy;
+  if (tiles < want_tiles && ns > 1) {
+    int split = static_cast<int>((want_tiles + tiles - 1) / tiles);
+    split = split > ns ? ns : split;
+    const int per = (ns + split - 1) / split;
+    const unsigned gz = static_cast<unsigned>((ns + per - 1) / per);
+    const hipError_t e = launch_fill_zero(y, m * n, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_gemm_w4a8_w<T32, SG, true>), dim3(gx, gy, gz), dim3(kThreadsM), 0, s, codes, scales, xq,
+                       xs, y, static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), per);
+  } else {
+    hipLaunchKernelGGL((k_gemm_w4a8_w<T32, SG, false>), dim3(gx, gy, 1), dim3(kThreadsM), 0, s, codes, scales, xq,
+                       xs, y, static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), ns);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_w4a8(const void* blocks, int64_t m, int64_t k, const int8_t* xq, const float* xs,
@@ -396,9 +588,16 @@ hipError_t launch_gemm_w4a8(const void* blocks, int64_t m, int64_t k, const int8
   const uint8_t* codes = static_cast<const uint8_t*>(blocks);
   const uint16_t* scales = reinterpret_cast<const uint16_t*>(codes + m * k / 2);
   if (n == 1 && k <= 8 * 64 * 32) return launch_v(codes, scales, m, k, xq, xs, y, s);
+  // tilings measured at 14336 x 4096: 16 x 16 tiles with K split up to N = 16,
+  // then the wide kernel, 32 tokens (two groups per stage when the group
+  // count is even) up to N = 64, 128 tokens beyond
+  const int64_t cus = cu_count_w4();
   if (n <= 16) return launch_m<1, 1>(codes, scales, m, k, xq, xs, n, y, s);
-  if (n <= 64) return launch_m<2, 4>(codes, scales, m, k, xq, xs, n, y, s);
-  return launch_m<4, 4>(codes, scales, m, k, xq, xs, n, y, s);
+  if (n <= 64) {
+    if ((k / 128) % 2 == 0) return launch_w<1, 2>(codes, scales, m, k, xq, xs, n, y, cus, s);
+    return launch_w<1, 1>(codes, scales, m, k, xq, xs, n, y, cus, s);
+  }
+  return launch_w<4, 1>(codes, scales, m, k, xq, xs, n, y, cus, s);
 }
 
 }  // namespace qblk

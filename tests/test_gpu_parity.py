@@ -465,6 +465,12 @@ def test_gemm_w4a8_split_k(q, n):
     w4a8_case(q, 40, 14336, n, 38)
 
 
+@pytest.mark.parametrize("n", [40, 300])
+def test_gemm_w4a8_odd_group_count(q, n):
+    # k = 9 groups: the wide kernel stages one group at a time
+    w4a8_case(q, 200, 1152, n, 39)
+
+
 @pytest.mark.parametrize("n", [16, 64, 512])
 def test_gemm_w4a8_prefill_shape(q, n):
     w, X = WL.sb4_prefill("up", n)
