@@ -131,6 +131,8 @@ def main():
                          "launches of one prefill GEMM (--gemm-shape, --gemm-n), for counters")
     ap.add_argument("--gemm-shape", choices=("up", "down"), default="up")
     ap.add_argument("--gemm-n", type=int, default=512)
+    ap.add_argument("--gemm-fmt", choices=("sb4", "q4_0", "sb4a", "q4k", "w4a8"), default="sb4",
+                    help="weight format of the --mode gemm launches (w4a8: group-128 weights, int8 tokens)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -153,7 +155,7 @@ def main():
         traffic_run(torch, q, WL, dev)
         return
     if args.mode == "gemm":
-        gemm_run(torch, q, WL, np, dev, args.gemm_shape, args.gemm_n)
+        gemm_run(torch, q, WL, np, dev, args.gemm_shape, args.gemm_n, args.gemm_fmt)
         return
 
     # ------------------------------------------------------------ headline
@@ -264,19 +266,25 @@ def traffic_run(torch, q, WL, dev):
     log("traffic run done")
 
 
-def gemm_run(torch, q, WL, np, dev, shape, n_tok):
-    """Three launches of the Type 0 prefill GEMM on the seeded workload (one
-    weight copy: for counter runs, not timing)."""
+def gemm_run(torch, q, WL, np, dev, shape, n_tok, fmt_name="sb4"):
+    """Three launches of one prefill GEMM on the seeded workload (one weight
+    copy: for counter runs, not timing)."""
     w, X = WL.sb4_prefill(shape, n_tok)
     m, k = w.shape
-    b = q.quantize(torch.from_numpy(w).to(dev), q.SB4)
+    fmt = {"sb4": q.SB4, "q4_0": q.Q4_0, "sb4a": q.SB4_AFFINE, "q4k": q.Q4_K, "w4a8": q.W4G128}[fmt_name]
+    b = q.quantize(torch.from_numpy(w).to(dev), fmt)
     Xd = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16)
     Y = torch.empty((n_tok, m), dtype=torch.float32, device=dev)
+    if fmt == q.W4G128:
+        xq, xs = q.quantize_act_i8(Xd)
+        run = lambda: q.gemm_w4a8(b, m, k, xq, xs, out=Y)  # noqa: E731
+    else:
+        run = lambda: q.gemm(b, fmt, m, k, Xd, out=Y)  # noqa: E731
     torch.cuda.synchronize()
     for _ in range(3):
-        q.gemm(b, q.SB4, m, k, Xd, out=Y)
+        run()
     torch.cuda.synchronize()
-    log(f"gemm run done ({shape}, {m}x{k}, n={n_tok})")
+    log(f"gemm run done ({fmt_name}, {shape}, {m}x{k}, n={n_tok})")
 
 
 # ----------------------------------------------------------------- other rows

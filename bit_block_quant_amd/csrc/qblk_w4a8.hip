@@ -338,13 +338,14 @@ __global__ __launch_bounds__(kThreadsM) void k_gemm_w4a8(const uint8_t* __restri
 // (low nibbles) and 64+j0..64+j0+7 (high nibbles), and the same activations.
 // A = X (tokens), B = W^T, so all 16 outputs of a lane share one weight row
 // and one scale per group; the integer accumulator starts at -8*sum(xq) of
-// each output's token (16 values, four 16-byte LDS reads).
+// each output's token (16 values in output order: one 64-byte LDS read).
 //
 // A workgroup of 4 waves owns 128 weight rows (32 per wave) and 32*T32
 // tokens.  X is staged SG groups at a time in LDS, double-buffered: per token
 // and group 8 pieces of 16 bytes in operand order (piece 4h + s), token rows
 // 128*SG + 16 bytes apart, so the 16 lanes of one read phase (16 consecutive
-// tokens, one piece) hit 16 different 4-bank groups.
+// tokens, one piece) hit 16 different 4-bank groups.  Within a stage the
+// token tiles form a software pipeline.
 // ===================================================================
 typedef int i32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -405,7 +406,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4a8_w(const uint8_t* __restric
       s += __shfl_xor(s, 1, kWave);
       s += __shfl_xor(s, 2, kWave);
       s += __shfl_xor(s, 4, kWave);
-      if (cc == 0) reinterpret_cast<int*>(xcor4[buf][grp])[tok] = -8 * s;
+      // stored in output order: the 16 starting values of lane (tile t, half h)
+      // are slots 32t + 16h .. +15 (token 8(r/4) + 4h + r%4 of the tile at 16h + r)
+      const int u = tok & 31;
+      if (cc == 0) reinterpret_cast<int*>(xcor4[buf][grp])[(tok & ~31) + 16 * ((u >> 2) & 1) + 4 * (u >> 3) + (u & 3)] = -8 * s;
     }
   };
   auto load_w = [&](int st, uint4 raw[SG][2], uint32_t sc[SG]) {
@@ -425,9 +429,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4a8_w(const uint8_t* __restric
 #pragma unroll
     for (int r = 0; r < 16; r++) acc[t][r] = 0.0f;
 
+  // codes and activations of the next stage are fetched during this one
   uint4 xv[XPT];
-  uint4 raw[SG][2], nraw[SG][2];
-  uint32_t sc[SG], nsc[SG];
+  uint4 raw[SG][2], n1[SG][2];
+  uint32_t sc[SG], s1[SG];
   if (s_begin < s_end) {
     load_x(s_begin, xv);
     load_w(s_begin, raw, sc);
@@ -439,7 +444,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4a8_w(const uint8_t* __restric
     const bool more = st + 1 < s_end;
     if (more) {
       load_x(st + 1, xv);
-      load_w(st + 1, nraw, nsc);
+      load_w(st + 1, n1, s1);
     }
     const uint8_t* xsb = reinterpret_cast<const uint8_t*>(xs4[buf]);
 #pragma unroll
@@ -452,30 +457,41 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4a8_w(const uint8_t* __restric
       for (int s = 0; s < 4; s++)
         B[s] = i32x4_t{static_cast<int>(w[2 * s] & kLo4), static_cast<int>(w[2 * s + 1] & kLo4),
                        static_cast<int>((w[2 * s] >> 4) & kLo4), static_cast<int>((w[2 * s + 1] >> 4) & kLo4)};
+      // tiles in a software pipeline: tile t's matrix ops run while tile t+1's
+      // operands are read and tile t-1's sums are scaled on the VALU
+      const uint8_t* abase = xsb + l32 * XROW + 128 * grp + 64 * h;
+      const int* cbase = reinterpret_cast<const int*>(xcor4[buf][grp]) + 16 * h;
+      i32x4_t A[2][4];
+      i32x16_t D[2];
+#pragma unroll
+      for (int s = 0; s < 4; s++) A[0][s] = *reinterpret_cast<const i32x4_t*>(abase + 16 * s);
+      D[0] = *reinterpret_cast<const i32x16_t*>(cbase);
 #pragma unroll
       for (int t = 0; t < T32; t++) {
-        const i32x4_t* xc = xcor4[buf][grp] + 8 * t + h;
-        const i32x4_t c0 = xc[0], c1 = xc[2], c2 = xc[4], c3 = xc[6];
-        i32x16_t D = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w,
-                      c2.x, c2.y, c2.z, c2.w, c3.x, c3.y, c3.z, c3.w};
-        const uint8_t* ar = xsb + (32 * t + l32) * XROW + 128 * grp + 64 * h;
+        const int cur = t & 1, nxt = cur ^ 1;
+        if (t + 1 < T32) {
 #pragma unroll
-        for (int s = 0; s < 4; s++) {
-          const i32x4_t A = *reinterpret_cast<const i32x4_t*>(ar + 16 * s);
-          D = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B[s], D, 0, 0, 0);
+          for (int s = 0; s < 4; s++)
+            A[nxt][s] = *reinterpret_cast<const i32x4_t*>(abase + 32 * (t + 1) * XROW + 16 * s);
         }
 #pragma unroll
-        for (int r = 0; r < 16; r++) acc[t][r] = __builtin_fmaf(d, static_cast<float>(D[r]), acc[t][r]);
-      }
-    }
-    if (more) {
-      store_x(buf ^ 1, xv);
+        for (int s = 0; s < 4; s++) D[cur] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[cur][s], B[s], D[cur], 0, 0, 0);
+        if (t > 0) {
 #pragma unroll
-      for (int grp = 0; grp < SG; grp++) {
-        raw[grp][0] = nraw[grp][0];
-        raw[grp][1] = nraw[grp][1];
-        sc[grp] = nsc[grp];
+          for (int r = 0; r < 16; r++) acc[t - 1][r] = __builtin_fmaf(d, static_cast<float>(D[nxt][r]), acc[t - 1][r]);
+        }
+        if (t + 1 < T32) D[nxt] = *reinterpret_cast<const i32x16_t*>(cbase + 32 * (t + 1));
       }
+#pragma unroll
+      for (int r = 0; r < 16; r++)
+        acc[T32 - 1][r] = __builtin_fmaf(d, static_cast<float>(D[(T32 - 1) & 1][r]), acc[T32 - 1][r]);
+    }
+    if (more) store_x(buf ^ 1, xv);
+#pragma unroll
+    for (int grp = 0; grp < SG; grp++) {
+      raw[grp][0] = n1[grp][0];
+      raw[grp][1] = n1[grp][1];
+      sc[grp] = s1[grp];
     }
   }
 
