@@ -224,6 +224,8 @@ def main():
             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
         },
         "hbm_reference": achievable,
+        "inputs": {"numpy": WL.NUMPY_VERSION, "w_f32_sha256": WL.sha256(w), "x_f16_sha256": WL.sha256(x),
+                   "seeds": WL.SEEDS["sb4_decode_up"]},
         "device": props.name,
         "weights_per_s": round(M * K / (ms * 1e-3), 1),
         "gemv_per_s": round(1.0 / (ms * 1e-3), 1),

@@ -16,7 +16,18 @@ Workload recipes (std means standard deviation):
   sb4_prefill   14336 x 4096 and 4096 x 14336 f32 ~N(0, 0.02); activations
                 bf16 N x K ~N(0,1), N in {16, 64, 512}.
 """
+import hashlib
+
 import numpy as np
+
+NUMPY_VERSION = np.__version__
+
+
+def sha256(a):
+    """SHA-256 (hex) of an array's bytes in C order: the fingerprint recorded
+    with every measurement, so a run can show which inputs it used."""
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
 
 # ---------------------------------------------------------------- seeds
 SEEDS = {
