@@ -94,8 +94,9 @@ def near_ties(rows, k, seed):
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: NAMES[f])
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_quantize_bit_exact(q, fmt, dtype):
-    # 7 x 2304: 63 super-blocks (7 workgroups + a ragged tail) or 504 Q4_0 blocks
-    for w in (mixed_blocks(16, 2304, 1), near_ties(7, 2304, 2)):
+    # 16 x 2304: 144 super-blocks or 1152 Q4_0 blocks; 3 x 768: 9 super-blocks
+    # or 72 blocks, ragged tails of every quantizer's workgroup
+    for w in (mixed_blocks(16, 2304, 1), near_ties(7, 2304, 2), mixed_blocks(3, 768, 3)):
         d, h = gpu_input(w, dtype)
         got = host(q.quantize(d, fmt))
         ref = O.quantize(fmt, h)
@@ -339,16 +340,18 @@ def test_gemm_other_formats_split_k(q, fmt, n):
     check_products(Y, Y_ref, B, f"gemm {fmt} split-K")
 
 
-@pytest.mark.parametrize("n", [3, 40, 130])
-def test_gemm_single_super_block(q, n):
-    # K = 256: one super-block, so every K-split and pipelining path degenerates
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: NAMES[f])
+@pytest.mark.parametrize("n", [3, 24, 40, 130])
+def test_gemm_single_super_block(q, fmt, n):
+    # K = 256: one super-block (eight Q4_0 blocks), so every K-split and
+    # pipelining path degenerates
     m, k = 70, 256
     w = mixed_blocks(m, k, 13)
-    blocks = O.quantize_sb4(w)
+    blocks = O.quantize(fmt, w)
     X = WL.bf16_bits(np.random.default_rng(14).standard_normal((n, k)).astype(np.float32))
-    Y = host(q.gemm(dev(blocks), q.SB4, m, k, dev_bf16(X)))
-    Y_ref, B = O.gemm(O.SB4, blocks, m, k, WL.bf16_values(X).astype(np.float64))
-    check_products(Y, Y_ref, B, f"gemm k=256 n={n}")
+    Y = host(q.gemm(dev(blocks), fmt, m, k, dev_bf16(X)))
+    Y_ref, B = O.gemm(fmt, blocks, m, k, WL.bf16_values(X).astype(np.float64))
+    check_products(Y, Y_ref, B, f"gemm {NAMES[fmt]} k=256 n={n}")
 
 
 @pytest.mark.parametrize("shape", ["up", "down"])
@@ -463,6 +466,12 @@ def test_gemm_w4a8(q, n):
 @pytest.mark.parametrize("n", [3, 20, 130])
 def test_gemm_w4a8_split_k(q, n):
     w4a8_case(q, 40, 14336, n, 38)
+
+
+@pytest.mark.parametrize("n", [2, 20, 40, 130])
+def test_gemm_w4a8_single_group(q, n):
+    # k = 128: one group, one stage
+    w4a8_case(q, 70, 128, n, 40)
 
 
 @pytest.mark.parametrize("n", [40, 300])
