@@ -95,10 +95,16 @@ def time_region(torch, fn):
 
 
 def hbm_reference(torch, dev, nbytes, C):
-    """What a plain device copy reaches on this GPU: torch's copy kernel over
-    the headline's byte count (C rotating buffers, so reads come from HBM) and
-    over 1 GiB.  Reported beside the nominal 8 TB/s peak; bytes = read + write."""
+    """What torch's own copy kernel reaches on this GPU, beside the nominal
+    8 TB/s: over the headline's byte count (C rotating buffers, so reads come
+    from HBM) and over 1 GiB; bytes = read + write."""
     out = {}
+
+    def rec(name, ms, nb):
+        gbs = nb / (ms * 1e-3) / 1e9
+        out[name] = {"us": round(ms * 1e3, 2), "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        log(f"  reference {name}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s")
+
     for name, nb, n in (("copy_24MB_rotating", nbytes, C), ("copy_1GiB", 1 << 30, 1)):
         n_el = nb // 4
         src = [torch.empty(n_el, dtype=torch.float32, device=dev) for _ in range(n)]
@@ -106,10 +112,7 @@ def hbm_reference(torch, dev, nbytes, C):
         for t in src:
             t.fill_(1.0)
         t = Timer(torch, lambda i: dst.copy_(src[i]), n)
-        ms = t.run(max(1, 480 // n))
-        gbs = 2 * n_el * 4 / (ms * 1e-3) / 1e9
-        out[name] = {"us": round(ms * 1e3, 2), "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
-        log(f"  reference {name}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s")
+        rec(name, t.run(max(1, 480 // n)), 2 * n_el * 4)
         del src, dst
     return out
 
@@ -227,6 +230,7 @@ def main():
         "inputs": {"numpy": WL.NUMPY_VERSION, "w_f32_sha256": WL.sha256(w), "x_f16_sha256": WL.sha256(x),
                    "seeds": WL.SEEDS["sb4_decode_up"]},
         "device": props.name,
+        "arch": getattr(props, "gcnArchName", ""),
         "weights_per_s": round(M * K / (ms * 1e-3), 1),
         "gemv_per_s": round(1.0 / (ms * 1e-3), 1),
     }
