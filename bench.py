@@ -330,12 +330,16 @@ def measure_rows(torch, q, WL, np, dev):
     gemv_row("gemv_q4k_11008x4096_f16", q.Q4_K, torch.from_numpy(w).to(dev), torch.from_numpy(x).to(dev))
 
     # quantizers
-    def quant_row(name, fmt, w, reps=20):
+    def quant_row(name, fmt, w):
+        # rotating input copies (past the last-level cache), one graph of C launches
         out = torch.empty(q.packed_bytes(fmt, *w.shape), dtype=torch.uint8, device=dev)
-        t = Timer(torch, lambda i: q.quantize(w, fmt, out=out), 1)
-        ms = t.run(reps)
+        C = n_copies(w.numel() * w.element_size())
+        ws = [w] + [w.clone() for _ in range(C - 1)]
+        t = Timer(torch, lambda i: q.quantize(ws[i], fmt, out=out), C)
+        ms = t.run(max(2, 40 // C))
         nb = w.numel() * w.element_size() + out.numel()
         hbm_row(name, ms, nb, weights_per_s=round(w.numel() / (ms * 1e-3), 1))
+        del ws
 
     w, _ = WL.q4_0_decode()
     quant_row("quantize_q4_0_4096x4096_f32", q.Q4_0, torch.from_numpy(w).to(dev))
@@ -349,9 +353,11 @@ def measure_rows(torch, q, WL, np, dev):
     # dequant
     b = q.quantize(wup, q.SB4)
     out = torch.empty(wup.shape, dtype=torch.float32, device=dev)
-    t = Timer(torch, lambda i: q.dequant(b, q.SB4, *wup.shape, out=out), 1)
-    hbm_row("dequant_sb4_11008x4096_to_f32", t.run(20), b.numel() + out.numel() * 4)
-    del wup, out, b
+    C = n_copies(b.numel())
+    bs = [b] + [b.clone() for _ in range(C - 1)]
+    t = Timer(torch, lambda i: q.dequant(bs[i], q.SB4, *wup.shape, out=out), C)
+    hbm_row("dequant_sb4_11008x4096_to_f32", t.run(max(2, 120 // C)), b.numel() + out.numel() * 4)
+    del wup, out, b, bs
 
     # 7B-shaped 32-layer stack, Type 1: quantize from fp16, then one GEMV pass
     mats, outs, xs = [], [], []
@@ -456,10 +462,12 @@ def w4a8_rows(torch, q, WL, np, dev):
     m, k = w.shape
     wd = torch.from_numpy(w).to(dev)
     out = torch.empty(q.packed_bytes(q.W4G128, m, k), dtype=torch.uint8, device=dev)
-    t = Timer(torch, lambda i: q.quantize(wd, q.W4G128, out=out), 1)
-    row(f"quantize_w4g128_{m}x{k}_f32", t.run(20), wd.numel() * 4 + out.numel())
+    C = n_copies(wd.numel() * 4)
+    ws = [wd] + [wd.clone() for _ in range(C - 1)]
+    t = Timer(torch, lambda i: q.quantize(ws[i], q.W4G128, out=out), C)
+    row(f"quantize_w4g128_{m}x{k}_f32", t.run(max(2, 40 // C)), wd.numel() * 4 + out.numel())
     b0 = out.clone()
-    del wd, out
+    del wd, out, ws
     xd = torch.from_numpy(x).to(dev).view(1, k)
     xq, xs = q.quantize_act_i8(xd)
     C = n_copies(b0.numel())
@@ -467,8 +475,8 @@ def w4a8_rows(torch, q, WL, np, dev):
     y = torch.empty((1, m), dtype=torch.float32, device=dev)
     t = Timer(torch, lambda i: q.gemm_w4a8(cps[i], m, k, xq, xs, out=y), C)
     row(f"gemv_w4a8_{m}x{k}_i8", t.run(max(1, 400 // C)), b0.numel() + k + 4 + 4 * m)
-    t = Timer(torch, lambda i: q.quantize_act_i8(xd, out=xq, scale=xs), 1)
-    row(f"quantize_act_i8_1x{k}_f16", t.run(50), k * 2 + k + 4)
+    t = Timer(torch, lambda i: q.quantize_act_i8(xd, out=xq, scale=xs), 50)  # 50 launches per graph
+    row(f"quantize_act_i8_1x{k}_f16", t.run(4), k * 2 + k + 4)
     del cps
 
     # prefill shape: int8 activations from bf16, then the product
@@ -482,8 +490,8 @@ def w4a8_rows(torch, q, WL, np, dev):
         Xd = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16)
         xq, xs = q.quantize_act_i8(Xd)
         if n_tok == 512:
-            t = Timer(torch, lambda i: q.quantize_act_i8(Xd, out=xq, scale=xs), 1)
-            row(f"quantize_act_i8_{n_tok}x{k}_bf16", t.run(50), n_tok * k * 3 + 4 * n_tok)
+            t = Timer(torch, lambda i: q.quantize_act_i8(Xd, out=xq, scale=xs), 50)
+            row(f"quantize_act_i8_{n_tok}x{k}_bf16", t.run(4), n_tok * k * 3 + 4 * n_tok)
         Y = torch.empty((n_tok, m), dtype=torch.float32, device=dev)
         t = Timer(torch, lambda i: q.gemm_w4a8(cps[i], m, k, xq, xs, out=Y), C)
         row(f"gemm_w4a8_{m}x{k}_n{n_tok}_i8", t.run(max(1, 100 // C)),
