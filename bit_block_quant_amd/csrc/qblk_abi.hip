@@ -53,6 +53,15 @@ qblk_status_t check_ptr(const void* p, bool needed) {
   return QBLK_OK;
 }
 
+// fp32 scale arrays (one per token) are read element by element: 4-byte
+// alignment, so that a slice of them starting at any token is accepted
+qblk_status_t check_ptr4(const void* p, bool needed) {
+  if (!needed) return QBLK_OK;
+  if (!p) return QBLK_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(p) & 3u) != 0) return QBLK_ERR_ALIGN;
+  return QBLK_OK;
+}
+
 qblk_status_t from_hip(hipError_t e) { return e == hipSuccess ? QBLK_OK : QBLK_ERR_LAUNCH; }
 
 #define QBLK_TRY(expr)                 \
@@ -141,7 +150,7 @@ qblk_status_t qblk_quantize_act_i8(const void* x, qblk_dtype_t xt, int64_t n, in
   if (!dtype_ok(xt)) return QBLK_ERR_DTYPE;
   QBLK_TRY(check_ptr(x, n > 0 && k > 0));
   QBLK_TRY(check_ptr(xq, n > 0 && k > 0));
-  QBLK_TRY(check_ptr(scale, n > 0));
+  QBLK_TRY(check_ptr4(scale, n > 0));
   if (n == 0) return QBLK_OK;
   return from_hip(qblk::launch_quantize_act_i8(x, xt, n, k, xq, scale,
                                                static_cast<hipStream_t>(stream)));
@@ -154,7 +163,7 @@ qblk_status_t qblk_gemm_w4a8(const void* blocks, int64_t m, int64_t k, const int
   const bool out = m > 0 && n > 0;
   QBLK_TRY(check_ptr(blocks, out && k > 0));
   QBLK_TRY(check_ptr(xq, out && k > 0));
-  QBLK_TRY(check_ptr(scale, out && k > 0));
+  QBLK_TRY(check_ptr4(scale, out && k > 0));
   QBLK_TRY(check_ptr(y, out));
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (!out) return QBLK_OK;

@@ -75,7 +75,8 @@
  *   - Arguments are checked on the host before any launch; on error nothing is
  *     launched and nothing is written.  A failed launch returns
  *     QBLK_ERR_LAUNCH.
- *   - Data pointers must be 16-byte aligned (QBLK_ERR_ALIGN).
+ *   - Data pointers must be 16-byte aligned (QBLK_ERR_ALIGN); the fp32
+ *     per-token scale arrays of the 8-bit activations only 4-byte aligned.
  *   - k must be a multiple of the format's block size (QBLK_ERR_SHAPE);
  *     rows/m/n/k may be 0 (an empty product writes zeros to y when m, n > 0).
  *   - rows, m, n and k must each stay below 2^31, and a packed matrix below

@@ -88,7 +88,7 @@ def test_argument_errors(q):
     assert L.qblk_quantize_w4g128(A, 0, 1, 192, B, S) == 2
     assert L.qblk_quantize_w4g128(A, 4, 1, 128, B, S) == 3
     assert L.qblk_quantize_act_i8(A, 0, 2, 12, B, Y, S) == 2
-    assert L.qblk_quantize_act_i8(A, 0, 2, 16, B, MIS, S) == 4
+    assert L.qblk_quantize_act_i8(A, 0, 2, 16, B, C.c_void_p(0x30001), S) == 4  # scales: 4-byte alignment
     assert L.qblk_gemm_w4a8(A, 4, 192, B, Y, 2, Y, S) == 2
     assert L.qblk_gemm_w4a8(A, 4, 128, B, NUL, 2, Y, S) == 1
     # group-128 weights multiply only 8-bit activations

@@ -496,3 +496,19 @@ def test_gemm_w4a8_prefill_shape(q, n):
     rows = np.concatenate([rows, [0, m - 1]])
     Y_ref, B = O.gemm_w4a8(blocks, m, k, xq_ref, s_ref, rows=rows)
     check_products(Y[:, rows], Y_ref, B, f"w4a8 prefill n={n}")
+
+
+def test_w4a8_token_slices(q):
+    # slices of the int8 tokens and of their fp32 scales (4-byte aligned) are
+    # valid inputs and give those tokens' rows of the product
+    m, k, n = 96, 1024, 9
+    w = mixed_blocks(m, k, 41)
+    blocks = O.quantize_w4g128(w)
+    bd = dev(blocks)
+    x = act_rows(n, k, 42)
+    xq, s = q.quantize_act_i8(dev(x))
+    xq_ref, s_ref = O.quantize_act_i8(x)
+    Y_ref, B = O.gemm_w4a8(blocks, m, k, xq_ref, s_ref)
+    for a, b in ((1, 2), (3, 9), (5, 6)):
+        Ys = host(q.gemm_w4a8(bd, m, k, xq[a:b], s[a:b]))
+        check_products(Ys, Y_ref[a:b], B[a:b], f"w4a8 tokens {a}:{b}")
