@@ -990,6 +990,192 @@ hipError_t launch_w(const void* blocks, int64_t m, int64_t k, const void* x, int
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Few tokens, Type 0, weights loaded by whole 16-byte code units.
+//
+// Loading the codes directly in matrix-operand order (a dword per lane and
+// sub-block, lanes spread over 16 rows) asks for every cache line of a
+// super-block about eight times.  Here the workgroup's tile -- 64*R16 rows
+// by NSB super-blocks -- is fetched as the batch-1 GEMV fetches it: each lane
+// takes whole sub-blocks (16 code bytes, dword-aligned from just below plus
+// the 2 bytes that spill past, and the two header fields), consecutive lanes
+// consecutive sub-blocks of a row.  The codes are written to LDS realigned,
+// one 16-byte slot per (row, sub-block) with rows padded to 16 slots + 16
+// bytes, and the fp32 scale 16*S*sc_j beside them; the matrix ops then read a
+// dword per lane from LDS (16 rows x 4 k-groups: 64 different banks).  As in
+// k_gemm_sb4_s every load of the workgroup is issued before the single
+// barrier, and the K range is split over the grid.
+// ---------------------------------------------------------------------------
+template <int R16, int T16, int NSB, bool SPLIT>
+__global__ __launch_bounds__(kThreads) void k_gemm_sb4_u(const uint8_t* __restrict__ W,
+                                                       const uint16_t* __restrict__ X,
+                                                       float* __restrict__ Y, int M, int K, int N) {
+  constexpr int NT = 16 * T16;
+  constexpr int RW = 64 * R16;             // weight rows per workgroup
+  constexpr int UR = NSB * 8;              // sub-blocks per row in the K slice
+  constexpr int kUPT = RW * UR / kThreads; // sub-blocks per thread
+  static_assert(RW * UR % kThreads == 0, "whole sub-blocks per thread");
+  constexpr int kCodeRow = UR * 16 + 16;   // bytes per staged row of codes
+  constexpr int kScRow = UR + 1;           // floats per staged row of scales
+  constexpr int kPieces = NSB * NT * 32;   // 16-byte pieces of the X slice
+  constexpr int kPer = (kPieces + kThreads - 1) / kThreads;
+  __shared__ uint4 xs4[NSB * NT * kLdsRow / 8];
+  __shared__ uint4 cs4[RW * kCodeRow / 16];
+  __shared__ float scs[RW * kScRow];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * RW;
+  const int n0 = blockIdx.y * NT;
+  const int nsb = K / 256;
+  const int b0 = blockIdx.z * NSB;
+  const int nb = min(NSB, nsb - b0);  // super-blocks in this piece of K (>= 1)
+  const int64_t rowbytes = static_cast<int64_t>(nsb) * 138;
+
+  // X first (L2-resident), then every sub-block of the tile.  Pieces past the
+  // slice's last super-block or past row M-1 / token N-1 re-read valid data
+  // that is never used or never stored.
+  uint4 xv[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; i++) {
+    const int c = min(static_cast<int>(threadIdx.x) + i * kThreads, kPieces - 1);
+    const int sb = c / (NT * 32), rem = c % (NT * 32);
+    const int t = min(n0 + (rem >> 5), N - 1), col = rem & 31;
+    const int b = b0 + min(sb, nb - 1);
+    xv[i] = *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(t) * K + 256 * b + 8 * col);
+  }
+  uint32_t q[kUPT][5], hs[kUPT];
+  int hc[kUPT];
+#pragma unroll
+  for (int i = 0; i < kUPT; i++) {
+    const int U = static_cast<int>(threadIdx.x) + i * kThreads;
+    const int r = U / UR, u = U % UR;
+    const int64_t m = m0 + r < M ? m0 + r : M - 1;
+    const uint8_t* blk = W + m * rowbytes + 138 * (b0 + min(u >> 3, nb - 1));
+    const uint8_t* cp = blk + 10 + 16 * (u & 7);
+    const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(cp) & 3u);  // 0 or 2
+    const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(cp - mis);  // covers [cp-2, cp+14) at worst
+    q[i][0] = v.x;
+    q[i][1] = v.y;
+    q[i][2] = v.z;
+    q[i][3] = v.w;
+    q[i][4] = load_u16(cp + 14);
+    hs[i] = load_u16(blk);
+    hc[i] = *reinterpret_cast<const int8_t*>(blk + 2 + (u & 7));
+  }
+
+  uint16_t* xs = reinterpret_cast<uint16_t*>(xs4);
+#pragma unroll
+  for (int i = 0; i < kPer; i++) {
+    const int c = static_cast<int>(threadIdx.x) + i * kThreads;
+    if (kPieces % kThreads == 0 || c < kPieces) {
+      const int sb = c / (NT * 32), rem = c % (NT * 32);
+      // entries 8cc..8cc+7 of sub-block j go to the k-group slots 32j + 8g (+4)
+      const int j = (rem & 31) >> 2, cc = rem & 3;
+      const int g0 = 2 * (cc & 1), half = cc >> 1;
+      uint16_t* row = xs + (sb * NT + (rem >> 5)) * kLdsRow + 32 * j + 4 * half;
+      *reinterpret_cast<uint2*>(row + 8 * g0) = make_uint2(xv[i].x, xv[i].y);
+      *reinterpret_cast<uint2*>(row + 8 * (g0 + 1)) = make_uint2(xv[i].z, xv[i].w);
+    }
+  }
+  uint8_t* cs = reinterpret_cast<uint8_t*>(cs4);
+#pragma unroll
+  for (int i = 0; i < kUPT; i++) {
+    const int U = static_cast<int>(threadIdx.x) + i * kThreads;
+    const int r = U / UR, u = U % UR;
+    const int64_t m = m0 + r < M ? m0 + r : M - 1;
+    const uint8_t* cp = W + m * rowbytes + 138 * (b0 + min(u >> 3, nb - 1)) + 10 + 16 * (u & 7);
+    const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(cp) & 3u);
+    *reinterpret_cast<uint4*>(cs + r * kCodeRow + 16 * u) =
+        make_uint4(__builtin_amdgcn_alignbyte(q[i][1], q[i][0], a), __builtin_amdgcn_alignbyte(q[i][2], q[i][1], a),
+                   __builtin_amdgcn_alignbyte(q[i][3], q[i][2], a), __builtin_amdgcn_alignbyte(q[i][4], q[i][3], a));
+    scs[r * kScRow + u] = (f16_bits_to_f32(hs[i]) * 16.0f) * static_cast<float>(hc[i]);
+  }
+  __syncthreads();
+
+  float4_t acc[R16][T16];
+#pragma unroll
+  for (int tm = 0; tm < R16; tm++)
+#pragma unroll
+    for (int tn = 0; tn < T16; tn++) acc[tm][tn] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+
+#pragma unroll
+  for (int sb = 0; sb < NSB; sb++) {
+    if (sb >= nb) break;
+    const uint16_t* xb = xs + sb * NT * kLdsRow;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int u = 8 * sb + j;
+      bf16x8v_t Bop[R16];
+      float sc[R16];
+#pragma unroll
+      for (int tm = 0; tm < R16; tm++) {
+        const int rl = wave * 16 * R16 + 16 * tm + l16;
+        Bop[tm] = decode_codes(*reinterpret_cast<const uint32_t*>(cs + rl * kCodeRow + 16 * u + 4 * g));
+        sc[tm] = scs[rl * kScRow + u];
+      }
+#pragma unroll
+      for (int tn = 0; tn < T16; tn++) {
+        const bf16x8v_t Aop = *reinterpret_cast<const bf16x8v_t*>(xb + (16 * tn + l16) * kLdsRow + 32 * j + 8 * g);
+#pragma unroll
+        for (int tm = 0; tm < R16; tm++) {
+          const float4_t P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aop, Bop[tm], zero, 0, 0, 0);
+          float4_t& A = acc[tm][tn];
+          A.x = __builtin_fmaf(sc[tm], P.x, A.x);
+          A.y = __builtin_fmaf(sc[tm], P.y, A.y);
+          A.z = __builtin_fmaf(sc[tm], P.z, A.z);
+          A.w = __builtin_fmaf(sc[tm], P.w, A.w);
+        }
+      }
+#pragma unroll
+      for (int tm = 0; tm < R16; tm++)
+#pragma unroll
+        for (int tn = 0; tn < T16; tn++)
+          asm volatile("" : "+v"(acc[tm][tn].x), "+v"(acc[tm][tn].y), "+v"(acc[tm][tn].z), "+v"(acc[tm][tn].w));
+    }
+  }
+
+#pragma unroll
+  for (int tm = 0; tm < R16; tm++) {
+    const int64_t m = m0 + wave * 16 * R16 + 16 * tm + l16;
+    if (m >= M) continue;
+#pragma unroll
+    for (int tn = 0; tn < T16; tn++) {
+      const float v[4] = {acc[tm][tn].x, acc[tm][tn].y, acc[tm][tn].z, acc[tm][tn].w};
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const int n = n0 + 16 * tn + 4 * g + r;
+        if (n < N) {
+          float* dst = Y + static_cast<int64_t>(n) * M + m;
+          if constexpr (SPLIT) atomicAdd(dst, v[r]);
+          else *dst = v[r];
+        }
+      }
+    }
+  }
+}
+
+template <int R16, int T16, int NSB>
+hipError_t launch_u(const void* blocks, int64_t m, int64_t k, const void* x, int64_t n, float* y,
+                    hipStream_t s) {
+  const unsigned gx = static_cast<unsigned>((m + 64 * R16 - 1) / (64 * R16));
+  const unsigned gy = static_cast<unsigned>((n + 16 * T16 - 1) / (16 * T16));
+  const int nsb = static_cast<int>(k / 256);
+  const unsigned gz = static_cast<unsigned>((nsb + NSB - 1) / NSB);
+  if (gz > 1) {
+    const hipError_t e = launch_fill_zero(y, m * n, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_gemm_sb4_u<R16, T16, NSB, true>), dim3(gx, gy, gz), dim3(kThreads), 0, s,
+                       static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
+                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(n));
+  } else {
+    hipLaunchKernelGGL((k_gemm_sb4_u<R16, T16, NSB, false>), dim3(gx, gy, 1), dim3(kThreads), 0, s,
+                       static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
+                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(n));
+  }
+  return hipGetLastError();
+}
+
 template <int R16, int T16, int NSB>
 hipError_t launch_s(const void* blocks, int64_t m, int64_t k, const void* x, int64_t n, float* y,
                     hipStream_t s) {
@@ -1017,7 +1203,9 @@ hipError_t launch_gemm(int fmt, const void* blocks, int64_t m, int64_t k, const 
                        int64_t n, float* y, hipStream_t s) {
   (void)xt;  // only BF16 activations reach this point
   if (fmt == QBLK_SB4) {
-    if (n <= 16) return launch_s<2, 1, 2>(blocks, m, k, x, n, y, s);
+    // (a sweep at 14336 x 4096, N = 16: 15.6 us for the unit-loaded kernel
+    // with 64-row tiles, 20.7 us for k_gemm_sb4_s; at N = 32 the latter wins)
+    if (n <= 16) return launch_u<1, 1, 2>(blocks, m, k, x, n, y, s);
     if (n <= 32) return launch_s<2, 2, 2>(blocks, m, k, x, n, y, s);
     if (n <= 64) return launch_t<QBLK_SB4, 2, 4>(blocks, m, k, x, n, y, s);
     return launch_w<QBLK_SB4, 4>(blocks, m, k, x, n, y, s);
