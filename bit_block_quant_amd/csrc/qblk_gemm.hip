@@ -991,30 +991,142 @@ hipError_t launch_w(const void* blocks, int64_t m, int64_t k, const void* x, int
 }
 
 // ---------------------------------------------------------------------------
-// Few tokens, Type 0, weights loaded by whole 16-byte code units.
+// Few tokens, weights loaded by whole 16-byte code units (all formats).
 //
 // Loading the codes directly in matrix-operand order (a dword per lane and
 // sub-block, lanes spread over 16 rows) asks for every cache line of a
 // super-block about eight times.  Here the workgroup's tile -- 64*R16 rows
-// by NSB super-blocks -- is fetched as the batch-1 GEMV fetches it: each lane
-// takes whole sub-blocks (16 code bytes, dword-aligned from just below plus
-// the 2 bytes that spill past, and the two header fields), consecutive lanes
-// consecutive sub-blocks of a row.  The codes are written to LDS realigned,
-// one 16-byte slot per (row, sub-block) with rows padded to 16 slots + 16
-// bytes, and the fp32 scale 16*S*sc_j beside them; the matrix ops then read a
-// dword per lane from LDS (16 rows x 4 k-groups: 64 different banks).  As in
-// k_gemm_sb4_s every load of the workgroup is issued before the single
-// barrier, and the K range is split over the grid.
+// by NSB 256-weight groups -- is fetched as the batch-1 GEMV fetches it: each
+// lane takes whole 32-weight units (16 code bytes and the unit's header
+// fields), consecutive lanes consecutive units of a row.  The codes are
+// written to LDS realigned, one 16-byte slot per (row, unit) and 16 bytes
+// of padding per row, with the unit's fp32 scale (times 16: the codes
+// decode to (code-8)/16) and, for the affine formats, its offset term
+// 8*s + a beside them; the matrix ops then read a dword per lane from LDS
+// (16 rows x 4 k-groups: 64 different banks).  Every load of the workgroup
+// is issued before the single barrier, and the K range is split over the
+// grid.  The affine formats add sum_j (8 s_j + a_j) * sum(x over sub-block j)
+// per group with two fp32 16x16x4 matrix ops, as k_gemm_t does.
 // ---------------------------------------------------------------------------
-template <int R16, int T16, int NSB, bool SPLIT>
-__global__ __launch_bounds__(kThreads) void k_gemm_sb4_u(const uint8_t* __restrict__ W,
-                                                       const uint16_t* __restrict__ X,
-                                                       float* __restrict__ Y, int M, int K, int N) {
+
+// One 32-weight unit: raw loads, then code dwords, scale*16 and offset term.
+template <int FMT>
+struct UnitU;
+
+template <>
+struct UnitU<QBLK_SB4> {
+  static constexpr int GB = 138;  // bytes per 256-weight group
+  static constexpr int RAW = 7;
+  // g: the group's first byte, j: the unit in the group
+  static __device__ __forceinline__ void load(const uint8_t* g, int j, uint32_t raw[RAW]) {
+    const uint8_t* cp = g + 10 + 16 * j;
+    const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(cp) & 3u);  // 0 or 2
+    const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(cp - mis);  // inside the group
+    raw[0] = v.x;
+    raw[1] = v.y;
+    raw[2] = v.z;
+    raw[3] = v.w;
+    raw[4] = load_u16(cp + 14);
+    raw[5] = load_u16(g);
+    raw[6] = static_cast<uint32_t>(*reinterpret_cast<const int8_t*>(g + 2 + j));
+  }
+  static __device__ __forceinline__ void finish(const uint8_t* g, int j, const uint32_t raw[RAW], uint4& c,
+                                                float& scale, float& corr) {
+    const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(g + 10 + 16 * j) & 3u);
+    c = make_uint4(__builtin_amdgcn_alignbyte(raw[1], raw[0], a), __builtin_amdgcn_alignbyte(raw[2], raw[1], a),
+                   __builtin_amdgcn_alignbyte(raw[3], raw[2], a), __builtin_amdgcn_alignbyte(raw[4], raw[3], a));
+    scale = (f16_bits_to_f32(raw[5]) * 16.0f) * static_cast<float>(static_cast<int32_t>(raw[6]));
+    corr = 0.0f;
+  }
+};
+
+template <>
+struct UnitU<QBLK_Q4_0> {
+  static constexpr int GB = 144;  // eight 18-byte blocks
+  static constexpr int RAW = 6;
+  static __device__ __forceinline__ void load(const uint8_t* g, int j, uint32_t raw[RAW]) {
+    const uint8_t* blk = g + 18 * j;
+    const uint8_t* cp = blk + 2;
+    const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(cp) & 3u);  // 0 or 2
+    const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(cp - mis);  // starts at blk or blk + 2
+    raw[0] = v.x;
+    raw[1] = v.y;
+    raw[2] = v.z;
+    raw[3] = v.w;
+    raw[4] = load_u16(cp + 14);
+    raw[5] = load_u16(blk);
+  }
+  static __device__ __forceinline__ void finish(const uint8_t* g, int j, const uint32_t raw[RAW], uint4& c,
+                                                float& scale, float& corr) {
+    const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(g + 18 * j + 2) & 3u);
+    c = make_uint4(__builtin_amdgcn_alignbyte(raw[1], raw[0], a), __builtin_amdgcn_alignbyte(raw[2], raw[1], a),
+                   __builtin_amdgcn_alignbyte(raw[3], raw[2], a), __builtin_amdgcn_alignbyte(raw[4], raw[3], a));
+    scale = f16_bits_to_f32(raw[5]) * 16.0f;
+    corr = 0.0f;
+  }
+};
+
+template <>
+struct UnitU<QBLK_SB4_AFFINE> {
+  static constexpr int GB = 148;  // dword aligned
+  static constexpr int RAW = 7;
+  static __device__ __forceinline__ void load(const uint8_t* g, int j, uint32_t raw[RAW]) {
+    const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(g + 20 + 16 * j);
+    raw[0] = v.x;
+    raw[1] = v.y;
+    raw[2] = v.z;
+    raw[3] = v.w;
+    raw[4] = *reinterpret_cast<const uint32_t*>(g);  // Ss | Sa << 16
+    raw[5] = static_cast<uint32_t>(*reinterpret_cast<const int8_t*>(g + 4 + j));
+    raw[6] = static_cast<uint32_t>(*reinterpret_cast<const int8_t*>(g + 12 + j));
+  }
+  static __device__ __forceinline__ void finish(const uint8_t*, int, const uint32_t raw[RAW], uint4& c,
+                                                float& scale, float& corr) {
+    c = make_uint4(raw[0], raw[1], raw[2], raw[3]);
+    const float s = f16_bits_to_f32(raw[4] & 0xffffu) * static_cast<float>(static_cast<int32_t>(raw[5]));
+    const float o = f16_bits_to_f32(raw[4] >> 16) * static_cast<float>(static_cast<int32_t>(raw[6]));
+    scale = s * 16.0f;
+    corr = __builtin_fmaf(8.0f, s, o);  // w = s*n + o = s*(n-8) + (8s + o)
+  }
+};
+
+template <>
+struct UnitU<QBLK_Q4_K> {
+  static constexpr int GB = 144;  // 16-byte aligned
+  static constexpr int RAW = 8;
+  static __device__ __forceinline__ void load(const uint8_t* g, int j, uint32_t raw[RAW]) {
+    const uint4 h = *reinterpret_cast<const uint4*>(g);
+    const uint4 v = *reinterpret_cast<const uint4*>(g + 16 + 16 * j);
+    raw[0] = v.x;
+    raw[1] = v.y;
+    raw[2] = v.z;
+    raw[3] = v.w;
+    raw[4] = h.x;
+    raw[5] = h.y;
+    raw[6] = h.z;
+    raw[7] = h.w;
+  }
+  static __device__ __forceinline__ void finish(const uint8_t*, int j, const uint32_t raw[RAW], uint4& c,
+                                                float& scale, float& corr) {
+    c = make_uint4(raw[0], raw[1], raw[2], raw[3]);
+    const float s = f16_bits_to_f32(raw[4] & 0xffffu) * static_cast<float>(q4k_scale6(raw[5], raw[6], j));
+    const float mn = f16_bits_to_f32(raw[4] >> 16) * static_cast<float>(q4k_min6(raw[6], raw[7], j));
+    scale = s * 16.0f;
+    corr = __builtin_fmaf(8.0f, s, -mn);  // w = s*n - mn = s*(n-8) + (8s - mn)
+  }
+};
+
+template <int FMT, int R16, int T16, int NSB, bool SPLIT>
+__global__ __launch_bounds__(kThreads) void k_gemm_u(const uint8_t* __restrict__ W,
+                                                   const uint16_t* __restrict__ X,
+                                                   float* __restrict__ Y, int M, int K, int N) {
+  using UU = UnitU<FMT>;
+  constexpr bool AFFINE = FMT == QBLK_SB4_AFFINE || FMT == QBLK_Q4_K;
   constexpr int NT = 16 * T16;
   constexpr int RW = 64 * R16;             // weight rows per workgroup
-  constexpr int UR = NSB * 8;              // sub-blocks per row in the K slice
-  constexpr int kUPT = RW * UR / kThreads; // sub-blocks per thread
-  static_assert(RW * UR % kThreads == 0, "whole sub-blocks per thread");
+  constexpr int UR = NSB * 8;              // units per row in the K slice
+  constexpr int kUPT = RW * UR / kThreads; // units per thread
+  static_assert(RW * UR % kThreads == 0, "whole units per thread");
   constexpr int kCodeRow = UR * 16 + 16;   // bytes per staged row of codes
   constexpr int kScRow = UR + 1;           // floats per staged row of scales
   constexpr int kPieces = NSB * NT * 32;   // 16-byte pieces of the X slice
@@ -1022,18 +1134,20 @@ __global__ __launch_bounds__(kThreads) void k_gemm_sb4_u(const uint8_t* __restri
   __shared__ uint4 xs4[NSB * NT * kLdsRow / 8];
   __shared__ uint4 cs4[RW * kCodeRow / 16];
   __shared__ float scs[RW * kScRow];
+  __shared__ float cos_[AFFINE ? RW * kScRow : 1];   // offset terms 8s + a
+  __shared__ float xsum[AFFINE ? NSB * NT * 8 : 1];  // [group][token][sub-block]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * RW;
   const int n0 = blockIdx.y * NT;
-  const int nsb = K / 256;
+  const int ngr = K / 256;
   const int b0 = blockIdx.z * NSB;
-  const int nb = min(NSB, nsb - b0);  // super-blocks in this piece of K (>= 1)
-  const int64_t rowbytes = static_cast<int64_t>(nsb) * 138;
+  const int nb = min(NSB, ngr - b0);  // groups in this piece of K (>= 1)
+  const int64_t rowbytes = static_cast<int64_t>(ngr) * UU::GB;
 
-  // X first (L2-resident), then every sub-block of the tile.  Pieces past the
-  // slice's last super-block or past row M-1 / token N-1 re-read valid data
-  // that is never used or never stored.
+  // X first (L2-resident), then every unit of the tile.  Pieces past the
+  // slice's last group or past row M-1 / token N-1 re-read valid data that is
+  // never used or never stored.
   uint4 xv[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; i++) {
@@ -1043,38 +1157,40 @@ __global__ __launch_bounds__(kThreads) void k_gemm_sb4_u(const uint8_t* __restri
     const int b = b0 + min(sb, nb - 1);
     xv[i] = *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(t) * K + 256 * b + 8 * col);
   }
-  uint32_t q[kUPT][5], hs[kUPT];
-  int hc[kUPT];
+  uint32_t raw[kUPT][UU::RAW];
 #pragma unroll
   for (int i = 0; i < kUPT; i++) {
     const int U = static_cast<int>(threadIdx.x) + i * kThreads;
     const int r = U / UR, u = U % UR;
     const int64_t m = m0 + r < M ? m0 + r : M - 1;
-    const uint8_t* blk = W + m * rowbytes + 138 * (b0 + min(u >> 3, nb - 1));
-    const uint8_t* cp = blk + 10 + 16 * (u & 7);
-    const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(cp) & 3u);  // 0 or 2
-    const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(cp - mis);  // covers [cp-2, cp+14) at worst
-    q[i][0] = v.x;
-    q[i][1] = v.y;
-    q[i][2] = v.z;
-    q[i][3] = v.w;
-    q[i][4] = load_u16(cp + 14);
-    hs[i] = load_u16(blk);
-    hc[i] = *reinterpret_cast<const int8_t*>(blk + 2 + (u & 7));
+    UU::load(W + m * rowbytes + static_cast<int64_t>(UU::GB) * (b0 + min(u >> 3, nb - 1)), u & 7, raw[i]);
   }
 
   uint16_t* xs = reinterpret_cast<uint16_t*>(xs4);
 #pragma unroll
   for (int i = 0; i < kPer; i++) {
     const int c = static_cast<int>(threadIdx.x) + i * kThreads;
+    const int sb = c / (NT * 32), rem = c % (NT * 32);
     if (kPieces % kThreads == 0 || c < kPieces) {
-      const int sb = c / (NT * 32), rem = c % (NT * 32);
       // entries 8cc..8cc+7 of sub-block j go to the k-group slots 32j + 8g (+4)
       const int j = (rem & 31) >> 2, cc = rem & 3;
       const int g0 = 2 * (cc & 1), half = cc >> 1;
       uint16_t* row = xs + (sb * NT + (rem >> 5)) * kLdsRow + 32 * j + 4 * half;
       *reinterpret_cast<uint2*>(row + 8 * g0) = make_uint2(xv[i].x, xv[i].y);
       *reinterpret_cast<uint2*>(row + 8 * (g0 + 1)) = make_uint2(xv[i].z, xv[i].w);
+    }
+    if constexpr (AFFINE) {
+      // sum of x over the sub-block: products with 1.0 are exact, fp32 sums;
+      // the 4 pieces of a sub-block sit on 4 adjacent lanes
+      const bf16x2v_t one = __builtin_bit_cast(bf16x2v_t, 0x3f803f80u);
+      float part = 0.0f;
+      part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].x), one, part, false);
+      part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].y), one, part, false);
+      part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].z), one, part, false);
+      part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].w), one, part, false);
+      part = quad_sum(part);
+      if ((kPieces % kThreads == 0 || c < kPieces) && (c & 3) == 0)
+        xsum[(sb * NT + (rem >> 5)) * 8 + ((rem & 31) >> 2)] = part;
     }
   }
   uint8_t* cs = reinterpret_cast<uint8_t*>(cs4);
@@ -1083,12 +1199,13 @@ __global__ __launch_bounds__(kThreads) void k_gemm_sb4_u(const uint8_t* __restri
     const int U = static_cast<int>(threadIdx.x) + i * kThreads;
     const int r = U / UR, u = U % UR;
     const int64_t m = m0 + r < M ? m0 + r : M - 1;
-    const uint8_t* cp = W + m * rowbytes + 138 * (b0 + min(u >> 3, nb - 1)) + 10 + 16 * (u & 7);
-    const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(cp) & 3u);
-    *reinterpret_cast<uint4*>(cs + r * kCodeRow + 16 * u) =
-        make_uint4(__builtin_amdgcn_alignbyte(q[i][1], q[i][0], a), __builtin_amdgcn_alignbyte(q[i][2], q[i][1], a),
-                   __builtin_amdgcn_alignbyte(q[i][3], q[i][2], a), __builtin_amdgcn_alignbyte(q[i][4], q[i][3], a));
-    scs[r * kScRow + u] = (f16_bits_to_f32(hs[i]) * 16.0f) * static_cast<float>(hc[i]);
+    uint4 c;
+    float scale, corr;
+    UU::finish(W + m * rowbytes + static_cast<int64_t>(UU::GB) * (b0 + min(u >> 3, nb - 1)), u & 7, raw[i], c,
+               scale, corr);
+    *reinterpret_cast<uint4*>(cs + r * kCodeRow + 16 * u) = c;
+    scs[r * kScRow + u] = scale;
+    if constexpr (AFFINE) cos_[r * kScRow + u] = corr;
   }
   __syncthreads();
 
@@ -1133,6 +1250,19 @@ __global__ __launch_bounds__(kThreads) void k_gemm_sb4_u(const uint8_t* __restri
         for (int tn = 0; tn < T16; tn++)
           asm volatile("" : "+v"(acc[tm][tn].x), "+v"(acc[tm][tn].y), "+v"(acc[tm][tn].z), "+v"(acc[tm][tn].w));
     }
+    if constexpr (AFFINE) {
+      // A = sum(x) [token][sub-block 4q + g], B = (8 s + a) [sub-block 4q + g][row]
+#pragma unroll
+      for (int tn = 0; tn < T16; tn++) {
+        const float* xq = xsum + (sb * NT + 16 * tn + l16) * 8 + g;
+#pragma unroll
+        for (int tm = 0; tm < R16; tm++) {
+          const float* co = cos_ + (wave * 16 * R16 + 16 * tm + l16) * kScRow + 8 * sb + g;
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[0], co[0], acc[tm][tn], 0, 0, 0);
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[4], co[4], acc[tm][tn], 0, 0, 0);
+        }
+      }
+    }
   }
 
 #pragma unroll
@@ -1155,7 +1285,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_sb4_u(const uint8_t* __restri
   }
 }
 
-template <int R16, int T16, int NSB>
+template <int FMT, int R16, int T16, int NSB>
 hipError_t launch_u(const void* blocks, int64_t m, int64_t k, const void* x, int64_t n, float* y,
                     hipStream_t s) {
   const unsigned gx = static_cast<unsigned>((m + 64 * R16 - 1) / (64 * R16));
@@ -1165,11 +1295,11 @@ hipError_t launch_u(const void* blocks, int64_t m, int64_t k, const void* x, int
   if (gz > 1) {
     const hipError_t e = launch_fill_zero(y, m * n, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_gemm_sb4_u<R16, T16, NSB, true>), dim3(gx, gy, gz), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((k_gemm_u<FMT, R16, T16, NSB, true>), dim3(gx, gy, gz), dim3(kThreads), 0, s,
                        static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
                        static_cast<int>(m), static_cast<int>(k), static_cast<int>(n));
   } else {
-    hipLaunchKernelGGL((k_gemm_sb4_u<R16, T16, NSB, false>), dim3(gx, gy, 1), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((k_gemm_u<FMT, R16, T16, NSB, false>), dim3(gx, gy, 1), dim3(kThreads), 0, s,
                        static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
                        static_cast<int>(m), static_cast<int>(k), static_cast<int>(n));
   }
@@ -1202,27 +1332,31 @@ hipError_t launch_s(const void* blocks, int64_t m, int64_t k, const void* x, int
 hipError_t launch_gemm(int fmt, const void* blocks, int64_t m, int64_t k, const void* x, int xt,
                        int64_t n, float* y, hipStream_t s) {
   (void)xt;  // only BF16 activations reach this point
+  // (sweeps at 14336 x 4096: up to 16 tokens the unit-loaded kernel with
+  // 64-row tiles takes 15.8-16.9 us for every format, against 20.7-34.7 us
+  // for the per-lane-loaded kernels; at 32 tokens it wins only for Q4_0,
+  // 26 us against 37, and k_gemm_sb4_s is best for Type 0, 24 us)
+  if (n <= 16) {
+    if (fmt == QBLK_SB4) return launch_u<QBLK_SB4, 1, 1, 2>(blocks, m, k, x, n, y, s);
+    if (fmt == QBLK_Q4_0) return launch_u<QBLK_Q4_0, 1, 1, 2>(blocks, m, k, x, n, y, s);
+    if (fmt == QBLK_Q4_K) return launch_u<QBLK_Q4_K, 1, 1, 2>(blocks, m, k, x, n, y, s);
+    return launch_u<QBLK_SB4_AFFINE, 1, 1, 2>(blocks, m, k, x, n, y, s);
+  }
   if (fmt == QBLK_SB4) {
-    // (a sweep at 14336 x 4096, N = 16: 15.6 us for the unit-loaded kernel
-    // with 64-row tiles, 20.7 us for k_gemm_sb4_s; at N = 32 the latter wins)
-    if (n <= 16) return launch_u<1, 1, 2>(blocks, m, k, x, n, y, s);
     if (n <= 32) return launch_s<2, 2, 2>(blocks, m, k, x, n, y, s);
     if (n <= 64) return launch_t<QBLK_SB4, 2, 4>(blocks, m, k, x, n, y, s);
     return launch_w<QBLK_SB4, 4>(blocks, m, k, x, n, y, s);
   }
   if (fmt == QBLK_Q4_0) {
-    if (n <= 16) return launch_t<QBLK_Q4_0, 1, 1>(blocks, m, k, x, n, y, s);
-    if (n <= 32) return launch_t<QBLK_Q4_0, 1, 2>(blocks, m, k, x, n, y, s);
+    if (n <= 32) return launch_u<QBLK_Q4_0, 1, 2, 2>(blocks, m, k, x, n, y, s);
     if (n <= 64) return launch_t<QBLK_Q4_0, 2, 4>(blocks, m, k, x, n, y, s);
     return launch_w<QBLK_Q4_0, 4>(blocks, m, k, x, n, y, s);
   }
   if (fmt == QBLK_Q4_K) {
-    if (n <= 16) return launch_t<QBLK_Q4_K, 1, 1>(blocks, m, k, x, n, y, s);
     if (n <= 32) return launch_t<QBLK_Q4_K, 1, 2>(blocks, m, k, x, n, y, s);
     if (n <= 64) return launch_t<QBLK_Q4_K, 2, 4>(blocks, m, k, x, n, y, s);
     return launch_w<QBLK_Q4_K, 4>(blocks, m, k, x, n, y, s);
   }
-  if (n <= 16) return launch_t<QBLK_SB4_AFFINE, 1, 1>(blocks, m, k, x, n, y, s);
   if (n <= 32) return launch_t<QBLK_SB4_AFFINE, 1, 2>(blocks, m, k, x, n, y, s);
   if (n <= 64) return launch_t<QBLK_SB4_AFFINE, 2, 4>(blocks, m, k, x, n, y, s);
   return launch_w<QBLK_SB4_AFFINE, 4>(blocks, m, k, x, n, y, s);

@@ -313,7 +313,7 @@ def gemm_fmt(q, name):
 
 
 @pytest.mark.parametrize("fmt", ["q4_0", "sb4a", "q4k"])
-@pytest.mark.parametrize("n", [1, 16, 24, 40, 64, 100])
+@pytest.mark.parametrize("n", [1, 5, 16, 24, 32, 40, 64, 100])
 def test_gemm_other_formats(q, fmt, n):
     # Q4_0 (scale per 32-block), Type 1 and Q4_K (scale and offset per sub-block)
     m, k = 150, 2304
