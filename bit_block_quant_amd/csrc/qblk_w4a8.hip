@@ -148,180 +148,181 @@ __global__ __launch_bounds__(kWavesV * kWave) void k_gemv_w4a8(const uint8_t* __
 }
 
 // ===================================================================
-// Several tokens: v_mfma_i32_16x16x64_i8.
+// Up to 16 tokens: v_mfma_i32_16x16x64_i8, weights loaded by whole units.
 //
 // Operand layout: lane l holds row (l % 16) of A and column (l % 16) of B,
 // each with 16 int8 k values of its lane group (l / 16); lane l receives
 // D[4*(l/16) + r][l % 16], r = 0..3.  Only A and B sharing the k assignment
 // matters: for step s (0, 1) of a 128-weight group, lane group g takes code
-// bytes j0..j0+7, j0 = 8*(4s + g): weights j0..j0+7 (low nibbles) and
-// 64+j0..64+j0+7 (high nibbles), and the same 16 activations.  A = X (tokens),
-// B = W^T (weight rows), so a lane's four outputs share one weight row and
-// one scale per group.  The integer accumulator of a group starts at
-// -8 * sum(xq) of its token over the group (staged with X).
+// bytes j0..j0+7, j0 = 16g + 8s -- weights j0..j0+7 (low nibbles) and
+// 64+j0..64+j0+7 (high nibbles) -- and the same 16 activations.  A = X
+// (tokens), B = W^T (weight rows), so a lane's four outputs share one weight
+// row and one scale per group.  The integer accumulator of a group starts at
+// -8 * sum(xq) of its token over the group.
 //
-// A workgroup of 4 waves owns 64*TM weight rows (16*TM per wave) and 16*TN
-// tokens.  X is staged one group (128 k) at a time in LDS, double-buffered:
-// token row = 8 pieces of 16 bytes in operand order (piece 4s+g = the 16
-// activations above), rows 144 bytes apart so 8 lanes reading one piece of 8
-// consecutive tokens hit distinct banks.  When the M x N tiling leaves too
-// few workgroups, the groups are split over a third grid dimension and the
-// partial products are added into Y (zeroed first).
+// Loading B straight from the code plane (16 rows per instruction) would ask
+// for each cache line several times.  Instead a workgroup's tile -- 64 rows
+// by NG groups -- is fetched as plain rows: lane after lane takes consecutive
+// 16-byte units of a row (a group's 64 code bytes are 4 units), and the units
+// go unchanged to LDS, each row padded by 16 bytes; with the contiguous k
+// assignment above, one 16-byte LDS read per row and group feeds both steps
+// (16 rows of a read phase: row stride = 4 mod 64 dwords, 64 different
+// banks).  X is staged per group and token as 8 pieces of 16 bytes (piece p:
+// activations 8p..8p+7 and 64+8p..64+8p+7), token rows 144 bytes apart, and
+// a lane reads its pieces 2g and 2g+1.  KW waves share each 16 rows, each
+// taking NG/KW of the groups, and add their sums in LDS at the end.  Every
+// load is issued before the single barrier; the K range is split over the
+// grid and the partial products are added into Y (zeroed first).
 // ===================================================================
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kThreadsM = 256;
 constexpr int kXRow = 144;  // bytes per staged token row
 
-template <int TM, int TN, bool SPLIT>
-__global__ __launch_bounds__(kThreadsM) void k_gemm_w4a8(const uint8_t* __restrict__ codes,
-                                                         const uint16_t* __restrict__ scales,
-                                                         const int8_t* __restrict__ xq,
-                                                         const float* __restrict__ xs,
-                                                         float* __restrict__ Y, int M, int K, int N,
-                                                         int groups_per_split) {
-  constexpr int NT = 16 * TN;
-  constexpr int XCH = NT * 8;                                  // 16-byte X chunks per stage
-  constexpr int XPT = (XCH + kThreadsM - 1) / kThreadsM;       // per thread
-  __shared__ uint4 xs4[2][NT * kXRow / 16];
-  __shared__ i32x4_t xcor4[2][NT / 4];                         // -8 * sum(xq) per token
-  int* const xcor0 = reinterpret_cast<int*>(xcor4[0]);
-  int* const xcor1 = reinterpret_cast<int*>(xcor4[1]);
+template <int NG, int KW, bool SPLIT>
+__global__ __launch_bounds__(kThreadsM * KW) void k_gemm_w4a8_u(const uint8_t* __restrict__ codes,
+                                                           const uint16_t* __restrict__ scales,
+                                                           const int8_t* __restrict__ xq,
+                                                           const float* __restrict__ xs,
+                                                           float* __restrict__ Y, int M, int K, int N) {
+  constexpr int kT = kThreadsM * KW;             // KW waves per 16 rows, each a share of the groups
+  constexpr int UR = 4 * NG;                      // units per row in the slice
+  constexpr int kUPT = 64 * UR / kT;              // units per thread
+  static_assert(64 * UR % kT == 0 && NG % KW == 0, "whole units per thread, whole groups per wave");
+  constexpr int kCodeRow = 16 * UR + 16;          // bytes per staged code row
+  constexpr int kPieces = NG * 16 * 8;            // 16-byte pieces of the X slice
+  constexpr int kPer = (kPieces + kT - 1) / kT;
+  constexpr int kSc = 64 * NG;                    // scales of the tile
+  __shared__ uint4 xs4[NG * 16 * kXRow / 16];
+  __shared__ uint4 cs4[64 * kCodeRow / 16];
+  __shared__ float scs[kSc];
+  __shared__ i32x4_t xcor4[NG * 4];               // -8 * sum(xq) per group and token
+  __shared__ float4_t red[KW > 1 ? (KW - 1) * 4 * 64 : 1];
+  int* const xcor = reinterpret_cast<int*>(xcor4);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int NG = K >> 7;
+  const int ngr = K >> 7;
   const int64_t rowbytes = K >> 1;
-  const int64_t mw = static_cast<int64_t>(blockIdx.x) * 64 * TM + wave * 16 * TM;
-  const int n0 = blockIdx.y * NT;
-  const int g_begin = SPLIT ? blockIdx.z * groups_per_split : 0;
-  const int g_end = SPLIT ? min(NG, g_begin + groups_per_split) : NG;
-  int64_t rowi[TM];
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int n0 = blockIdx.y * 16;
+  const int b0 = blockIdx.z * NG;
+  const int nb = min(NG, ngr - b0);  // groups in this piece of K (>= 1)
+
+  // X first (L2-resident), then the units and scales of the tile.  Loads past
+  // the slice's last group or past row M-1 re-read valid data that is never
+  // used or never stored; tokens past N-1 read as zero.
+  uint4 xv[kPer];
 #pragma unroll
-  for (int tm = 0; tm < TM; tm++) {
-    const int64_t m = mw + 16 * tm + l16;
-    rowi[tm] = m < M ? m : M - 1;
+  for (int i = 0; i < kPer; i++) {
+    const int c = min(static_cast<int>(threadIdx.x) + i * kT, kPieces - 1);
+    const int gi = c >> 7, tok = (c >> 3) & 15, cc = c & 7;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (n0 + tok < N)
+      v = *reinterpret_cast<const uint4*>(xq + static_cast<int64_t>(n0 + tok) * K + 128 * (b0 + min(gi, nb - 1)) +
+                                          16 * cc);
+    xv[i] = v;
+  }
+  uint4 cu[kUPT];
+#pragma unroll
+  for (int i = 0; i < kUPT; i++) {
+    const int U = static_cast<int>(threadIdx.x) + i * kT;
+    const int r = U / UR, u = U % UR;
+    const int64_t m = m0 + r < M ? m0 + r : M - 1;
+    cu[i] = *reinterpret_cast<const uint4*>(codes + m * rowbytes + 64 * static_cast<int64_t>(b0 + min(u >> 2, nb - 1)) +
+                                            16 * (u & 3));
+  }
+  uint32_t scv[(kSc + kT - 1) / kT];
+#pragma unroll
+  for (int i = 0; i < (kSc + kT - 1) / kT; i++) {
+    const int c = min(static_cast<int>(threadIdx.x) + i * kT, kSc - 1);
+    const int r = c / NG, gi = c % NG;
+    const int64_t m = m0 + r < M ? m0 + r : M - 1;
+    scv[i] = scales[m * ngr + b0 + min(gi, nb - 1)];
   }
 
-  auto load_x = [&](int G, uint4 xv[XPT]) {
+  uint8_t* xsb = reinterpret_cast<uint8_t*>(xs4);
 #pragma unroll
-    for (int i = 0; i < XPT; i++) {
-      const int c = threadIdx.x + i * kThreadsM;
-      const int tok = c >> 3, cc = c & 7;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (c < XCH && n0 + tok < N)
-        v = *reinterpret_cast<const uint4*>(xq + static_cast<int64_t>(n0 + tok) * K + 128 * G + 16 * cc);
-      xv[i] = v;
-    }
-  };
-  auto store_x = [&](int buf, const uint4 xv[XPT]) {
-    uint8_t* xsb = reinterpret_cast<uint8_t*>(xs4[buf]);
-#pragma unroll
-    for (int i = 0; i < XPT; i++) {
-      const int c = threadIdx.x + i * kThreadsM;
-      const int tok = c >> 3, cc = c & 7;
+  for (int i = 0; i < kPer; i++) {
+    const int c = static_cast<int>(threadIdx.x) + i * kT;
+    const int gi = c >> 7, tok = (c >> 3) & 15, cc = c & 7;
+    if (kPieces % kT == 0 || c < kPieces) {
       // activations 16cc..16cc+15 of the group: pieces 2(cc&3) and 2(cc&3)+1,
       // first halves (cc < 4) or second halves (cc >= 4)
-      if (c < XCH) {
-        uint8_t* row = xsb + tok * kXRow + 32 * (cc & 3) + 8 * (cc >> 2);
-        *reinterpret_cast<uint2*>(row) = make_uint2(xv[i].x, xv[i].y);
-        *reinterpret_cast<uint2*>(row + 16) = make_uint2(xv[i].z, xv[i].w);
-      }
-      int s = dot4(xv[i].x, kOnes8, 0);
-      s = dot4(xv[i].y, kOnes8, s);
-      s = dot4(xv[i].z, kOnes8, s);
-      s = dot4(xv[i].w, kOnes8, s);
-      // the 8 chunks of a token sit on 8 adjacent lanes
-      s += __shfl_xor(s, 1, kWave);
-      s += __shfl_xor(s, 2, kWave);
-      s += __shfl_xor(s, 4, kWave);
-      if (c < XCH && cc == 0) (buf ? xcor1 : xcor0)[tok] = -8 * s;
+      uint8_t* row = xsb + (gi * 16 + tok) * kXRow + 32 * (cc & 3) + 8 * (cc >> 2);
+      *reinterpret_cast<uint2*>(row) = make_uint2(xv[i].x, xv[i].y);
+      *reinterpret_cast<uint2*>(row + 16) = make_uint2(xv[i].z, xv[i].w);
     }
-  };
-  auto load_w = [&](int G, uint2 cw[TM][2], uint32_t sc[TM]) {
+    int sm = dot4(xv[i].x, kOnes8, 0);
+    sm = dot4(xv[i].y, kOnes8, sm);
+    sm = dot4(xv[i].z, kOnes8, sm);
+    sm = dot4(xv[i].w, kOnes8, sm);
+    // the 8 pieces of a token and group sit on 8 adjacent lanes
+    sm += __shfl_xor(sm, 1, kWave);
+    sm += __shfl_xor(sm, 2, kWave);
+    sm += __shfl_xor(sm, 4, kWave);
+    if ((kPieces % kT == 0 || c < kPieces) && cc == 0) xcor[gi * 16 + tok] = -8 * sm;
+  }
+  uint8_t* cs = reinterpret_cast<uint8_t*>(cs4);
 #pragma unroll
-    for (int tm = 0; tm < TM; tm++) {
-      const uint8_t* p = codes + rowi[tm] * rowbytes + 64 * G + 8 * g;
-      cw[tm][0] = *reinterpret_cast<const uint2*>(p);
-      cw[tm][1] = *reinterpret_cast<const uint2*>(p + 32);
-      sc[tm] = scales[rowi[tm] * NG + G];
-    }
-  };
+  for (int i = 0; i < kUPT; i++) {
+    const int U = static_cast<int>(threadIdx.x) + i * kT;
+    const int r = U / UR, u = U % UR;
+    *reinterpret_cast<uint4*>(cs + r * kCodeRow + 16 * u) = cu[i];
+  }
+#pragma unroll
+  for (int i = 0; i < (kSc + kT - 1) / kT; i++) {
+    const int c = static_cast<int>(threadIdx.x) + i * kT;
+    if (kSc % kT == 0 || c < kSc) scs[c] = f16_bits_to_f32(scv[i]);
+  }
+  __syncthreads();
 
-  float4_t acc[TM][TN];
+  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int rl = (wave & 3) * 16 + l16, kw = wave >> 2;
 #pragma unroll
-  for (int tm = 0; tm < TM; tm++)
-#pragma unroll
-    for (int tn = 0; tn < TN; tn++) acc[tm][tn] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-  uint4 xv[XPT];
-  uint2 cw[TM][2];
-  uint32_t sc[TM];
-  i32x4_t Bop[TM][2];
-  float dsc[TM];
-  auto decode = [&]() {
-#pragma unroll
-    for (int tm = 0; tm < TM; tm++) {
-#pragma unroll
-      for (int s = 0; s < 2; s++) {
-        const uint2 c = cw[tm][s];
-        Bop[tm][s] = i32x4_t{static_cast<int>(c.x & kLo4), static_cast<int>(c.y & kLo4),
-                             static_cast<int>((c.x >> 4) & kLo4), static_cast<int>((c.y >> 4) & kLo4)};
-      }
-      dsc[tm] = f16_bits_to_f32(sc[tm]);
-    }
-  };
-  if (g_begin < g_end) {
-    load_x(g_begin, xv);
-    load_w(g_begin, cw, sc);
-    store_x(0, xv);
-    decode();
+  for (int gq = 0; gq < NG / KW; gq++) {
+    const int gi = kw * (NG / KW) + gq;
+    if (gi >= nb) break;
+    const uint4 c = *reinterpret_cast<const uint4*>(cs + rl * kCodeRow + 64 * gi + 16 * g);
+    const i32x4_t B0 = {static_cast<int>(c.x & kLo4), static_cast<int>(c.y & kLo4),
+                        static_cast<int>((c.x >> 4) & kLo4), static_cast<int>((c.y >> 4) & kLo4)};
+    const i32x4_t B1 = {static_cast<int>(c.z & kLo4), static_cast<int>(c.w & kLo4),
+                        static_cast<int>((c.z >> 4) & kLo4), static_cast<int>((c.w >> 4) & kLo4)};
+    const uint8_t* xr = xsb + (gi * 16 + l16) * kXRow + 32 * g;
+    const i32x4_t A0 = *reinterpret_cast<const i32x4_t*>(xr);
+    const i32x4_t A1 = *reinterpret_cast<const i32x4_t*>(xr + 16);
+    const i32x4_t C0 = xcor4[gi * 4 + g];  // tokens 4g .. 4g+3
+    i32x4_t D = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, B0, C0, 0, 0, 0);
+    D = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, B1, D, 0, 0, 0);
+    const float d = scs[rl * NG + gi];
+    acc.x = __builtin_fmaf(d, static_cast<float>(D.x), acc.x);
+    acc.y = __builtin_fmaf(d, static_cast<float>(D.y), acc.y);
+    acc.z = __builtin_fmaf(d, static_cast<float>(D.z), acc.z);
+    acc.w = __builtin_fmaf(d, static_cast<float>(D.w), acc.w);
   }
 
-  for (int G = g_begin; G < g_end; G++) {
-    const int buf = (G - g_begin) & 1;
+  if constexpr (KW > 1) {
+    // the K shares of a row tile meet in LDS
+    if (kw > 0) red[((kw - 1) * 4 + (wave & 3)) * 64 + lane] = acc;
     __syncthreads();
-    const bool more = G + 1 < g_end;
-    if (more) {
-      load_x(G + 1, xv);
-      load_w(G + 1, cw, sc);
-    }
-    const uint8_t* xsb = reinterpret_cast<const uint8_t*>(xs4[buf]);
+    if (kw > 0) return;
 #pragma unroll
-    for (int tn = 0; tn < TN; tn++) {
-      const i32x4_t A0 = *reinterpret_cast<const i32x4_t*>(xsb + (16 * tn + l16) * kXRow + 16 * g);
-      const i32x4_t A1 = *reinterpret_cast<const i32x4_t*>(xsb + (16 * tn + l16) * kXRow + 16 * (4 + g));
-      const i32x4_t C0 = xcor4[buf][4 * tn + g];  // tokens 16tn + 4g .. +3
-#pragma unroll
-      for (int tm = 0; tm < TM; tm++) {
-        i32x4_t D = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, Bop[tm][0], C0, 0, 0, 0);
-        D = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, Bop[tm][1], D, 0, 0, 0);
-        float4_t& a = acc[tm][tn];
-        a.x = __builtin_fmaf(dsc[tm], static_cast<float>(D.x), a.x);
-        a.y = __builtin_fmaf(dsc[tm], static_cast<float>(D.y), a.y);
-        a.z = __builtin_fmaf(dsc[tm], static_cast<float>(D.z), a.z);
-        a.w = __builtin_fmaf(dsc[tm], static_cast<float>(D.w), a.w);
-      }
-    }
-    if (more) {
-      store_x(buf ^ 1, xv);
-      decode();
+    for (int q = 1; q < KW; q++) {
+      const float4_t o = red[((q - 1) * 4 + wave) * 64 + lane];
+      acc.x += o.x;
+      acc.y += o.y;
+      acc.z += o.z;
+      acc.w += o.w;
     }
   }
-
-#pragma unroll
-  for (int tn = 0; tn < TN; tn++) {
+  const int64_t m = m0 + rl;
+  if (m < M) {
+    const float v[4] = {acc.x, acc.y, acc.z, acc.w};
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-      const int n = n0 + 16 * tn + 4 * g + r;
-      if (n >= N) continue;
-      const float st = xs[n];
-#pragma unroll
-      for (int tm = 0; tm < TM; tm++) {
-        const int64_t m = mw + 16 * tm + l16;
-        if (m >= M) continue;
-        const float v = (r == 0 ? acc[tm][tn].x : r == 1 ? acc[tm][tn].y : r == 2 ? acc[tm][tn].z : acc[tm][tn].w) * st;
+      const int n = n0 + 4 * g + r;
+      if (n < N) {
         float* dst = Y + static_cast<int64_t>(n) * M + m;
-        if constexpr (SPLIT) atomicAdd(dst, v);
-        else *dst = v;
+        if constexpr (SPLIT) atomicAdd(dst, v[r] * xs[n]);
+        else *dst = v[r] * xs[n];
       }
     }
   }
@@ -550,26 +551,20 @@ hipError_t launch_v(const uint8_t* codes, const uint16_t* scales, int64_t m, int
   }
 }
 
-template <int TM, int TN>
-hipError_t launch_m(const uint8_t* codes, const uint16_t* scales, int64_t m, int64_t k, const int8_t* xq,
-                    const float* xs, int64_t n, float* y, hipStream_t s) {
-  const unsigned gx = static_cast<unsigned>((m + 64 * TM - 1) / (64 * TM));
-  const unsigned gy = static_cast<unsigned>((n + 16 * TN - 1) / (16 * TN));
-  const int ng = static_cast<int>(k / 128);
-  const int64_t tiles = static_cast<int64_t>(gx) * gy;
-  const int64_t want = 2 * static_cast<int64_t>(cu_count_w4());
-  if (tiles < want && ng > 1) {
-    int split = static_cast<int>((want + tiles - 1) / tiles);
-    split = split > ng ? ng : split;
-    const int per = (ng + split - 1) / split;
-    const unsigned gz = static_cast<unsigned>((ng + per - 1) / per);
+template <int NG, int KW>
+hipError_t launch_mu(const uint8_t* codes, const uint16_t* scales, int64_t m, int64_t k, const int8_t* xq,
+                     const float* xs, int64_t n, float* y, hipStream_t s) {
+  const unsigned gx = static_cast<unsigned>((m + 63) / 64);
+  const unsigned gy = static_cast<unsigned>((n + 15) / 16);
+  const unsigned gz = static_cast<unsigned>((k / 128 + NG - 1) / NG);
+  if (gz > 1) {
     const hipError_t e = launch_fill_zero(y, m * n, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_gemm_w4a8<TM, TN, true>), dim3(gx, gy, gz), dim3(kThreadsM), 0, s, codes, scales, xq, xs,
-                       y, static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), per);
+    hipLaunchKernelGGL((k_gemm_w4a8_u<NG, KW, true>), dim3(gx, gy, gz), dim3(kThreadsM * KW), 0, s, codes, scales, xq, xs, y,
+                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(n));
   } else {
-    hipLaunchKernelGGL((k_gemm_w4a8<TM, TN, false>), dim3(gx, gy, 1), dim3(kThreadsM), 0, s, codes, scales, xq, xs,
-                       y, static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), ng);
+    hipLaunchKernelGGL((k_gemm_w4a8_u<NG, KW, false>), dim3(gx, gy, 1), dim3(kThreadsM * KW), 0, s, codes, scales, xq, xs, y,
+                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(n));
   }
   return hipGetLastError();
 }
@@ -604,11 +599,14 @@ hipError_t launch_gemm_w4a8(const void* blocks, int64_t m, int64_t k, const int8
   const uint8_t* codes = static_cast<const uint8_t*>(blocks);
   const uint16_t* scales = reinterpret_cast<const uint16_t*>(codes + m * k / 2);
   if (n == 1 && k <= 8 * 64 * 32) return launch_v(codes, scales, m, k, xq, xs, y, s);
-  // tilings measured at 14336 x 4096: 16 x 16 tiles with K split up to N = 16,
-  // then the wide kernel, 32 tokens (two groups per stage when the group
-  // count is even) up to N = 64, 128 tokens beyond
+  // tilings measured at 14336 x 4096 and 4096 x 14336: up to N = 16 the
+  // unit-loaded kernel, 64 rows x 4 groups per workgroup of 8 waves (N = 2 /
+  // 16: 12.0 / 14.8 us, against 16.4 / 17.9 us for k_gemm_w4a8 with K split
+  // three ways; 1, 2, 8 and 16 groups per workgroup and 4 or 16 waves were
+  // slower), then the wide kernel, 32 tokens (two groups per stage when the
+  // group count is even) up to N = 64, 128 tokens beyond
   const int64_t cus = cu_count_w4();
-  if (n <= 16) return launch_m<1, 1>(codes, scales, m, k, xq, xs, n, y, s);
+  if (n <= 16) return launch_mu<4, 2>(codes, scales, m, k, xq, xs, n, y, s);
   if (n <= 64) {
     if ((k / 128) % 2 == 0) return launch_w<1, 2>(codes, scales, m, k, xq, xs, n, y, cus, s);
     return launch_w<1, 1>(codes, scales, m, k, xq, xs, n, y, cus, s);

@@ -474,9 +474,10 @@ def test_gemm_w4a8_single_group(q, n):
     w4a8_case(q, 70, 128, n, 40)
 
 
-@pytest.mark.parametrize("n", [40, 300])
+@pytest.mark.parametrize("n", [5, 16, 40, 300])
 def test_gemm_w4a8_odd_group_count(q, n):
-    # k = 9 groups: the wide kernel stages one group at a time
+    # k = 9 groups: the K slices of the small-N kernel end ragged (4 + 4 + 1);
+    # the wide kernel stages one group at a time
     w4a8_case(q, 200, 1152, n, 39)
 
 
