@@ -1004,9 +1004,11 @@ hipError_t launch_w(const void* blocks, int64_t m, int64_t k, const void* x, int
 // decode to (code-8)/16) and, for the affine formats, its offset term
 // 8*s + a beside them; the matrix ops then read a dword per lane from LDS
 // (16 rows x 4 k-groups: 64 different banks).  Every load of the workgroup
-// is issued before the single barrier, and the K range is split over the
-// grid.  The affine formats add sum_j (8 s_j + a_j) * sum(x over sub-block j)
-// per group with two fp32 16x16x4 matrix ops, as k_gemm_t does.
+// is issued before the first barrier, and the K range is split over the
+// grid.  With KW > 1 the workgroup has 4*KW waves: KW waves share each
+// 16*R16 rows, each taking NSB/KW of the groups, and add their sums in LDS
+// at the end.  The affine formats add sum_j (8 s_j + a_j) * sum(x over
+// sub-block j) per group with two fp32 16x16x4 matrix ops, as k_gemm_t does.
 // ---------------------------------------------------------------------------
 
 // One 32-weight unit: raw loads, then code dwords, scale*16 and offset term.
@@ -1116,8 +1118,8 @@ struct UnitU<QBLK_Q4_K> {
   }
 };
 
-template <int FMT, int R16, int T16, int NSB, bool SPLIT>
-__global__ __launch_bounds__(kThreads) void k_gemm_u(const uint8_t* __restrict__ W,
+template <int FMT, int R16, int T16, int NSB, int KW, bool SPLIT>
+__global__ __launch_bounds__(kThreads * KW) void k_gemm_u(const uint8_t* __restrict__ W,
                                                    const uint16_t* __restrict__ X,
                                                    float* __restrict__ Y, int M, int K, int N) {
   using UU = UnitU<FMT>;
@@ -1125,18 +1127,20 @@ __global__ __launch_bounds__(kThreads) void k_gemm_u(const uint8_t* __restrict__
   constexpr int NT = 16 * T16;
   constexpr int RW = 64 * R16;             // weight rows per workgroup
   constexpr int UR = NSB * 8;              // units per row in the K slice
-  constexpr int kUPT = RW * UR / kThreads; // units per thread
-  static_assert(RW * UR % kThreads == 0, "whole units per thread");
+  constexpr int kT = kThreads * KW;        // KW waves per 16*R16 rows, each a share of the groups
+  constexpr int kUPT = RW * UR / kT;       // units per thread
+  static_assert(RW * UR % kT == 0 && NSB % KW == 0, "whole units per thread, whole groups per wave");
   constexpr int kCodeRow = UR * 16 + 16;   // bytes per staged row of codes
   constexpr int kScRow = UR + 1;           // floats per staged row of scales
   constexpr int kPieces = NSB * NT * 32;   // 16-byte pieces of the X slice
-  constexpr int kPer = (kPieces + kThreads - 1) / kThreads;
+  constexpr int kPer = (kPieces + kT - 1) / kT;
   __shared__ uint4 xs4[NSB * NT * kLdsRow / 8];
   __shared__ uint4 cs4[RW * kCodeRow / 16];
   __shared__ float scs[RW * kScRow];
   __shared__ float cos_[AFFINE ? RW * kScRow : 1];   // offset terms 8s + a
   __shared__ float xsum[AFFINE ? NSB * NT * 8 : 1];  // [group][token][sub-block]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ float4_t red[KW > 1 ? (KW - 1) * 4 * R16 * T16 * 64 : 1];
+  const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & 3, kw = threadIdx.x >> 8;
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * RW;
   const int n0 = blockIdx.y * NT;
@@ -1151,7 +1155,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_u(const uint8_t* __restrict__
   uint4 xv[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; i++) {
-    const int c = min(static_cast<int>(threadIdx.x) + i * kThreads, kPieces - 1);
+    const int c = min(static_cast<int>(threadIdx.x) + i * kT, kPieces - 1);
     const int sb = c / (NT * 32), rem = c % (NT * 32);
     const int t = min(n0 + (rem >> 5), N - 1), col = rem & 31;
     const int b = b0 + min(sb, nb - 1);
@@ -1160,7 +1164,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_u(const uint8_t* __restrict__
   uint32_t raw[kUPT][UU::RAW];
 #pragma unroll
   for (int i = 0; i < kUPT; i++) {
-    const int U = static_cast<int>(threadIdx.x) + i * kThreads;
+    const int U = static_cast<int>(threadIdx.x) + i * kT;
     const int r = U / UR, u = U % UR;
     const int64_t m = m0 + r < M ? m0 + r : M - 1;
     UU::load(W + m * rowbytes + static_cast<int64_t>(UU::GB) * (b0 + min(u >> 3, nb - 1)), u & 7, raw[i]);
@@ -1169,9 +1173,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_u(const uint8_t* __restrict__
   uint16_t* xs = reinterpret_cast<uint16_t*>(xs4);
 #pragma unroll
   for (int i = 0; i < kPer; i++) {
-    const int c = static_cast<int>(threadIdx.x) + i * kThreads;
+    const int c = static_cast<int>(threadIdx.x) + i * kT;
     const int sb = c / (NT * 32), rem = c % (NT * 32);
-    if (kPieces % kThreads == 0 || c < kPieces) {
+    if (kPieces % kT == 0 || c < kPieces) {
       // entries 8cc..8cc+7 of sub-block j go to the k-group slots 32j + 8g (+4)
       const int j = (rem & 31) >> 2, cc = rem & 3;
       const int g0 = 2 * (cc & 1), half = cc >> 1;
@@ -1189,14 +1193,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_u(const uint8_t* __restrict__
       part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].z), one, part, false);
       part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].w), one, part, false);
       part = quad_sum(part);
-      if ((kPieces % kThreads == 0 || c < kPieces) && (c & 3) == 0)
+      if ((kPieces % kT == 0 || c < kPieces) && (c & 3) == 0)
         xsum[(sb * NT + (rem >> 5)) * 8 + ((rem & 31) >> 2)] = part;
     }
   }
   uint8_t* cs = reinterpret_cast<uint8_t*>(cs4);
 #pragma unroll
   for (int i = 0; i < kUPT; i++) {
-    const int U = static_cast<int>(threadIdx.x) + i * kThreads;
+    const int U = static_cast<int>(threadIdx.x) + i * kT;
     const int r = U / UR, u = U % UR;
     const int64_t m = m0 + r < M ? m0 + r : M - 1;
     uint4 c;
@@ -1217,7 +1221,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_u(const uint8_t* __restrict__
   const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
 
 #pragma unroll
-  for (int sb = 0; sb < NSB; sb++) {
+  for (int sq = 0; sq < NSB / KW; sq++) {
+    const int sb = kw * (NSB / KW) + sq;
     if (sb >= nb) break;
     const uint16_t* xb = xs + sb * NT * kLdsRow;
 #pragma unroll
@@ -1265,6 +1270,30 @@ __global__ __launch_bounds__(kThreads) void k_gemm_u(const uint8_t* __restrict__
     }
   }
 
+  if constexpr (KW > 1) {
+    // the K shares of a row tile meet in LDS
+    if (kw > 0) {
+#pragma unroll
+      for (int tm = 0; tm < R16; tm++)
+#pragma unroll
+        for (int tn = 0; tn < T16; tn++)
+          red[((((kw - 1) * 4 + wave) * R16 + tm) * T16 + tn) * 64 + lane] = acc[tm][tn];
+    }
+    __syncthreads();
+    if (kw > 0) return;
+#pragma unroll
+    for (int q = 1; q < KW; q++)
+#pragma unroll
+      for (int tm = 0; tm < R16; tm++)
+#pragma unroll
+        for (int tn = 0; tn < T16; tn++) {
+          const float4_t o = red[((((q - 1) * 4 + wave) * R16 + tm) * T16 + tn) * 64 + lane];
+          acc[tm][tn].x += o.x;
+          acc[tm][tn].y += o.y;
+          acc[tm][tn].z += o.z;
+          acc[tm][tn].w += o.w;
+        }
+  }
 #pragma unroll
   for (int tm = 0; tm < R16; tm++) {
     const int64_t m = m0 + wave * 16 * R16 + 16 * tm + l16;
@@ -1285,7 +1314,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_u(const uint8_t* __restrict__
   }
 }
 
-template <int FMT, int R16, int T16, int NSB>
+template <int FMT, int R16, int T16, int NSB, int KW = 1>
 hipError_t launch_u(const void* blocks, int64_t m, int64_t k, const void* x, int64_t n, float* y,
                     hipStream_t s) {
   const unsigned gx = static_cast<unsigned>((m + 64 * R16 - 1) / (64 * R16));
@@ -1295,11 +1324,11 @@ hipError_t launch_u(const void* blocks, int64_t m, int64_t k, const void* x, int
   if (gz > 1) {
     const hipError_t e = launch_fill_zero(y, m * n, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_gemm_u<FMT, R16, T16, NSB, true>), dim3(gx, gy, gz), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((k_gemm_u<FMT, R16, T16, NSB, KW, true>), dim3(gx, gy, gz), dim3(kThreads * KW), 0, s,
                        static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
                        static_cast<int>(m), static_cast<int>(k), static_cast<int>(n));
   } else {
-    hipLaunchKernelGGL((k_gemm_u<FMT, R16, T16, NSB, false>), dim3(gx, gy, 1), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((k_gemm_u<FMT, R16, T16, NSB, KW, false>), dim3(gx, gy, 1), dim3(kThreads * KW), 0, s,
                        static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
                        static_cast<int>(m), static_cast<int>(k), static_cast<int>(n));
   }
@@ -1333,14 +1362,16 @@ hipError_t launch_gemm(int fmt, const void* blocks, int64_t m, int64_t k, const 
                        int64_t n, float* y, hipStream_t s) {
   (void)xt;  // only BF16 activations reach this point
   // (sweeps at 14336 x 4096: up to 16 tokens the unit-loaded kernel with
-  // 64-row tiles takes 15.8-16.9 us for every format, against 20.7-34.7 us
-  // for the per-lane-loaded kernels; at 32 tokens it wins only for Q4_0,
-  // 26 us against 37, and k_gemm_sb4_s is best for Type 0, 24 us)
+  // 64-row tiles takes 15.5-16.0 us for every format, against 20.7-34.7 us
+  // for the per-lane-loaded kernels -- Type 1 and Q4_K with two waves per
+  // row tile, each half of the K slice, 16.9 us with one; at 32 tokens it
+  // wins only for Q4_0, 26 us against 37, and k_gemm_sb4_s is best for
+  // Type 0, 24 us)
   if (n <= 16) {
     if (fmt == QBLK_SB4) return launch_u<QBLK_SB4, 1, 1, 2>(blocks, m, k, x, n, y, s);
     if (fmt == QBLK_Q4_0) return launch_u<QBLK_Q4_0, 1, 1, 2>(blocks, m, k, x, n, y, s);
-    if (fmt == QBLK_Q4_K) return launch_u<QBLK_Q4_K, 1, 1, 2>(blocks, m, k, x, n, y, s);
-    return launch_u<QBLK_SB4_AFFINE, 1, 1, 2>(blocks, m, k, x, n, y, s);
+    if (fmt == QBLK_Q4_K) return launch_u<QBLK_Q4_K, 1, 1, 2, 2>(blocks, m, k, x, n, y, s);
+    return launch_u<QBLK_SB4_AFFINE, 1, 1, 2, 2>(blocks, m, k, x, n, y, s);
   }
   if (fmt == QBLK_SB4) {
     if (n <= 32) return launch_s<2, 2, 2>(blocks, m, k, x, n, y, s);

@@ -441,6 +441,17 @@ __global__ __launch_bounds__(kThreadsH) void k_gemv_h(const uint8_t* __restrict_
   for (int k = 0; k < UPL; k++) {
 #pragma unroll
     for (int i = 0; i < RMAX; i++) {
+      // one group at a time: the accumulators (written by the groups before)
+      // and this group's loaded registers are "redefined" here, in order, so
+      // neither can a later group's decode move up nor an earlier group's
+      // products move down (either keeps several groups' decoded codes live).
+      // Not for Q4_K with two waves per row: there the pinned 16-byte headers
+      // would not fit in a wave's registers.
+      if constexpr (!(QK && KS > 1)) {
+#pragma unroll
+        for (int r = 0; r < RMAX; r++) asm volatile("" : "+v"(acc[r]));
+        asm volatile("" : "+v"(q[i][k][0]), "+v"(q[i][k][1]), "+v"(q[i][k][2]), "+v"(q[i][k][3]), "+v"(q[i][k][4]));
+      }
       uint32_t c[4];
       if constexpr (AFFINE) {
         c[0] = q[i][k][0]; c[1] = q[i][k][1]; c[2] = q[i][k][2]; c[3] = q[i][k][3];
@@ -479,6 +490,10 @@ __global__ __launch_bounds__(kThreadsH) void k_gemv_h(const uint8_t* __restrict_
         oa = live[k] ? oa : 0.0f;
         acc[i] = __builtin_fmaf(oa, sx[k], acc[i]);
       }
+      // (and for the machine scheduler: hoisting the realignment of later
+      // groups above this point would make the first product wait for every
+      // load of the wave)
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   // (5) one sum per row; lane 63 holds it
