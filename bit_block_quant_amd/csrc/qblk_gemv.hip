@@ -447,6 +447,10 @@ __global__ __launch_bounds__(kThreadsH) void k_gemv_h(const uint8_t* __restrict_
       // products move down (either keeps several groups' decoded codes live).
       // Not for Q4_K with two waves per row: there the pinned 16-byte headers
       // would not fit in a wave's registers.
+      // a last row slot past the workgroup's rows repeats its last row
+      // (loaded, to keep every wave's loads unconditional): skip the math
+      // (one wave per row only: with two, Q4_K would run out of registers)
+      if (KS == 1 && i == RMAX - 1 && row0 + slot + SLOTS * i >= row_end) continue;
       if constexpr (!(QK && KS > 1)) {
 #pragma unroll
         for (int r = 0; r < RMAX; r++) asm volatile("" : "+v"(acc[r]));
