@@ -447,14 +447,25 @@ __global__ __launch_bounds__(kThreadsH) void k_gemv_h(const uint8_t* __restrict_
       // products move down (either keeps several groups' decoded codes live).
       // Not for Q4_K with two waves per row: there the pinned 16-byte headers
       // would not fit in a wave's registers.
-      // a last row slot past the workgroup's rows repeats its last row
-      // (loaded, to keep every wave's loads unconditional): skip the math
-      // (one wave per row only: with two, Q4_K would run out of registers)
-      if (KS == 1 && i == RMAX - 1 && row0 + slot + SLOTS * i >= row_end) continue;
-      if constexpr (!(QK && KS > 1)) {
+      // A last row slot past the workgroup's rows repeats its last row
+      // (loaded, to keep every wave's loads unconditional): its math is
+      // skipped (one wave per row only).  For the affine formats the compiler
+      // sinks that row's loads into the skip branch unless the pins below
+      // come first, so there the skip follows them; for Type 0 and Q4_0 it
+      // does not, and skipping before the pins is a little faster.
+      const bool dup = KS == 1 && i == RMAX - 1 && row0 + slot + SLOTS * i >= row_end;
+      if constexpr (!AFFINE) {
+        if (dup) continue;
+      }
+      if constexpr (!(QK && KS > 1)) {  // (Q4_K with two waves per row: no registers to spare)
 #pragma unroll
         for (int r = 0; r < RMAX; r++) asm volatile("" : "+v"(acc[r]));
         asm volatile("" : "+v"(q[i][k][0]), "+v"(q[i][k][1]), "+v"(q[i][k][2]), "+v"(q[i][k][3]), "+v"(q[i][k][4]));
+        if constexpr (QK) asm volatile("" : "+v"(hk[i][k].x), "+v"(hk[i][k].y), "+v"(hk[i][k].z), "+v"(hk[i][k].w));
+        else if constexpr (AFFINE) asm volatile("" : "+v"(hs[i][k]), "+v"(hc[i][k]), "+v"(ha[i][k]));
+        if constexpr (AFFINE) {
+          if (dup) continue;
+        }
       }
       uint32_t c[4];
       if constexpr (AFFINE) {

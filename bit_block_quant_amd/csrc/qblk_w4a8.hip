@@ -124,6 +124,16 @@ __global__ __launch_bounds__(kWavesV * kWave) void k_gemv_w4a8(const uint8_t* __
   for (int i = 0; i < UPL; i++) {
 #pragma unroll
     for (int r = 0; r < RMAX; r++) {
+      // one (chunk, row) group at a time: the accumulators and this group's
+      // loaded registers are "redefined" here, in order, so the compiler can
+      // neither hoist a later group's work nor sink an earlier group's, and
+      // each group waits only for its own loads
+#pragma unroll
+      for (int q = 0; q < RMAX; q++) asm volatile("" : "+v"(acc[q]));
+      asm volatile("" : "+v"(cw[r][i].x), "+v"(cw[r][i].y), "+v"(cw[r][i].z), "+v"(cw[r][i].w), "+v"(sc[r][i]));
+      // a last row slot past the workgroup's rows repeats its last row: skip
+      // the math (only after the pins, which keep its loads out of the branch)
+      if (r == RMAX - 1 && row0 + wave + kWavesV * r >= row_end) continue;
       const uint4 c = cw[r][i];
       int a = corr[i];
       a = dot4(c.x & kLo4, xl[i].x, a);
@@ -136,6 +146,7 @@ __global__ __launch_bounds__(kWavesV * kWave) void k_gemv_w4a8(const uint8_t* __
       a = dot4((c.w >> 4) & kLo4, xh[i].w, a);
       const float d = live[i] ? f16_bits_to_f32(sc[r][i]) : 0.0f;
       acc[r] = __builtin_fmaf(d, static_cast<float>(a), acc[r]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   const float st = xs[0];
