@@ -25,13 +25,14 @@
 // nibbles) -- and the same eight X entries.
 //
 // Tiling: A = X (16 tokens per tile), B = W^T (16 weight rows per tile), so a
-// lane's outputs share one weight row and one scale.  A workgroup of 4 waves
-// owns 64*TM weight rows (16*TM per wave) and 16*TN tokens.  Per super-block
-// (256 k) the X tile (16*TN x 256 bf16) is double-buffered in LDS (one barrier
-// per super-block) and the next super-block's codes and header are fetched
-// into registers while the current one is multiplied.  When the M x N tiling
-// leaves too few workgroups for the GPU, the K range is split over a third
-// grid dimension and the partial products are added into Y (zeroed first).
+// lane's outputs share one weight row and one scale.  Three kernels: up to 16
+// tokens k_gemm_u (one stage of 64 rows x 2 super-blocks per workgroup, every
+// load issued up front, K split over the grid), up to 64 tokens k_gemm_s (the
+// same stages walked over the whole K range, the next stage's loads in flight
+// while the current one is multiplied), beyond that k_gemm_w (32x32x16
+// matrix ops, 128 rows x 128 tokens per workgroup).  When a K range is split
+// over a third grid dimension the partial products are added into Y (zeroed
+// first).
 #include "qblk_device.h"
 #include "qblk_launch.h"
 
@@ -77,326 +78,11 @@ __device__ __forceinline__ bf16x8v_t decode_codes(uint32_t q) {
   return __builtin_bit_cast(bf16x8v_t, w);
 }
 
-// The registers a lane needs from one 256-weight group of one weight row:
-// the 8 code dwords of its k-group (one per sub-block), the 8 sub-block
-// scales, and (Type 1) the sub-block offsets of sub-blocks g and g+4.
-struct SbRegs {
-  uint32_t code[8];
-  float scale[8];  // 16 * (scale of sub-block j): codes decode to (code-8)/16
-  float corr[2];   // Type 1: 8*s_j + a_j for j = g, g+4 (see k_gemm_t)
-};
-
-// How each format lays out a 256-weight group (8 sub-blocks of 32):
-//  Type 0   [S16][sc x8][qs x128]              138 B, scale S*sc_j
-//  Q4_0     8 blocks [d16][qs x16]              144 B, scale d_j
-//  Type 1   [Ss16][Sa16][sc x8][ac x8][qs x128] 148 B, scale Ss*sc_j, offset Sa*ac_j
-//  Q4_K     [d16][dmin16][6-bit fields x16][qs x128] 144 B, scale d*s_j, offset -dmin*m_j
-// Lane k-group g needs code bytes 4g..4g+3 of every sub-block.
-template <int FMT>
-struct Group;
-
-template <>
-struct Group<QBLK_SB4> {
-  static constexpr int GB = 138, RAW = 3 + 16;
-  // header: the dword-aligned 12 bytes holding the 10 header bytes; codes
-  // (2-byte aligned): two u16 per sub-block
-  static __device__ __forceinline__ void load(const uint8_t* p, int g, uint32_t raw[RAW]) {
-    const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
-    const u32x3_a4 h = *reinterpret_cast<const u32x3_a4*>(p - mis);
-    raw[0] = h.x;
-    raw[1] = h.y;
-    raw[2] = h.z;
-#pragma unroll
-    for (int s = 0; s < 8; s++) {
-      const uint8_t* o = p + 10 + 16 * s + 4 * g;
-      raw[3 + 2 * s] = load_u16(o);
-      raw[4 + 2 * s] = load_u16(o + 2);
-    }
-  }
-  static __device__ __forceinline__ void finish(const uint8_t* p, int, const uint32_t raw[RAW], SbRegs& r) {
-    const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
-    const uint32_t w0 = __builtin_amdgcn_alignbyte(raw[1], raw[0], sh);  // S16, sc0, sc1
-    const uint32_t w1 = __builtin_amdgcn_alignbyte(raw[2], raw[1], sh);  // sc2..sc5
-    const uint32_t w2 = raw[2] >> (8 * sh);                              // sc6, sc7
-    const float S16 = f16_bits_to_f32(w0 & 0xffffu) * 16.0f;
-    const uint32_t sc03 = (w0 >> 16) | (w1 << 16), sc47 = (w1 >> 16) | (w2 << 16);
-#pragma unroll
-    for (int s = 0; s < 8; s++) {
-      r.code[s] = raw[3 + 2 * s] | (raw[4 + 2 * s] << 16);
-      const uint32_t word = s < 4 ? sc03 : sc47;
-      const int8_t c = static_cast<int8_t>((word >> (8 * (s & 3))) & 0xffu);
-      r.scale[s] = S16 * static_cast<float>(c);
-    }
-    r.corr[0] = r.corr[1] = 0.0f;
-  }
-};
-
-template <>
-struct Group<QBLK_Q4_0> {
-  // p is 4-byte aligned (rows are whole multiples of 144 bytes): block j
-  // starts at 18j, 2 bytes past a dword boundary when j is odd.
-  static constexpr int GB = 144, RAW = 8 + 12;
-  static __device__ __forceinline__ void load(const uint8_t* p, int g, uint32_t raw[RAW]) {
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-      raw[j] = *reinterpret_cast<const uint32_t*>(p + ((18 * j) & ~3));  // d16 in the low or high half
-      if (j & 1) {
-        raw[8 + (j >> 1) * 3 + 2] = *reinterpret_cast<const uint32_t*>(p + 18 * j + 2 + 4 * g);  // aligned
-      } else {
-        const u32x2_a4 v = *reinterpret_cast<const u32x2_a4*>(p + 18 * j + 4 * g);  // bytes 2..5 at +2
-        raw[8 + (j >> 1) * 3] = v.x;
-        raw[8 + (j >> 1) * 3 + 1] = v.y;
-      }
-    }
-  }
-  static __device__ __forceinline__ void finish(const uint8_t*, int, const uint32_t raw[RAW], SbRegs& r) {
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const uint32_t d = (j & 1) ? raw[j] >> 16 : raw[j] & 0xffffu;
-      r.scale[j] = f16_bits_to_f32(d) * 16.0f;
-      r.code[j] = (j & 1) ? raw[8 + (j >> 1) * 3 + 2]
-                          : __builtin_amdgcn_alignbyte(raw[8 + (j >> 1) * 3 + 1], raw[8 + (j >> 1) * 3], 2);
-    }
-    r.corr[0] = r.corr[1] = 0.0f;
-  }
-};
-
-template <>
-struct Group<QBLK_SB4_AFFINE> {
-  // 148-byte groups are dword aligned: header dwords 0..4, codes 4-aligned
-  static constexpr int GB = 148, RAW = 5 + 8;
-  static __device__ __forceinline__ void load(const uint8_t* p, int g, uint32_t raw[RAW]) {
-    const u32x4_a4 h = *reinterpret_cast<const u32x4_a4*>(p);
-    raw[0] = h.x;
-    raw[1] = h.y;
-    raw[2] = h.z;
-    raw[3] = h.w;
-    raw[4] = *reinterpret_cast<const uint32_t*>(p + 16);
-#pragma unroll
-    for (int s = 0; s < 8; s++) raw[5 + s] = *reinterpret_cast<const uint32_t*>(p + 20 + 16 * s + 4 * g);
-  }
-  static __device__ __forceinline__ void finish(const uint8_t*, int g, const uint32_t raw[RAW], SbRegs& r) {
-    const float Ss = f16_bits_to_f32(raw[0] & 0xffffu), Sa = f16_bits_to_f32(raw[0] >> 16);
-#pragma unroll
-    for (int s = 0; s < 8; s++) {
-      r.code[s] = raw[5 + s];
-      const int8_t c = static_cast<int8_t>((raw[1 + (s >> 2)] >> (8 * (s & 3))) & 0xffu);
-      r.scale[s] = (Ss * static_cast<float>(c)) * 16.0f;
-    }
-    // w = s*n + a = s*(n-8) + (8s + a): the codes decode to n-8 as for Type 0,
-    // and (8s + a) * sum(x over the sub-block) is added per group
-#pragma unroll
-    for (int q = 0; q < 2; q++) {
-      const uint32_t sw = raw[1 + q], aw = raw[3 + q];
-      const int8_t c = static_cast<int8_t>((sw >> (8 * g)) & 0xffu);
-      const int8_t o = static_cast<int8_t>((aw >> (8 * g)) & 0xffu);
-      r.corr[q] = __builtin_fmaf(8.0f, Ss * static_cast<float>(c), Sa * static_cast<float>(o));
-    }
-  }
-};
-
-template <>
-struct Group<QBLK_Q4_K> {
-  // 144-byte groups are 16-byte aligned: the header as one dwordx4, codes
-  // (codes 0..15, offset -dmin*m_j) handled like Type 1's
-  static constexpr int GB = 144, RAW = 4 + 8;
-  static __device__ __forceinline__ void load(const uint8_t* p, int g, uint32_t raw[RAW]) {
-    const uint4 h = *reinterpret_cast<const uint4*>(p);
-    raw[0] = h.x;
-    raw[1] = h.y;
-    raw[2] = h.z;
-    raw[3] = h.w;
-#pragma unroll
-    for (int s = 0; s < 8; s++) raw[4 + s] = *reinterpret_cast<const uint32_t*>(p + 16 + 16 * s + 4 * g);
-  }
-  static __device__ __forceinline__ void finish(const uint8_t*, int g, const uint32_t raw[RAW], SbRegs& r) {
-    const float D = f16_bits_to_f32(raw[0] & 0xffffu), Dm = f16_bits_to_f32(raw[0] >> 16);
-#pragma unroll
-    for (int s = 0; s < 8; s++) {
-      r.code[s] = raw[4 + s];
-      r.scale[s] = (D * static_cast<float>(q4k_scale6(raw[1], raw[2], s))) * 16.0f;
-    }
-    // w = S*n - M = S*(n-8) + (8S - M), as for Type 1
-#pragma unroll
-    for (int q = 0; q < 2; q++) {
-      const int sb = 4 * q + g;
-      const float S = D * static_cast<float>(q4k_scale6(raw[1], raw[2], sb));
-      r.corr[q] = __builtin_fmaf(8.0f, S, -(Dm * static_cast<float>(q4k_min6(raw[2], raw[3], sb))));
-    }
-  }
-};
-
 // sum over the 4 lanes of a quad (lanes 4i..4i+3)
 __device__ __forceinline__ float quad_sum(float v) {
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));  // quad_perm 2,3,0,1
   return v;
-}
-
-// Type 1 also needs sum(x) over every sub-block of every token: the staging
-// threads form it (the 4 quarters of a sub-block sit on 4 adjacent lanes) and
-// the per-group correction sum_j (8 s_j + a_j) sum(x_j) is added with two
-// fp32 16x16x4 matrix ops (sub-blocks 0..3 and 4..7) into the accumulators.
-template <int FMT, int TM, int TN, bool SPLIT>
-__global__ __launch_bounds__(kThreads) void k_gemm_t(const uint8_t* __restrict__ W,
-                                                     const uint16_t* __restrict__ X,
-                                                     float* __restrict__ Y, int M, int K, int N,
-                                                     int sb_per_split) {
-  using G = Group<FMT>;
-  constexpr bool AFFINE = FMT == QBLK_SB4_AFFINE || FMT == QBLK_Q4_K;
-  constexpr int NT = 16 * TN;
-  __shared__ uint4 xs4[2][NT * kLdsRow / 8];
-  __shared__ float xsum[2][AFFINE ? NT * 8 : 1];  // [token][sub-block]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
-  const int64_t mw = static_cast<int64_t>(blockIdx.x) * 64 * TM + wave * 16 * TM;
-  const int n0 = blockIdx.y * NT;
-  const int nsb = K / 256;
-  const int b_begin = SPLIT ? blockIdx.z * sb_per_split : 0;
-  const int b_end = SPLIT ? min(nsb, b_begin + sb_per_split) : nsb;
-  const int64_t rowbytes = static_cast<int64_t>(nsb) * G::GB;
-  const uint8_t* rowp[TM];
-#pragma unroll
-  for (int tm = 0; tm < TM; tm++) {
-    int64_t m = mw + 16 * tm + l16;
-    m = m < M ? m : M - 1;
-    rowp[tm] = W + m * rowbytes;
-  }
-
-  // X tile staging: thread t moves uint4 c = t, t+256, ... of the NT x 256 tile
-  auto load_x = [&](int b, uint4 xv[(NT * 32 + kThreads - 1) / kThreads]) {
-#pragma unroll
-    for (int i = 0; i < (NT * 32 + kThreads - 1) / kThreads; i++) {
-      const int c = threadIdx.x + i * kThreads;
-      const int r = c >> 5, col = c & 31;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (c < NT * 32 && n0 + r < N)
-        v = *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(n0 + r) * K + 256 * b + 8 * col);
-      xv[i] = v;
-    }
-  };
-  auto store_x = [&](int buf, const uint4 xv[(NT * 32 + kThreads - 1) / kThreads]) {
-    uint16_t* xs = reinterpret_cast<uint16_t*>(xs4[buf]);
-#pragma unroll
-    for (int i = 0; i < (NT * 32 + kThreads - 1) / kThreads; i++) {
-      const int c = threadIdx.x + i * kThreads;
-      if (c < NT * 32) {
-        // entries 8cc..8cc+7 of sub-block j: the first half of k-groups 2cc and
-        // 2cc+1 (cc < 2) or the second half of k-groups 2cc-4, 2cc-3 (cc >= 2)
-        const int j = (c & 31) >> 2, cc = c & 3;
-        const int g0 = 2 * (cc & 1), half = cc >> 1;
-        uint16_t* row = xs + (c >> 5) * kLdsRow + 32 * j + 4 * half;
-        *reinterpret_cast<uint2*>(row + 8 * g0) = make_uint2(xv[i].x, xv[i].y);
-        *reinterpret_cast<uint2*>(row + 8 * (g0 + 1)) = make_uint2(xv[i].z, xv[i].w);
-      }
-      if constexpr (AFFINE) {
-        // products with 1.0 are exact; the sums are fp32
-        const bf16x2v_t one = __builtin_bit_cast(bf16x2v_t, 0x3f803f80u);
-        float part = 0.0f;
-        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].x), one, part, false);
-        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].y), one, part, false);
-        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].z), one, part, false);
-        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].w), one, part, false);
-        part = quad_sum(part);
-        if (c < NT * 32 && (c & 3) == 0) xsum[buf][(c >> 5) * 8 + ((c & 31) >> 2)] = part;
-      }
-    }
-  };
-
-  float4_t acc[TM][TN];
-#pragma unroll
-  for (int tm = 0; tm < TM; tm++)
-#pragma unroll
-    for (int tn = 0; tn < TN; tn++) acc[tm][tn] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-
-  uint4 xv[(NT * 32 + kThreads - 1) / kThreads];
-  uint32_t raw[TM][G::RAW];
-  SbRegs cur[TM];
-  if (b_begin < b_end) {
-    load_x(b_begin, xv);
-#pragma unroll
-    for (int tm = 0; tm < TM; tm++) G::load(rowp[tm] + static_cast<int64_t>(b_begin) * G::GB, g, raw[tm]);
-    store_x(0, xv);
-#pragma unroll
-    for (int tm = 0; tm < TM; tm++) G::finish(rowp[tm] + static_cast<int64_t>(b_begin) * G::GB, g, raw[tm], cur[tm]);
-  }
-
-  for (int b = b_begin; b < b_end; b++) {
-    const int buf = (b - b_begin) & 1;
-    __syncthreads();
-    const bool more = b + 1 < b_end;
-    if (more) {
-      load_x(b + 1, xv);
-#pragma unroll
-      for (int tm = 0; tm < TM; tm++) G::load(rowp[tm] + static_cast<int64_t>(b + 1) * G::GB, g, raw[tm]);
-    }
-    const uint16_t* xs = reinterpret_cast<const uint16_t*>(xs4[buf]);
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-      bf16x8v_t Bop[TM];
-#pragma unroll
-      for (int tm = 0; tm < TM; tm++) Bop[tm] = decode_codes(cur[tm].code[j]);
-#pragma unroll
-      for (int tn = 0; tn < TN; tn++) {
-        const bf16x8v_t Aop = *reinterpret_cast<const bf16x8v_t*>(xs + (16 * tn + l16) * kLdsRow + 32 * j + 8 * g);
-#pragma unroll
-        for (int tm = 0; tm < TM; tm++) {
-          const float4_t P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aop, Bop[tm], zero, 0, 0, 0);
-          const float sc = cur[tm].scale[j];
-          float4_t& A = acc[tm][tn];
-          A.x = __builtin_fmaf(sc, P.x, A.x);
-          A.y = __builtin_fmaf(sc, P.y, A.y);
-          A.z = __builtin_fmaf(sc, P.z, A.z);
-          A.w = __builtin_fmaf(sc, P.w, A.w);
-        }
-      }
-      // One sub-block at a time: the accumulators are "used" here, so the
-      // scaled additions cannot be sunk past later sub-blocks' MFMAs (which
-      // would keep every partial product live at once).
-#pragma unroll
-      for (int tm = 0; tm < TM; tm++)
-#pragma unroll
-        for (int tn = 0; tn < TN; tn++)
-          asm volatile("" : "+v"(acc[tm][tn].x), "+v"(acc[tm][tn].y), "+v"(acc[tm][tn].z), "+v"(acc[tm][tn].w));
-    }
-    if constexpr (AFFINE) {
-      // A = sum(x) [token][sub-block 4q + g], B = (8 s + a) [sub-block 4q + g][row]
-#pragma unroll
-      for (int tn = 0; tn < TN; tn++) {
-        const float* xq = xsum[buf] + (16 * tn + l16) * 8 + g;
-#pragma unroll
-        for (int tm = 0; tm < TM; tm++) {
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[0], cur[tm].corr[0], acc[tm][tn], 0, 0, 0);
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[4], cur[tm].corr[1], acc[tm][tn], 0, 0, 0);
-        }
-      }
-    }
-    if (more) {
-      store_x(buf ^ 1, xv);
-#pragma unroll
-      for (int tm = 0; tm < TM; tm++) G::finish(rowp[tm] + static_cast<int64_t>(b + 1) * G::GB, g, raw[tm], cur[tm]);
-    }
-  }
-
-#pragma unroll
-  for (int tm = 0; tm < TM; tm++) {
-    const int64_t m = mw + 16 * tm + l16;
-    if (m >= M) continue;
-#pragma unroll
-    for (int tn = 0; tn < TN; tn++) {
-      const float v[4] = {acc[tm][tn].x, acc[tm][tn].y, acc[tm][tn].z, acc[tm][tn].w};
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int n = n0 + 16 * tn + 4 * g + r;
-        if (n < N) {
-          float* dst = Y + static_cast<int64_t>(n) * M + m;
-          if constexpr (SPLIT) atomicAdd(dst, v[r]);
-          else *dst = v[r];
-        }
-      }
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -564,7 +250,7 @@ struct GroupW<QBLK_SB4_AFFINE> {
       const int8_t c = static_cast<int8_t>((raw[1 + (s >> 2)] >> (8 * (s & 3))) & 0xffu);
       r.scale[s] = (Ss * static_cast<float>(c)) * 16.0f;
     }
-    // w = s*n + a = s*(n-8) + (8s + a), as in Group<QBLK_SB4_AFFINE>
+    // w = s*n + a = s*(n-8) + (8s + a): the codes decode to n-8 as for Type 0
 #pragma unroll
     for (int q = 0; q < 4; q++) {
       const int sb = 2 * q + h;
@@ -752,172 +438,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_w(const uint8_t* __restric
   }
 }
 
-// ---------------------------------------------------------------------------
-// Few tokens (at most 64): the product is bound by streaming W, so each
-// workgroup issues every load it needs up front -- the codes of its 128 rows
-// over NSB super-blocks straight into registers, and the matching X slice into
-// LDS -- then multiplies and adds its partial sums into Y (zeroed first when
-// K is split over the grid).  Layout as in k_gemm_sb4: 16x16x32 steps, X in
-// MFMA order in LDS, lane k-group g taking code bytes 4g..4g+3.
-// ---------------------------------------------------------------------------
-constexpr int kRawS = 3 + 8 * 2;  // header dwords + an aligned dword pair per sub-block
-
-// Header (as in load_sb_w) and, per sub-block, code bytes 4g..4g+3 at A from
-// the dword pair at A & ~3 (sub-blocks 0..6) or, for sub-block 7, the dword
-// at A & ~3 plus the 2 bytes at A+2: nothing past the super-block is read.
-__device__ __forceinline__ void load_sb_s(const uint8_t* p, int g, uint32_t raw[kRawS]) {
-  const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
-  const u32x3_a4 hd = *reinterpret_cast<const u32x3_a4*>(p - mis);
-  raw[0] = hd.x;
-  raw[1] = hd.y;
-  raw[2] = hd.z;
-  const uint8_t* a = p + 10 + 4 * g;
-  const uint8_t* c = p - mis + ((mis + 10 + 4 * g) & ~3u);  // a & ~3
-#pragma unroll
-  for (int s = 0; s < 7; s++) {
-    const u32x2_a4 v = *reinterpret_cast<const u32x2_a4*>(c + 16 * s);
-    raw[3 + 2 * s] = v.x;
-    raw[4 + 2 * s] = v.y;
-  }
-  raw[3 + 2 * 7] = *reinterpret_cast<const uint32_t*>(c + 16 * 7);
-  raw[4 + 2 * 7] = load_u16(a + 16 * 7 + 2);
-}
-
-__device__ __forceinline__ void finish_sb_s(const uint8_t* p, const uint32_t raw[kRawS], SbRegs& r) {
-  const uint32_t sh = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p) & 3u);
-  const uint32_t w0 = __builtin_amdgcn_alignbyte(raw[1], raw[0], sh);  // S16, sc0, sc1
-  const uint32_t w1 = __builtin_amdgcn_alignbyte(raw[2], raw[1], sh);  // sc2..sc5
-  const uint32_t w2 = raw[2] >> (8 * sh);                              // sc6, sc7
-  const float S16 = f16_bits_to_f32(w0 & 0xffffu) * 16.0f;
-  const uint32_t sc03 = (w0 >> 16) | (w1 << 16), sc47 = (w1 >> 16) | (w2 << 16);
-  const uint32_t cs = (sh + 2) & 3u;  // code bytes start at p + 10
-#pragma unroll
-  for (int s = 0; s < 8; s++) {
-    r.code[s] = __builtin_amdgcn_alignbyte(raw[4 + 2 * s], raw[3 + 2 * s], cs);
-    const uint32_t word = s < 4 ? sc03 : sc47;
-    const int8_t c = static_cast<int8_t>((word >> (8 * (s & 3))) & 0xffu);
-    r.scale[s] = S16 * static_cast<float>(c);
-  }
-}
-
-template <int R16, int T16, int NSB, bool SPLIT>
-__global__ __launch_bounds__(kThreads) void k_gemm_sb4_s(const uint8_t* __restrict__ W,
-                                                       const uint16_t* __restrict__ X,
-                                                       float* __restrict__ Y, int M, int K, int N) {
-  constexpr int NT = 16 * T16;
-  constexpr int kPieces = NSB * NT * 32;  // 16-byte pieces of the X slice
-  constexpr int kPer = (kPieces + kThreads - 1) / kThreads;
-  __shared__ uint4 xs4[NSB * NT * kLdsRow / 8];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
-  const int64_t mw = static_cast<int64_t>(blockIdx.x) * 64 * R16 + wave * 16 * R16;
-  const int n0 = blockIdx.y * NT;
-  const int nsb = K / 256;
-  const int b0 = blockIdx.z * NSB;
-  const int nb = min(NSB, nsb - b0);  // super-blocks in this piece of K (>= 1)
-  const int64_t rowbytes = static_cast<int64_t>(nsb) * 138;
-  const uint8_t* rowp[R16];
-#pragma unroll
-  for (int tm = 0; tm < R16; tm++) {
-    const int64_t m = mw + 16 * tm + l16;
-    rowp[tm] = W + (m < M ? m : M - 1) * rowbytes + static_cast<int64_t>(b0) * 138;
-  }
-
-  // X first (L2-resident, needed before the barrier), then all the codes.
-  // Pieces past the piece's last super-block or past token N-1 re-read valid
-  // data that is never used or never stored.
-  uint4 xv[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; i++) {
-    const int c = min(static_cast<int>(threadIdx.x) + i * kThreads, kPieces - 1);
-    const int sb = c / (NT * 32), rem = c % (NT * 32);
-    const int t = min(n0 + (rem >> 5), N - 1), col = rem & 31;
-    const int b = b0 + min(sb, nb - 1);
-    xv[i] = *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(t) * K + 256 * b + 8 * col);
-  }
-  uint32_t raw[R16][NSB][kRawS];
-#pragma unroll
-  for (int sb = 0; sb < NSB; sb++)
-#pragma unroll
-    for (int tm = 0; tm < R16; tm++) load_sb_s(rowp[tm] + 138 * min(sb, nb - 1), g, raw[tm][sb]);
-
-  uint16_t* xs = reinterpret_cast<uint16_t*>(xs4);
-#pragma unroll
-  for (int i = 0; i < kPer; i++) {
-    const int c = static_cast<int>(threadIdx.x) + i * kThreads;
-    if (kPieces % kThreads == 0 || c < kPieces) {
-      const int sb = c / (NT * 32), rem = c % (NT * 32);
-      // entries 8cc..8cc+7 of sub-block j go to the k-group slots 32j + 8g (+4)
-      const int j = (rem & 31) >> 2, cc = rem & 3;
-      const int g0 = 2 * (cc & 1), half = cc >> 1;
-      uint16_t* row = xs + (sb * NT + (rem >> 5)) * kLdsRow + 32 * j + 4 * half;
-      *reinterpret_cast<uint2*>(row + 8 * g0) = make_uint2(xv[i].x, xv[i].y);
-      *reinterpret_cast<uint2*>(row + 8 * (g0 + 1)) = make_uint2(xv[i].z, xv[i].w);
-    }
-  }
-  __syncthreads();
-
-  float4_t acc[R16][T16];
-#pragma unroll
-  for (int tm = 0; tm < R16; tm++)
-#pragma unroll
-    for (int tn = 0; tn < T16; tn++) acc[tm][tn] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-
-#pragma unroll
-  for (int sb = 0; sb < NSB; sb++) {
-    if (sb >= nb) break;
-    SbRegs cur[R16];
-#pragma unroll
-    for (int tm = 0; tm < R16; tm++) finish_sb_s(rowp[tm] + 138 * sb, raw[tm][sb], cur[tm]);
-    const uint16_t* xb = xs + sb * NT * kLdsRow;
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-      bf16x8v_t Bop[R16];
-#pragma unroll
-      for (int tm = 0; tm < R16; tm++) Bop[tm] = decode_codes(cur[tm].code[j]);
-#pragma unroll
-      for (int tn = 0; tn < T16; tn++) {
-        const bf16x8v_t Aop = *reinterpret_cast<const bf16x8v_t*>(xb + (16 * tn + l16) * kLdsRow + 32 * j + 8 * g);
-#pragma unroll
-        for (int tm = 0; tm < R16; tm++) {
-          const float4_t P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aop, Bop[tm], zero, 0, 0, 0);
-          const float sc = cur[tm].scale[j];
-          float4_t& A = acc[tm][tn];
-          A.x = __builtin_fmaf(sc, P.x, A.x);
-          A.y = __builtin_fmaf(sc, P.y, A.y);
-          A.z = __builtin_fmaf(sc, P.z, A.z);
-          A.w = __builtin_fmaf(sc, P.w, A.w);
-        }
-      }
-#pragma unroll
-      for (int tm = 0; tm < R16; tm++)
-#pragma unroll
-        for (int tn = 0; tn < T16; tn++)
-          asm volatile("" : "+v"(acc[tm][tn].x), "+v"(acc[tm][tn].y), "+v"(acc[tm][tn].z), "+v"(acc[tm][tn].w));
-    }
-  }
-
-#pragma unroll
-  for (int tm = 0; tm < R16; tm++) {
-    const int64_t m = mw + 16 * tm + l16;
-    if (m >= M) continue;
-#pragma unroll
-    for (int tn = 0; tn < T16; tn++) {
-      const float v[4] = {acc[tm][tn].x, acc[tm][tn].y, acc[tm][tn].z, acc[tm][tn].w};
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int n = n0 + 16 * tn + 4 * g + r;
-        if (n < N) {
-          float* dst = Y + static_cast<int64_t>(n) * M + m;
-          if constexpr (SPLIT) atomicAdd(dst, v[r]);
-          else *dst = v[r];
-        }
-      }
-    }
-  }
-}
-
 int cu_count_gemm() {
   static int n = 0;
   if (n == 0) {
@@ -927,36 +447,6 @@ int cu_count_gemm() {
       n = 256;
   }
   return n;
-}
-
-template <int FMT, int TM, int TN>
-hipError_t launch_t(const void* blocks, int64_t m, int64_t k, const void* x, int64_t n, float* y,
-                    hipStream_t s) {
-  const unsigned gx = static_cast<unsigned>((m + 64 * TM - 1) / (64 * TM));
-  const unsigned gy = static_cast<unsigned>((n + 16 * TN - 1) / (16 * TN));
-  const int nsb = static_cast<int>(k / 256);
-  // split K when the tiles alone fill less than two workgroups per CU
-  const int64_t tiles = static_cast<int64_t>(gx) * gy;
-  int split = 1;
-  if (tiles < 2 * cu_count_gemm()) {
-    split = static_cast<int>((2 * cu_count_gemm() + tiles - 1) / tiles);
-    const int max_split = nsb / 2 > 1 ? nsb / 2 : 1;  // keep >= 2 super-blocks per piece
-    split = split > max_split ? max_split : split;
-  }
-  const int per = (nsb + split - 1) / split;
-  split = (nsb + per - 1) / per;
-  if (split > 1) {
-    const hipError_t e = launch_fill_zero(y, m * n, s);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_gemm_t<FMT, TM, TN, true>), dim3(gx, gy, split), dim3(kThreads), 0, s,
-                       static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
-                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), per);
-  } else {
-    hipLaunchKernelGGL((k_gemm_t<FMT, TM, TN, false>), dim3(gx, gy, 1), dim3(kThreads), 0, s,
-                       static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
-                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), nsb);
-  }
-  return hipGetLastError();
 }
 
 template <int FMT, int T32>
@@ -1008,7 +498,9 @@ hipError_t launch_w(const void* blocks, int64_t m, int64_t k, const void* x, int
 // grid.  With KW > 1 the workgroup has 4*KW waves: KW waves share each
 // 16*R16 rows, each taking NSB/KW of the groups, and add their sums in LDS
 // at the end.  The affine formats add sum_j (8 s_j + a_j) * sum(x over
-// sub-block j) per group with two fp32 16x16x4 matrix ops, as k_gemm_t does.
+// sub-block j) per group with two fp32 16x16x4 matrix ops (sub-blocks 0..3
+// and 4..7; the sums of x are formed while X is staged, the 4 pieces of a
+// sub-block sitting on 4 adjacent lanes).
 // ---------------------------------------------------------------------------
 
 // One 32-weight unit: raw loads, then code dwords, scale*16 and offset term.
@@ -1118,200 +610,283 @@ struct UnitU<QBLK_Q4_K> {
   }
 };
 
+// One stage of the unit-loaded kernels: NSB 256-weight groups of a tile of
+// 64*R16 rows and 16*T16 tokens, fetched into registers (load), written to
+// LDS (store) and multiplied out of LDS (compute).  KW waves share each
+// 16*R16 rows, each taking NSB/KW of the stage's groups.
+template <int FMT, int R16, int T16, int NSB, int KW>
+struct UStage {
+  using UU = UnitU<FMT>;
+  static constexpr bool AFFINE = FMT == QBLK_SB4_AFFINE || FMT == QBLK_Q4_K;
+  static constexpr int NT = 16 * T16;
+  static constexpr int RW = 64 * R16;             // weight rows per workgroup
+  static constexpr int UR = NSB * 8;              // units per row in a stage
+  static constexpr int kT = kThreads * KW;        // threads per workgroup
+  static constexpr int kUPT = RW * UR / kT;       // units per thread
+  static_assert(RW * UR % kT == 0 && NSB % KW == 0, "whole units per thread, whole groups per wave");
+  static constexpr int kCodeRow = UR * 16 + 16;   // bytes per staged row of codes
+  static constexpr int kScRow = UR + 1;           // floats per staged row of scales
+  static constexpr int kPieces = NSB * NT * 32;   // 16-byte pieces of the X slice
+  static constexpr int kPer = (kPieces + kT - 1) / kT;
+
+  struct Lds {
+    uint4 xs4[NSB * NT * kLdsRow / 8];
+    uint4 cs4[RW * kCodeRow / 16];
+    float scs[RW * kScRow];
+    float cos_[AFFINE ? RW * kScRow : 1];   // offset terms 8s + a
+    float xsum[AFFINE ? NSB * NT * 8 : 1];  // [group][token][sub-block]
+  };
+  struct Regs {
+    uint4 xv[kPer];
+    uint32_t raw[kUPT][UU::RAW];
+  };
+
+  // Issue the loads of groups [b0, b0 + nb): X first (L2-resident), then
+  // every unit of the tile.  Pieces past the stage's last group or past row
+  // M-1 / token N-1 re-read valid data that is never used or never stored.
+  static __device__ __forceinline__ void load(const uint8_t* __restrict__ W, const uint16_t* __restrict__ X,
+                                              int64_t m0, int n0, int M, int N, int K, int64_t rowbytes,
+                                              int b0, int nb, Regs& r) {
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+      const int c = min(static_cast<int>(threadIdx.x) + i * kT, kPieces - 1);
+      const int sb = c / (NT * 32), rem = c % (NT * 32);
+      const int t = min(n0 + (rem >> 5), N - 1), col = rem & 31;
+      const int b = b0 + min(sb, nb - 1);
+      r.xv[i] = *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(t) * K + 256 * b + 8 * col);
+    }
+#pragma unroll
+    for (int i = 0; i < kUPT; i++) {
+      const int U = static_cast<int>(threadIdx.x) + i * kT;
+      const int rr = U / UR, u = U % UR;
+      const int64_t m = m0 + rr < M ? m0 + rr : M - 1;
+      UU::load(W + m * rowbytes + static_cast<int64_t>(UU::GB) * (b0 + min(u >> 3, nb - 1)), u & 7, r.raw[i]);
+    }
+  }
+
+  // Write a loaded stage to LDS: X in matrix-operand order (and, for the
+  // affine formats, its sums over each sub-block), the realigned codes, the
+  // unit scales and offset terms.
+  static __device__ __forceinline__ void store(Lds& L, const Regs& r, const uint8_t* __restrict__ W, int64_t m0,
+                                               int M, int64_t rowbytes, int b0, int nb) {
+    uint16_t* xs = reinterpret_cast<uint16_t*>(L.xs4);
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+      const int c = static_cast<int>(threadIdx.x) + i * kT;
+      const int sb = c / (NT * 32), rem = c % (NT * 32);
+      if (kPieces % kT == 0 || c < kPieces) {
+        // entries 8cc..8cc+7 of sub-block j go to the k-group slots 32j + 8g (+4)
+        const int j = (rem & 31) >> 2, cc = rem & 3;
+        const int g0 = 2 * (cc & 1), half = cc >> 1;
+        uint16_t* row = xs + (sb * NT + (rem >> 5)) * kLdsRow + 32 * j + 4 * half;
+        *reinterpret_cast<uint2*>(row + 8 * g0) = make_uint2(r.xv[i].x, r.xv[i].y);
+        *reinterpret_cast<uint2*>(row + 8 * (g0 + 1)) = make_uint2(r.xv[i].z, r.xv[i].w);
+      }
+      if constexpr (AFFINE) {
+        // sum of x over the sub-block: products with 1.0 are exact, fp32 sums;
+        // the 4 pieces of a sub-block sit on 4 adjacent lanes
+        const bf16x2v_t one = __builtin_bit_cast(bf16x2v_t, 0x3f803f80u);
+        float part = 0.0f;
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, r.xv[i].x), one, part, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, r.xv[i].y), one, part, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, r.xv[i].z), one, part, false);
+        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, r.xv[i].w), one, part, false);
+        part = quad_sum(part);
+        if ((kPieces % kT == 0 || c < kPieces) && (c & 3) == 0)
+          L.xsum[(sb * NT + (rem >> 5)) * 8 + ((rem & 31) >> 2)] = part;
+      }
+    }
+    uint8_t* cs = reinterpret_cast<uint8_t*>(L.cs4);
+#pragma unroll
+    for (int i = 0; i < kUPT; i++) {
+      const int U = static_cast<int>(threadIdx.x) + i * kT;
+      const int rr = U / UR, u = U % UR;
+      const int64_t m = m0 + rr < M ? m0 + rr : M - 1;
+      uint4 c;
+      float scale, corr;
+      UU::finish(W + m * rowbytes + static_cast<int64_t>(UU::GB) * (b0 + min(u >> 3, nb - 1)), u & 7, r.raw[i],
+                 c, scale, corr);
+      *reinterpret_cast<uint4*>(cs + rr * kCodeRow + 16 * u) = c;
+      L.scs[rr * kScRow + u] = scale;
+      if constexpr (AFFINE) L.cos_[rr * kScRow + u] = corr;
+    }
+  }
+
+  // Multiply this wave's share of a staged stage (nb groups) into acc.
+  static __device__ __forceinline__ void compute(const Lds& L, int nb, int wave, int kw, int lane,
+                                                 float4_t (&acc)[R16][T16]) {
+    const int l16 = lane & 15, g = lane >> 4;
+    const uint16_t* xs = reinterpret_cast<const uint16_t*>(L.xs4);
+    const uint8_t* cs = reinterpret_cast<const uint8_t*>(L.cs4);
+    const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int sq = 0; sq < NSB / KW; sq++) {
+      const int sb = kw * (NSB / KW) + sq;
+      if (sb >= nb) break;
+      const uint16_t* xb = xs + sb * NT * kLdsRow;
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const int u = 8 * sb + j;
+        bf16x8v_t Bop[R16];
+        float sc[R16];
+#pragma unroll
+        for (int tm = 0; tm < R16; tm++) {
+          const int rl = wave * 16 * R16 + 16 * tm + l16;
+          Bop[tm] = decode_codes(*reinterpret_cast<const uint32_t*>(cs + rl * kCodeRow + 16 * u + 4 * g));
+          sc[tm] = L.scs[rl * kScRow + u];
+        }
+#pragma unroll
+        for (int tn = 0; tn < T16; tn++) {
+          const bf16x8v_t Aop = *reinterpret_cast<const bf16x8v_t*>(xb + (16 * tn + l16) * kLdsRow + 32 * j + 8 * g);
+#pragma unroll
+          for (int tm = 0; tm < R16; tm++) {
+            const float4_t P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aop, Bop[tm], zero, 0, 0, 0);
+            float4_t& A = acc[tm][tn];
+            A.x = __builtin_fmaf(sc[tm], P.x, A.x);
+            A.y = __builtin_fmaf(sc[tm], P.y, A.y);
+            A.z = __builtin_fmaf(sc[tm], P.z, A.z);
+            A.w = __builtin_fmaf(sc[tm], P.w, A.w);
+          }
+        }
+#pragma unroll
+        for (int tm = 0; tm < R16; tm++)
+#pragma unroll
+          for (int tn = 0; tn < T16; tn++)
+            asm volatile("" : "+v"(acc[tm][tn].x), "+v"(acc[tm][tn].y), "+v"(acc[tm][tn].z), "+v"(acc[tm][tn].w));
+      }
+      if constexpr (AFFINE) {
+        // A = sum(x) [token][sub-block 4q + g], B = (8 s + a) [sub-block 4q + g][row]
+#pragma unroll
+        for (int tn = 0; tn < T16; tn++) {
+          const float* xq = L.xsum + (sb * NT + 16 * tn + l16) * 8 + g;
+#pragma unroll
+          for (int tm = 0; tm < R16; tm++) {
+            const float* co = L.cos_ + (wave * 16 * R16 + 16 * tm + l16) * kScRow + 8 * sb + g;
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[0], co[0], acc[tm][tn], 0, 0, 0);
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[4], co[4], acc[tm][tn], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // The K shares of a row tile meet in LDS (KW > 1; every thread calls this),
+  // then the waves of share 0 write (or, with K split over the grid, add) Y.
+  template <bool SPLIT>
+  static __device__ __forceinline__ void finish(float4_t (&acc)[R16][T16], float4_t* red, int wave, int kw,
+                                                int lane, int64_t m0, int n0, int M, int N, float* __restrict__ Y) {
+    const int l16 = lane & 15, g = lane >> 4;
+    if constexpr (KW > 1) {
+      if (kw > 0) {
+#pragma unroll
+        for (int tm = 0; tm < R16; tm++)
+#pragma unroll
+          for (int tn = 0; tn < T16; tn++)
+            red[((((kw - 1) * 4 + wave) * R16 + tm) * T16 + tn) * 64 + lane] = acc[tm][tn];
+      }
+      __syncthreads();
+      if (kw > 0) return;
+#pragma unroll
+      for (int q = 1; q < KW; q++)
+#pragma unroll
+        for (int tm = 0; tm < R16; tm++)
+#pragma unroll
+          for (int tn = 0; tn < T16; tn++) {
+            const float4_t o = red[((((q - 1) * 4 + wave) * R16 + tm) * T16 + tn) * 64 + lane];
+            acc[tm][tn].x += o.x;
+            acc[tm][tn].y += o.y;
+            acc[tm][tn].z += o.z;
+            acc[tm][tn].w += o.w;
+          }
+    }
+#pragma unroll
+    for (int tm = 0; tm < R16; tm++) {
+      const int64_t m = m0 + wave * 16 * R16 + 16 * tm + l16;
+      if (m >= M) continue;
+#pragma unroll
+      for (int tn = 0; tn < T16; tn++) {
+        const float v[4] = {acc[tm][tn].x, acc[tm][tn].y, acc[tm][tn].z, acc[tm][tn].w};
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const int n = n0 + 16 * tn + 4 * g + r;
+          if (n < N) {
+            float* dst = Y + static_cast<int64_t>(n) * M + m;
+            if constexpr (SPLIT) atomicAdd(dst, v[r]);
+            else *dst = v[r];
+          }
+        }
+      }
+    }
+  }
+};
+
+// One stage per workgroup: every load issued before the single barrier
+// (few tokens; the K range is split over the grid).
 template <int FMT, int R16, int T16, int NSB, int KW, bool SPLIT>
 __global__ __launch_bounds__(kThreads * KW) void k_gemm_u(const uint8_t* __restrict__ W,
                                                    const uint16_t* __restrict__ X,
                                                    float* __restrict__ Y, int M, int K, int N) {
-  using UU = UnitU<FMT>;
-  constexpr bool AFFINE = FMT == QBLK_SB4_AFFINE || FMT == QBLK_Q4_K;
-  constexpr int NT = 16 * T16;
-  constexpr int RW = 64 * R16;             // weight rows per workgroup
-  constexpr int UR = NSB * 8;              // units per row in the K slice
-  constexpr int kT = kThreads * KW;        // KW waves per 16*R16 rows, each a share of the groups
-  constexpr int kUPT = RW * UR / kT;       // units per thread
-  static_assert(RW * UR % kT == 0 && NSB % KW == 0, "whole units per thread, whole groups per wave");
-  constexpr int kCodeRow = UR * 16 + 16;   // bytes per staged row of codes
-  constexpr int kScRow = UR + 1;           // floats per staged row of scales
-  constexpr int kPieces = NSB * NT * 32;   // 16-byte pieces of the X slice
-  constexpr int kPer = (kPieces + kT - 1) / kT;
-  __shared__ uint4 xs4[NSB * NT * kLdsRow / 8];
-  __shared__ uint4 cs4[RW * kCodeRow / 16];
-  __shared__ float scs[RW * kScRow];
-  __shared__ float cos_[AFFINE ? RW * kScRow : 1];   // offset terms 8s + a
-  __shared__ float xsum[AFFINE ? NSB * NT * 8 : 1];  // [group][token][sub-block]
+  using St = UStage<FMT, R16, T16, NSB, KW>;
+  __shared__ typename St::Lds L;
   __shared__ float4_t red[KW > 1 ? (KW - 1) * 4 * R16 * T16 * 64 : 1];
   const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & 3, kw = threadIdx.x >> 8;
-  const int l16 = lane & 15, g = lane >> 4;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * RW;
-  const int n0 = blockIdx.y * NT;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * St::RW;
+  const int n0 = blockIdx.y * St::NT;
   const int ngr = K / 256;
   const int b0 = blockIdx.z * NSB;
   const int nb = min(NSB, ngr - b0);  // groups in this piece of K (>= 1)
-  const int64_t rowbytes = static_cast<int64_t>(ngr) * UU::GB;
+  const int64_t rowbytes = static_cast<int64_t>(ngr) * St::UU::GB;
 
-  // X first (L2-resident), then every unit of the tile.  Pieces past the
-  // slice's last group or past row M-1 / token N-1 re-read valid data that is
-  // never used or never stored.
-  uint4 xv[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; i++) {
-    const int c = min(static_cast<int>(threadIdx.x) + i * kT, kPieces - 1);
-    const int sb = c / (NT * 32), rem = c % (NT * 32);
-    const int t = min(n0 + (rem >> 5), N - 1), col = rem & 31;
-    const int b = b0 + min(sb, nb - 1);
-    xv[i] = *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(t) * K + 256 * b + 8 * col);
-  }
-  uint32_t raw[kUPT][UU::RAW];
-#pragma unroll
-  for (int i = 0; i < kUPT; i++) {
-    const int U = static_cast<int>(threadIdx.x) + i * kT;
-    const int r = U / UR, u = U % UR;
-    const int64_t m = m0 + r < M ? m0 + r : M - 1;
-    UU::load(W + m * rowbytes + static_cast<int64_t>(UU::GB) * (b0 + min(u >> 3, nb - 1)), u & 7, raw[i]);
-  }
-
-  uint16_t* xs = reinterpret_cast<uint16_t*>(xs4);
-#pragma unroll
-  for (int i = 0; i < kPer; i++) {
-    const int c = static_cast<int>(threadIdx.x) + i * kT;
-    const int sb = c / (NT * 32), rem = c % (NT * 32);
-    if (kPieces % kT == 0 || c < kPieces) {
-      // entries 8cc..8cc+7 of sub-block j go to the k-group slots 32j + 8g (+4)
-      const int j = (rem & 31) >> 2, cc = rem & 3;
-      const int g0 = 2 * (cc & 1), half = cc >> 1;
-      uint16_t* row = xs + (sb * NT + (rem >> 5)) * kLdsRow + 32 * j + 4 * half;
-      *reinterpret_cast<uint2*>(row + 8 * g0) = make_uint2(xv[i].x, xv[i].y);
-      *reinterpret_cast<uint2*>(row + 8 * (g0 + 1)) = make_uint2(xv[i].z, xv[i].w);
-    }
-    if constexpr (AFFINE) {
-      // sum of x over the sub-block: products with 1.0 are exact, fp32 sums;
-      // the 4 pieces of a sub-block sit on 4 adjacent lanes
-      const bf16x2v_t one = __builtin_bit_cast(bf16x2v_t, 0x3f803f80u);
-      float part = 0.0f;
-      part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].x), one, part, false);
-      part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].y), one, part, false);
-      part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].z), one, part, false);
-      part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, xv[i].w), one, part, false);
-      part = quad_sum(part);
-      if ((kPieces % kT == 0 || c < kPieces) && (c & 3) == 0)
-        xsum[(sb * NT + (rem >> 5)) * 8 + ((rem & 31) >> 2)] = part;
-    }
-  }
-  uint8_t* cs = reinterpret_cast<uint8_t*>(cs4);
-#pragma unroll
-  for (int i = 0; i < kUPT; i++) {
-    const int U = static_cast<int>(threadIdx.x) + i * kT;
-    const int r = U / UR, u = U % UR;
-    const int64_t m = m0 + r < M ? m0 + r : M - 1;
-    uint4 c;
-    float scale, corr;
-    UU::finish(W + m * rowbytes + static_cast<int64_t>(UU::GB) * (b0 + min(u >> 3, nb - 1)), u & 7, raw[i], c,
-               scale, corr);
-    *reinterpret_cast<uint4*>(cs + r * kCodeRow + 16 * u) = c;
-    scs[r * kScRow + u] = scale;
-    if constexpr (AFFINE) cos_[r * kScRow + u] = corr;
-  }
+  typename St::Regs r;
+  St::load(W, X, m0, n0, M, N, K, rowbytes, b0, nb, r);
+  St::store(L, r, W, m0, M, rowbytes, b0, nb);
   __syncthreads();
+  float4_t acc[R16][T16];
+#pragma unroll
+  for (int tm = 0; tm < R16; tm++)
+#pragma unroll
+    for (int tn = 0; tn < T16; tn++) acc[tm][tn] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  St::compute(L, nb, wave, kw, lane, acc);
+  St::template finish<SPLIT>(acc, red, wave, kw, lane, m0, n0, M, N, Y);
+}
+
+// Many stages per workgroup (tens of tokens): the workgroup walks its K
+// range NSB groups at a time; the loads of the next stage are issued into
+// registers before the products of the current one, so they arrive while it
+// runs, and are written to LDS between two barriers.  With the whole K range
+// in one workgroup no partial products are added into Y.
+template <int FMT, int R16, int T16, int NSB, int KW, bool SPLIT>
+__global__ __launch_bounds__(kThreads * KW) void k_gemm_s(const uint8_t* __restrict__ W,
+                                                   const uint16_t* __restrict__ X,
+                                                   float* __restrict__ Y, int M, int K, int N,
+                                                   int groups_per_split) {
+  using St = UStage<FMT, R16, T16, NSB, KW>;
+  __shared__ typename St::Lds L;
+  __shared__ float4_t red[KW > 1 ? (KW - 1) * 4 * R16 * T16 * 64 : 1];
+  const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & 3, kw = threadIdx.x >> 8;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * St::RW;
+  const int n0 = blockIdx.y * St::NT;
+  const int ngr = K / 256;
+  const int g_begin = blockIdx.z * groups_per_split;
+  const int g_end = min(ngr, g_begin + groups_per_split);
+  const int64_t rowbytes = static_cast<int64_t>(ngr) * St::UU::GB;
 
   float4_t acc[R16][T16];
 #pragma unroll
   for (int tm = 0; tm < R16; tm++)
 #pragma unroll
     for (int tn = 0; tn < T16; tn++) acc[tm][tn] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  const float4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
-
-#pragma unroll
-  for (int sq = 0; sq < NSB / KW; sq++) {
-    const int sb = kw * (NSB / KW) + sq;
-    if (sb >= nb) break;
-    const uint16_t* xb = xs + sb * NT * kLdsRow;
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const int u = 8 * sb + j;
-      bf16x8v_t Bop[R16];
-      float sc[R16];
-#pragma unroll
-      for (int tm = 0; tm < R16; tm++) {
-        const int rl = wave * 16 * R16 + 16 * tm + l16;
-        Bop[tm] = decode_codes(*reinterpret_cast<const uint32_t*>(cs + rl * kCodeRow + 16 * u + 4 * g));
-        sc[tm] = scs[rl * kScRow + u];
-      }
-#pragma unroll
-      for (int tn = 0; tn < T16; tn++) {
-        const bf16x8v_t Aop = *reinterpret_cast<const bf16x8v_t*>(xb + (16 * tn + l16) * kLdsRow + 32 * j + 8 * g);
-#pragma unroll
-        for (int tm = 0; tm < R16; tm++) {
-          const float4_t P = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aop, Bop[tm], zero, 0, 0, 0);
-          float4_t& A = acc[tm][tn];
-          A.x = __builtin_fmaf(sc[tm], P.x, A.x);
-          A.y = __builtin_fmaf(sc[tm], P.y, A.y);
-          A.z = __builtin_fmaf(sc[tm], P.z, A.z);
-          A.w = __builtin_fmaf(sc[tm], P.w, A.w);
-        }
-      }
-#pragma unroll
-      for (int tm = 0; tm < R16; tm++)
-#pragma unroll
-        for (int tn = 0; tn < T16; tn++)
-          asm volatile("" : "+v"(acc[tm][tn].x), "+v"(acc[tm][tn].y), "+v"(acc[tm][tn].z), "+v"(acc[tm][tn].w));
-    }
-    if constexpr (AFFINE) {
-      // A = sum(x) [token][sub-block 4q + g], B = (8 s + a) [sub-block 4q + g][row]
-#pragma unroll
-      for (int tn = 0; tn < T16; tn++) {
-        const float* xq = xsum + (sb * NT + 16 * tn + l16) * 8 + g;
-#pragma unroll
-        for (int tm = 0; tm < R16; tm++) {
-          const float* co = cos_ + (wave * 16 * R16 + 16 * tm + l16) * kScRow + 8 * sb + g;
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[0], co[0], acc[tm][tn], 0, 0, 0);
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[4], co[4], acc[tm][tn], 0, 0, 0);
-        }
-      }
-    }
-  }
-
-  if constexpr (KW > 1) {
-    // the K shares of a row tile meet in LDS
-    if (kw > 0) {
-#pragma unroll
-      for (int tm = 0; tm < R16; tm++)
-#pragma unroll
-        for (int tn = 0; tn < T16; tn++)
-          red[((((kw - 1) * 4 + wave) * R16 + tm) * T16 + tn) * 64 + lane] = acc[tm][tn];
-    }
+  typename St::Regs r;
+  if (g_begin < g_end) St::load(W, X, m0, n0, M, N, K, rowbytes, g_begin, min(NSB, g_end - g_begin), r);
+  for (int b = g_begin; b < g_end; b += NSB) {
+    const int nb = min(NSB, g_end - b);
+    if (b != g_begin) __syncthreads();  // every wave is done with the previous stage
+    St::store(L, r, W, m0, M, rowbytes, b, nb);
     __syncthreads();
-    if (kw > 0) return;
-#pragma unroll
-    for (int q = 1; q < KW; q++)
-#pragma unroll
-      for (int tm = 0; tm < R16; tm++)
-#pragma unroll
-        for (int tn = 0; tn < T16; tn++) {
-          const float4_t o = red[((((q - 1) * 4 + wave) * R16 + tm) * T16 + tn) * 64 + lane];
-          acc[tm][tn].x += o.x;
-          acc[tm][tn].y += o.y;
-          acc[tm][tn].z += o.z;
-          acc[tm][tn].w += o.w;
-        }
+    if (b + NSB < g_end) St::load(W, X, m0, n0, M, N, K, rowbytes, b + NSB, min(NSB, g_end - b - NSB), r);
+    St::compute(L, nb, wave, kw, lane, acc);
   }
-#pragma unroll
-  for (int tm = 0; tm < R16; tm++) {
-    const int64_t m = m0 + wave * 16 * R16 + 16 * tm + l16;
-    if (m >= M) continue;
-#pragma unroll
-    for (int tn = 0; tn < T16; tn++) {
-      const float v[4] = {acc[tm][tn].x, acc[tm][tn].y, acc[tm][tn].z, acc[tm][tn].w};
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int n = n0 + 16 * tn + 4 * g + r;
-        if (n < N) {
-          float* dst = Y + static_cast<int64_t>(n) * M + m;
-          if constexpr (SPLIT) atomicAdd(dst, v[r]);
-          else *dst = v[r];
-        }
-      }
-    }
-  }
+  St::template finish<SPLIT>(acc, red, wave, kw, lane, m0, n0, M, N, Y);
 }
 
 template <int FMT, int R16, int T16, int NSB, int KW = 1>
@@ -1335,23 +910,33 @@ hipError_t launch_u(const void* blocks, int64_t m, int64_t k, const void* x, int
   return hipGetLastError();
 }
 
-template <int R16, int T16, int NSB>
-hipError_t launch_s(const void* blocks, int64_t m, int64_t k, const void* x, int64_t n, float* y,
-                    hipStream_t s) {
+// Full K per workgroup unless the tiles alone leave CUs idle; then K is
+// split over the grid (partial products added into Y, zeroed first).
+template <int FMT, int R16, int T16, int NSB, int KW>
+hipError_t launch_st(const void* blocks, int64_t m, int64_t k, const void* x, int64_t n, float* y,
+                     hipStream_t s) {
   const unsigned gx = static_cast<unsigned>((m + 64 * R16 - 1) / (64 * R16));
   const unsigned gy = static_cast<unsigned>((n + 16 * T16 - 1) / (16 * T16));
   const int nsb = static_cast<int>(k / 256);
-  const unsigned gz = static_cast<unsigned>((nsb + NSB - 1) / NSB);
-  if (gz > 1) {
+  const int64_t tiles = static_cast<int64_t>(gx) * gy;
+  int split = 1;
+  if (2 * tiles <= cu_count_gemm()) {
+    split = static_cast<int>(cu_count_gemm() / tiles);
+    const int max_split = nsb / (2 * NSB) > 1 ? nsb / (2 * NSB) : 1;  // >= 2 stages per piece
+    split = split > max_split ? max_split : split;
+  }
+  const int per = (nsb + split - 1) / split;
+  split = (nsb + per - 1) / per;
+  if (split > 1) {
     const hipError_t e = launch_fill_zero(y, m * n, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_gemm_sb4_s<R16, T16, NSB, true>), dim3(gx, gy, gz), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((k_gemm_s<FMT, R16, T16, NSB, KW, true>), dim3(gx, gy, split), dim3(kThreads * KW), 0, s,
                        static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
-                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(n));
+                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), per);
   } else {
-    hipLaunchKernelGGL((k_gemm_sb4_s<R16, T16, NSB, false>), dim3(gx, gy, 1), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((k_gemm_s<FMT, R16, T16, NSB, KW, false>), dim3(gx, gy, 1), dim3(kThreads * KW), 0, s,
                        static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
-                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(n));
+                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), nsb);
   }
   return hipGetLastError();
 }
@@ -1361,35 +946,33 @@ hipError_t launch_s(const void* blocks, int64_t m, int64_t k, const void* x, int
 hipError_t launch_gemm(int fmt, const void* blocks, int64_t m, int64_t k, const void* x, int xt,
                        int64_t n, float* y, hipStream_t s) {
   (void)xt;  // only BF16 activations reach this point
-  // (sweeps at 14336 x 4096: up to 16 tokens the unit-loaded kernel with
-  // 64-row tiles takes 15.5-16.0 us for every format, against 20.7-34.7 us
-  // for the per-lane-loaded kernels -- Type 1 and Q4_K with two waves per
-  // row tile, each half of the K slice, 16.9 us with one; at 32 tokens it
-  // wins only for Q4_0, 26 us against 37, and k_gemm_sb4_s is best for
-  // Type 0, 24 us)
+  // (sweeps at 14336 x 4096: up to 16 tokens one stage per workgroup with
+  // K split over the grid, 15.5-16.0 us for every format -- Type 1 and Q4_K
+  // with two waves per row tile, 16.9 us with one; up to 64 tokens the
+  // streaming kernel over the whole K range, N = 32: 19.9-21.2 us (Q4_K
+  // 25.5) against 24.1-26.8 us for the double-buffered kernel it replaced,
+  // N = 64: 29.0-31.7 us (Q4_K 35.9) against 35.1-44.9 us (Q4_K 36.5))
   if (n <= 16) {
     if (fmt == QBLK_SB4) return launch_u<QBLK_SB4, 1, 1, 2>(blocks, m, k, x, n, y, s);
     if (fmt == QBLK_Q4_0) return launch_u<QBLK_Q4_0, 1, 1, 2>(blocks, m, k, x, n, y, s);
     if (fmt == QBLK_Q4_K) return launch_u<QBLK_Q4_K, 1, 1, 2, 2>(blocks, m, k, x, n, y, s);
     return launch_u<QBLK_SB4_AFFINE, 1, 1, 2, 2>(blocks, m, k, x, n, y, s);
   }
-  if (fmt == QBLK_SB4) {
-    if (n <= 32) return launch_s<2, 2, 2>(blocks, m, k, x, n, y, s);
-    if (n <= 64) return launch_t<QBLK_SB4, 2, 4>(blocks, m, k, x, n, y, s);
-    return launch_w<QBLK_SB4, 4>(blocks, m, k, x, n, y, s);
+  if (n <= 32) {
+    if (fmt == QBLK_SB4) return launch_st<QBLK_SB4, 1, 2, 2, 2>(blocks, m, k, x, n, y, s);
+    if (fmt == QBLK_Q4_0) return launch_st<QBLK_Q4_0, 1, 2, 2, 2>(blocks, m, k, x, n, y, s);
+    if (fmt == QBLK_Q4_K) return launch_st<QBLK_Q4_K, 1, 2, 2, 2>(blocks, m, k, x, n, y, s);
+    return launch_st<QBLK_SB4_AFFINE, 1, 2, 2, 2>(blocks, m, k, x, n, y, s);
   }
-  if (fmt == QBLK_Q4_0) {
-    if (n <= 32) return launch_u<QBLK_Q4_0, 1, 2, 2>(blocks, m, k, x, n, y, s);
-    if (n <= 64) return launch_t<QBLK_Q4_0, 2, 4>(blocks, m, k, x, n, y, s);
-    return launch_w<QBLK_Q4_0, 4>(blocks, m, k, x, n, y, s);
+  if (n <= 64) {
+    if (fmt == QBLK_SB4) return launch_st<QBLK_SB4, 1, 4, 2, 2>(blocks, m, k, x, n, y, s);
+    if (fmt == QBLK_Q4_0) return launch_st<QBLK_Q4_0, 1, 4, 2, 2>(blocks, m, k, x, n, y, s);
+    if (fmt == QBLK_Q4_K) return launch_st<QBLK_Q4_K, 1, 4, 2, 2>(blocks, m, k, x, n, y, s);
+    return launch_st<QBLK_SB4_AFFINE, 1, 4, 2, 2>(blocks, m, k, x, n, y, s);
   }
-  if (fmt == QBLK_Q4_K) {
-    if (n <= 32) return launch_t<QBLK_Q4_K, 1, 2>(blocks, m, k, x, n, y, s);
-    if (n <= 64) return launch_t<QBLK_Q4_K, 2, 4>(blocks, m, k, x, n, y, s);
-    return launch_w<QBLK_Q4_K, 4>(blocks, m, k, x, n, y, s);
-  }
-  if (n <= 32) return launch_t<QBLK_SB4_AFFINE, 1, 2>(blocks, m, k, x, n, y, s);
-  if (n <= 64) return launch_t<QBLK_SB4_AFFINE, 2, 4>(blocks, m, k, x, n, y, s);
+  if (fmt == QBLK_SB4) return launch_w<QBLK_SB4, 4>(blocks, m, k, x, n, y, s);
+  if (fmt == QBLK_Q4_0) return launch_w<QBLK_Q4_0, 4>(blocks, m, k, x, n, y, s);
+  if (fmt == QBLK_Q4_K) return launch_w<QBLK_Q4_K, 4>(blocks, m, k, x, n, y, s);
   return launch_w<QBLK_SB4_AFFINE, 4>(blocks, m, k, x, n, y, s);
 }
 

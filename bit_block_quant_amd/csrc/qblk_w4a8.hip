@@ -612,10 +612,10 @@ hipError_t launch_gemm_w4a8(const void* blocks, int64_t m, int64_t k, const int8
   if (n == 1 && k <= 8 * 64 * 32) return launch_v(codes, scales, m, k, xq, xs, y, s);
   // tilings measured at 14336 x 4096 and 4096 x 14336: up to N = 16 the
   // unit-loaded kernel, 64 rows x 4 groups per workgroup of 8 waves (N = 2 /
-  // 16: 12.0 / 14.8 us, against 16.4 / 17.9 us for k_gemm_w4a8 with K split
-  // three ways; 1, 2, 8 and 16 groups per workgroup and 4 or 16 waves were
-  // slower), then the wide kernel, 32 tokens (two groups per stage when the
-  // group count is even) up to N = 64, 128 tokens beyond
+  // 16: 12.0 / 14.8 us, against 16.4 / 17.9 us for operand-order loads with
+  // K split three ways; 1, 2, 8 and 16 groups per workgroup and 4 or 16
+  // waves were slower), then the wide kernel, 32 tokens (two groups per
+  // stage when the group count is even) up to N = 64, 128 tokens beyond
   const int64_t cus = cu_count_w4();
   if (n <= 16) return launch_mu<4, 2>(codes, scales, m, k, xq, xs, n, y, s);
   if (n <= 64) {
