@@ -911,7 +911,8 @@ hipError_t launch_u(const void* blocks, int64_t m, int64_t k, const void* x, int
 }
 
 // Full K per workgroup unless the tiles alone leave CUs idle; then K is
-// split over the grid (partial products added into Y, zeroed first).
+// split over the grid, for about two workgroups per CU (partial products
+// added into Y, zeroed first).
 template <int FMT, int R16, int T16, int NSB, int KW>
 hipError_t launch_st(const void* blocks, int64_t m, int64_t k, const void* x, int64_t n, float* y,
                      hipStream_t s) {
@@ -920,8 +921,8 @@ hipError_t launch_st(const void* blocks, int64_t m, int64_t k, const void* x, in
   const int nsb = static_cast<int>(k / 256);
   const int64_t tiles = static_cast<int64_t>(gx) * gy;
   int split = 1;
-  if (2 * tiles <= cu_count_gemm()) {
-    split = static_cast<int>(cu_count_gemm() / tiles);
+  if (tiles < cu_count_gemm()) {
+    split = static_cast<int>((2 * cu_count_gemm() + tiles - 1) / tiles);
     const int max_split = nsb / (2 * NSB) > 1 ? nsb / (2 * NSB) : 1;  // >= 2 stages per piece
     split = split > max_split ? max_split : split;
   }
@@ -949,26 +950,24 @@ hipError_t launch_gemm(int fmt, const void* blocks, int64_t m, int64_t k, const 
   // (sweeps at 14336 x 4096: up to 16 tokens one stage per workgroup with
   // K split over the grid, 15.5-16.0 us for every format -- Type 1 and Q4_K
   // with two waves per row tile, 16.9 us with one; up to 64 tokens the
-  // streaming kernel over the whole K range, N = 32: 19.9-21.2 us (Q4_K
-  // 25.5) against 24.1-26.8 us for the double-buffered kernel it replaced,
-  // N = 64: 29.0-31.7 us (Q4_K 35.9) against 35.1-44.9 us (Q4_K 36.5))
+  // streaming kernel over the whole K range with 32-token tiles (Q4_K: 16
+  // up to 32 tokens), N = 32: 19.9-22.3 us against 24.1-26.8 us for the
+  // double-buffered kernel it replaced, N = 64: 27.2-29.8 us against
+  // 35.1-44.9 us; 64-token tiles were 29-36 us at N = 64)
   if (n <= 16) {
     if (fmt == QBLK_SB4) return launch_u<QBLK_SB4, 1, 1, 2>(blocks, m, k, x, n, y, s);
     if (fmt == QBLK_Q4_0) return launch_u<QBLK_Q4_0, 1, 1, 2>(blocks, m, k, x, n, y, s);
     if (fmt == QBLK_Q4_K) return launch_u<QBLK_Q4_K, 1, 1, 2, 2>(blocks, m, k, x, n, y, s);
     return launch_u<QBLK_SB4_AFFINE, 1, 1, 2, 2>(blocks, m, k, x, n, y, s);
   }
-  if (n <= 32) {
+  if (n <= 64) {
     if (fmt == QBLK_SB4) return launch_st<QBLK_SB4, 1, 2, 2, 2>(blocks, m, k, x, n, y, s);
     if (fmt == QBLK_Q4_0) return launch_st<QBLK_Q4_0, 1, 2, 2, 2>(blocks, m, k, x, n, y, s);
-    if (fmt == QBLK_Q4_K) return launch_st<QBLK_Q4_K, 1, 2, 2, 2>(blocks, m, k, x, n, y, s);
+    if (fmt == QBLK_Q4_K) {
+      if (n <= 32) return launch_st<QBLK_Q4_K, 1, 1, 2, 2>(blocks, m, k, x, n, y, s);
+      return launch_st<QBLK_Q4_K, 1, 2, 2, 2>(blocks, m, k, x, n, y, s);
+    }
     return launch_st<QBLK_SB4_AFFINE, 1, 2, 2, 2>(blocks, m, k, x, n, y, s);
-  }
-  if (n <= 64) {
-    if (fmt == QBLK_SB4) return launch_st<QBLK_SB4, 1, 4, 2, 2>(blocks, m, k, x, n, y, s);
-    if (fmt == QBLK_Q4_0) return launch_st<QBLK_Q4_0, 1, 4, 2, 2>(blocks, m, k, x, n, y, s);
-    if (fmt == QBLK_Q4_K) return launch_st<QBLK_Q4_K, 1, 4, 2, 2>(blocks, m, k, x, n, y, s);
-    return launch_st<QBLK_SB4_AFFINE, 1, 4, 2, 2>(blocks, m, k, x, n, y, s);
   }
   if (fmt == QBLK_SB4) return launch_w<QBLK_SB4, 4>(blocks, m, k, x, n, y, s);
   if (fmt == QBLK_Q4_0) return launch_w<QBLK_Q4_0, 4>(blocks, m, k, x, n, y, s);
