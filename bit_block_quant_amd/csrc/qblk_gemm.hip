@@ -829,7 +829,9 @@ __global__ __launch_bounds__(kThreads * KW) void k_gemm_u(const uint8_t* __restr
   using St = UStage<FMT, R16, T16, NSB, KW>;
   __shared__ typename St::Lds L;
   __shared__ float4_t red[KW > 1 ? (KW - 1) * 4 * R16 * T16 * 64 : 1];
-  const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & 3, kw = threadIdx.x >> 8;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3);  // wave-uniform: scalar
+  const int kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * St::RW;
   const int n0 = blockIdx.y * St::NT;
   const int ngr = K / 256;
@@ -863,7 +865,9 @@ __global__ __launch_bounds__(kThreads * KW) void k_gemm_s(const uint8_t* __restr
   using St = UStage<FMT, R16, T16, NSB, KW>;
   __shared__ typename St::Lds L;
   __shared__ float4_t red[KW > 1 ? (KW - 1) * 4 * R16 * T16 * 64 : 1];
-  const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) & 3, kw = threadIdx.x >> 8;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3);  // wave-uniform: scalar
+  const int kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * St::RW;
   const int n0 = blockIdx.y * St::NT;
   const int ngr = K / 256;

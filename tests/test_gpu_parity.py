@@ -513,3 +513,87 @@ def test_w4a8_token_slices(q):
     for a, b in ((1, 2), (3, 9), (5, 6)):
         Ys = host(q.gemm_w4a8(bd, m, k, xq[a:b], s[a:b]))
         check_products(Ys, Y_ref[a:b], B[a:b], f"w4a8 tokens {a}:{b}")
+
+
+# ------------------------------------------------------- streams and graphs
+def test_side_stream(q):
+    # every step enqueues on the stream it is handed: the same calls on a
+    # second stream give the oracle's bytes and products
+    m, k = 150, 2304
+    w = mixed_blocks(m, k, 51)
+    x = np.random.default_rng(52).standard_normal(k).astype(np.float16)
+    X = WL.bf16_bits(np.random.default_rng(53).standard_normal((20, k)).astype(np.float32))
+    xa = act_rows(5, k, 54)
+    wd, xd, Xd, xad = dev(w), dev(x), dev_bf16(X), dev(xa)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):  # (the binding's default is the current stream)
+        b = q.quantize(wd, q.SB4, stream=side)
+        bw = q.quantize(wd, q.W4G128, stream=side)
+        deq = q.dequant(b, q.SB4, m, k, stream=side)
+        y = q.gemv(b, q.SB4, m, k, xd, stream=side)
+        Y = q.gemm(b, q.SB4, m, k, Xd, stream=side)
+        xq, s = q.quantize_act_i8(xad, stream=side)
+        Yw = q.gemm_w4a8(bw, m, k, xq, s, stream=side)
+    side.synchronize()
+    b_ref = O.quantize_sb4(w)
+    assert np.array_equal(host(b), b_ref)
+    assert np.array_equal(host(bw), O.quantize_w4g128(w))
+    assert np.array_equal(host(deq).view(np.uint32), O.dequant(O.SB4, b_ref, m, k).view(np.uint32))
+    y_ref, yb = O.gemv(O.SB4, b_ref, m, k, x.astype(np.float64))
+    check_products(host(y), y_ref, yb, "side-stream gemv")
+    Y_ref, Yb = O.gemm(O.SB4, b_ref, m, k, WL.bf16_values(X).astype(np.float64))
+    check_products(host(Y), Y_ref, Yb, "side-stream gemm")
+    xq_ref, s_ref = O.quantize_act_i8(xa)
+    Yw_ref, Ywb = O.gemm_w4a8(O.quantize_w4g128(w), m, k, xq_ref, s_ref)
+    check_products(host(Yw), Yw_ref, Ywb, "side-stream w4a8")
+
+
+def test_graph_replay(q):
+    # the products captured once into a HIP graph and replayed: the split-K
+    # GEMMs clear Y with a fill kernel inside the graph before adding their
+    # partial sums, so every replay must reproduce the product from a Y that
+    # eager work in between has overwritten
+    m, k = 150, 2304
+    w = mixed_blocks(m, k, 55)
+    b_ref, bw_ref = O.quantize_sb4(w), O.quantize_w4g128(w)
+    x = np.random.default_rng(56).standard_normal(k).astype(np.float16)
+    X = WL.bf16_bits(np.random.default_rng(57).standard_normal((16, k)).astype(np.float32))
+    X64 = WL.bf16_bits(np.random.default_rng(58).standard_normal((40, k)).astype(np.float32))
+    xa = act_rows(5, k, 59)
+    b, bw, xd, Xd, X64d = dev(b_ref), dev(bw_ref), dev(x), dev_bf16(X), dev_bf16(X64)
+    xq, s = q.quantize_act_i8(dev(xa))
+    y = torch.empty(m, device="cuda")
+    Y = torch.empty((16, m), device="cuda")
+    Y64 = torch.empty((40, m), device="cuda")
+    Yw = torch.empty((5, m), device="cuda")
+    cap = torch.cuda.Stream()
+
+    def step():
+        q.gemv(b, q.SB4, m, k, xd, out=y)
+        q.gemm(b, q.SB4, m, k, Xd, out=Y)        # one stage per workgroup, K split 5 ways
+        q.gemm(b, q.SB4, m, k, X64d, out=Y64)    # streaming kernel
+        q.gemm_w4a8(bw, m, k, xq, s, out=Yw)     # K split 5 ways
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(cap):
+        step()  # warm-up on the capture stream
+    cap.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        step()
+    y_ref, yb = O.gemv(O.SB4, b_ref, m, k, x.astype(np.float64))
+    Y_ref, Yb = O.gemm(O.SB4, b_ref, m, k, WL.bf16_values(X).astype(np.float64))
+    Y64_ref, Y64b = O.gemm(O.SB4, b_ref, m, k, WL.bf16_values(X64).astype(np.float64))
+    xq_ref, s_ref = O.quantize_act_i8(xa)
+    Yw_ref, Ywb = O.gemm_w4a8(bw_ref, m, k, xq_ref, s_ref)
+    for rep in range(3):
+        for t in (y, Y, Y64, Yw):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check_products(host(y), y_ref, yb, f"graph gemv, replay {rep}")
+        check_products(host(Y), Y_ref, Yb, f"graph gemm n=16, replay {rep}")
+        check_products(host(Y64), Y64_ref, Y64b, f"graph gemm n=40, replay {rep}")
+        check_products(host(Yw), Yw_ref, Ywb, f"graph w4a8 n=5, replay {rep}")
