@@ -610,17 +610,18 @@ hipError_t launch_gemm_w4a8(const void* blocks, int64_t m, int64_t k, const int8
   const uint8_t* codes = static_cast<const uint8_t*>(blocks);
   const uint16_t* scales = reinterpret_cast<const uint16_t*>(codes + m * k / 2);
   if (n == 1 && k <= 8 * 64 * 32) return launch_v(codes, scales, m, k, xq, xs, y, s);
-  // tilings measured at 14336 x 4096 and 4096 x 14336: up to N = 16 the
+  // tilings measured at 14336 x 4096 and 4096 x 14336: up to N = 32 the
   // unit-loaded kernel, 64 rows x 4 groups per workgroup of 8 waves (N = 2 /
   // 16: 12.0 / 14.8 us, against 16.4 / 17.9 us for operand-order loads with
   // K split three ways; 1, 2, 8 and 16 groups per workgroup and 4 or 16
-  // waves were slower), then the wide kernel: 32 tokens (two groups per
-  // stage when the group count is even) up to N = 64, 64 tokens up to
+  // waves were slower; N = 32: 20.5 us against 21.4-22.8 for the wide
+  // kernel), then the wide kernel: 32 tokens (two groups per stage when the
+  // group count is even) up to N = 64, 64 tokens up to
   // N = 256 (N = 200: 40 us against 61 for 128-token tiles, which leave CUs
   // idle at 14336 rows), 128 tokens beyond (N = 512: 69 us against 80; two
   // groups per stage spill at 128 tokens and lose at 64)
   const int64_t cus = cu_count_w4();
-  if (n <= 16) return launch_mu<4, 2>(codes, scales, m, k, xq, xs, n, y, s);
+  if (n <= 32) return launch_mu<4, 2>(codes, scales, m, k, xq, xs, n, y, s);
   if (n <= 64) {
     if ((k / 128) % 2 == 0) return launch_w<1, 2>(codes, scales, m, k, xq, xs, n, y, cus, s);
     return launch_w<1, 1>(codes, scales, m, k, xq, xs, n, y, cus, s);

@@ -458,7 +458,7 @@ def test_gemv_w4a8(q, shape):
     w4a8_case(q, m, k, 1, 36)
 
 
-@pytest.mark.parametrize("n", [2, 5, 16, 24, 40, 64, 100, 200])
+@pytest.mark.parametrize("n", [2, 5, 16, 24, 32, 33, 40, 64, 100, 200])
 def test_gemm_w4a8(q, n):
     w4a8_case(q, 150, 2304, n, 37)
 
@@ -481,7 +481,7 @@ def test_gemm_w4a8_odd_group_count(q, n):
     w4a8_case(q, 200, 1152, n, 39)
 
 
-@pytest.mark.parametrize("n", [16, 64, 512])
+@pytest.mark.parametrize("n", [16, 32, 64, 512])
 def test_gemm_w4a8_prefill_shape(q, n):
     w, X = WL.sb4_prefill("up", n)
     m, k = w.shape
