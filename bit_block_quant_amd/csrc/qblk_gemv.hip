@@ -285,18 +285,21 @@ __global__ __launch_bounds__(kThreads) void k_gemv(const uint8_t* __restrict__ b
 }
 
 // ===================================================================
-// fp16-x kernel: every load of a wave issued up front, no LDS, no barrier.
+// fp16-x kernel: every load of a wave issued up front, no LDS; one barrier
+// at the end when two waves share a row.
 //
 // The rows are split evenly over the workgroups (one 16-wave workgroup per
-// CU); wave w of a workgroup takes rows w, w+16, w+32 of its slice (RMAX of
-// them at most) and lane l takes units l, l+64, ... (UPL of them at most) of
-// each row.  A lane therefore sees the same units of x in every row: it
-// loads their 32 halves once, issued first, and forms the fp16 pairs in
-// registers (v_perm), to be reused for its RMAX rows.  All weight loads
-// follow, group by group -- unit k of row i, unit-major -- with the row base
-// in SGPRs and a fixed 32-bit offset per (lane, unit); the products consume
-// the groups in the same order, so each waits only for its own loads (the
-// load counter drains in issue order).  Nothing here waits for another wave.
+// CU).  With one wave per row (KS = 1) wave w of a workgroup takes rows w,
+// w+16, w+32 of its slice (RMAX of them at most) and lane l takes units l,
+// l+64, ... (UPL of them at most) of each row; with KS = 2 waves 2j and
+// 2j+1 take rows j, j+8, ... and split each row's units into two halves.  A
+// lane therefore sees the same units of x in every row: it loads their 32
+// halves once, issued first, and forms the fp16 pairs in registers (v_perm),
+// to be reused for its RMAX rows.  All weight loads follow, group by group
+// -- unit k of row i, unit-major -- with the row base in SGPRs and a fixed
+// 32-bit offset per (lane, unit); the products consume the groups in the
+// same order, so each waits only for its own loads (the load counter drains
+// in issue order).  No wave waits for another before its last product.
 //
 // Code groups of Q4_0 blocks and Type 0 sub-blocks start 2 bytes past a dword
 // boundary every other unit: a dword-aligned 16-byte load from just below,
@@ -445,19 +448,20 @@ __global__ __launch_bounds__(kThreadsH) void k_gemv_h(const uint8_t* __restrict_
       // and this group's loaded registers are "redefined" here, in order, so
       // neither can a later group's decode move up nor an earlier group's
       // products move down (either keeps several groups' decoded codes live).
-      // Not for Q4_K with two waves per row: there the pinned 16-byte headers
-      // would not fit in a wave's registers.
+      // Not for Q4_K with three units per lane: there the pinned 16-byte
+      // headers would not fit in a wave's registers.
       // A last row slot past the workgroup's rows repeats its last row
       // (loaded, to keep every wave's loads unconditional): its math is
-      // skipped (one wave per row only).  For the affine formats the compiler
-      // sinks that row's loads into the skip branch unless the pins below
-      // come first, so there the skip follows them; for Type 0 and Q4_0 it
-      // does not, and skipping before the pins is a little faster.
-      const bool dup = KS == 1 && i == RMAX - 1 && row0 + slot + SLOTS * i >= row_end;
+      // skipped (the wave still meets the barrier below when KS > 1).  For the
+      // affine formats the compiler sinks that row's loads into the skip
+      // branch unless the pins below come first, so there the skip follows
+      // them; for Type 0 and Q4_0 it does not, and skipping before the pins
+      // is a little faster.
+      const bool dup = i == RMAX - 1 && row0 + slot + SLOTS * i >= row_end;
       if constexpr (!AFFINE) {
         if (dup) continue;
       }
-      if constexpr (!(QK && KS > 1)) {  // (Q4_K with two waves per row: no registers to spare)
+      if constexpr (!(QK && UPL > 2)) {  // (Q4_K, three units per lane: no registers to spare)
 #pragma unroll
         for (int r = 0; r < RMAX; r++) asm volatile("" : "+v"(acc[r]));
         asm volatile("" : "+v"(q[i][k][0]), "+v"(q[i][k][1]), "+v"(q[i][k][2]), "+v"(q[i][k][3]), "+v"(q[i][k][4]));
@@ -596,25 +600,45 @@ inline int rows_per_wg(int64_t m, int slots, int rmax_cap) {
   return static_cast<int>(per);
 }
 
-// fp16 x and at most 384 units (12288 weights) per row: the up-front kernel,
-// 2 units per lane (one wave per row) or 3 (two waves per row).
+// Row slots per wave: the smallest template count R >= rmax, up to RCAP.
+template <int FMT, int UPL, int KS, int RCAP, int R = 1>
+hipError_t launch_h_r(int rmax, const void* blocks, int64_t m, int64_t k, const void* x, float* y,
+                      int rpw, hipStream_t s) {
+  if constexpr (R < RCAP) {
+    if (rmax > R) return launch_h_r<FMT, UPL, KS, RCAP, R + 1>(rmax, blocks, m, k, x, y, rpw, s);
+  }
+  return launch_h_t<FMT, R, UPL, KS>(blocks, m, k, x, y, rpw, s);
+}
+
+template <int FMT, int UPL, int KS, int RCAP>
+hipError_t launch_h_k(const void* blocks, int64_t m, int64_t k, const void* x, float* y, hipStream_t s) {
+  constexpr int slots = kWavesH / KS;
+  const int rpw = rows_per_wg(m, slots, RCAP);
+  return launch_h_r<FMT, UPL, KS, RCAP>((rpw + slots - 1) / slots, blocks, m, k, x, y, rpw, s);
+}
+
+// fp16 x and at most 384 units (12288 weights) per row: the up-front kernel.
+// Each wave loads x for every unit it covers and reuses it across its rows,
+// so x is re-read once per wave; splitting a row over two waves halves the x
+// each wave loads (it matters most when a CU holds few rows). By units per
+// row S: up to 64 one wave per row and one unit per lane; up to 128 two
+// waves per row with one unit per lane each, up to 6 rows per wave (at
+// 4096 x 4096: 4.8-4.9 -> 4.3-4.5 us; at 11008 x 4096 Q4_0 8.0 -> 7.7,
+// Type 1 7.6 -> 7.4, Q4_K 7.8 -> 7.5 us) -- except Type 0 with more than 32
+// rows per CU, which is as fast with one wave per row and two units per lane
+// (7.44 against 7.48 us at 11008 x 4096); up to 256 two waves per row with
+// two units per lane; up to 384 three.
 template <int FMT>
 bool launch_h(const void* blocks, int64_t m, int64_t k, const void* x, float* y, hipStream_t s,
               hipError_t* err) {
   const int64_t S = k / 32;
   if (S > 6 * 64) return false;
-  if (S <= 2 * 64) {
-    const int rpw = rows_per_wg(m, kWavesH, 3);
-    const int rmax = (rpw + kWavesH - 1) / kWavesH;
-    if (rmax == 1) *err = launch_h_t<FMT, 1, 2, 1>(blocks, m, k, x, y, rpw, s);
-    else if (rmax == 2) *err = launch_h_t<FMT, 2, 2, 1>(blocks, m, k, x, y, rpw, s);
-    else *err = launch_h_t<FMT, 3, 2, 1>(blocks, m, k, x, y, rpw, s);
-  } else {
-    const int rpw = rows_per_wg(m, kWavesH / 2, 2);
-    const int rmax = (rpw + kWavesH / 2 - 1) / (kWavesH / 2);
-    if (rmax == 1) *err = launch_h_t<FMT, 1, 3, 2>(blocks, m, k, x, y, rpw, s);
-    else *err = launch_h_t<FMT, 2, 3, 2>(blocks, m, k, x, y, rpw, s);
-  }
+  const int64_t per_cu = (m + cu_count() - 1) / cu_count();
+  if (S <= 64) *err = launch_h_k<FMT, 1, 1, 3>(blocks, m, k, x, y, s);
+  else if (S <= 128 && FMT == QBLK_SB4 && per_cu > 32) *err = launch_h_k<FMT, 2, 1, 3>(blocks, m, k, x, y, s);
+  else if (S <= 128) *err = launch_h_k<FMT, 1, 2, 6>(blocks, m, k, x, y, s);
+  else if (S <= 256) *err = launch_h_k<FMT, 2, 2, 3>(blocks, m, k, x, y, s);
+  else *err = launch_h_k<FMT, 3, 2, 2>(blocks, m, k, x, y, s);
   return true;
 }
 

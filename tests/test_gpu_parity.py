@@ -278,6 +278,32 @@ def test_gemv_stack_matrices(q):
         check_products(y, y_ref, bound, f"sb4a layer {layer} proj {p}")
 
 
+# fp16 x: every tiling of the up-front kernel (units of 32 weights per row S):
+# S <= 64 one wave per row; S <= 128 two waves per row, one unit per lane
+# (Type 0 beyond 32 rows per CU: one wave, two units per lane); S <= 256 two
+# units per lane; S <= 384 three -- with 1 to 6 row slots per wave (rows per
+# CU 2 .. 48 and beyond, on 256 CUs) and ragged halves (S = 33, 73).
+GEMV_TILINGS = [(300, 2048), (5000, 2048), (11008, 2048), (2048, 4096), (6144, 4096), (8192, 4096),
+                (10240, 4096), (12300, 4096), (500, 8192), (4096, 8192), (6200, 8192), (90, 1056),
+                (700, 2336)]
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: NAMES[f])
+@pytest.mark.parametrize("shape", GEMV_TILINGS, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_gemv_f16_tilings(q, fmt, shape):
+    m, k = shape
+    if fmt != q.Q4_0 and k % 256:
+        pytest.skip("super-block formats need k % 256 == 0")
+    rng = np.random.default_rng(m + k)
+    w = (rng.standard_normal((m, k)) * 0.02).astype(np.float32)
+    w[::7] *= 40.0  # rows of another magnitude
+    x = rng.standard_normal(k).astype(np.float16)
+    blocks = O.quantize(fmt, w)
+    y = host(q.gemv(dev(blocks), fmt, m, k, dev(x)))
+    y_ref, bound = O.gemv(fmt, blocks, m, k, x.astype(np.float64))
+    check_products(y, y_ref, bound, f"{NAMES[fmt]} {m}x{k} f16")
+
+
 def test_gemv_empty_k_writes_zeros(q):
     y = torch.full((33,), 7.0, device="cuda")
     q.gemv(torch.empty(0, dtype=torch.uint8, device="cuda"), q.SB4, 33, 0,
