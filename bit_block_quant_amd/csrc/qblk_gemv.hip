@@ -553,7 +553,12 @@ __global__ __launch_bounds__(256) void k_fill_zero(float* y, int64_t n) {
   if (blockIdx.x == 0 && threadIdx.x < (n & 3)) y[(n4 << 2) + threadIdx.x] = 0.0f;
 }
 
-constexpr int kRows = 4;
+// Rows per wave of the generic kernel (fp32 or bf16 x, or rows past 12288
+// weights): 2 measured faster than 4 at every size tried, by the number of
+// workgroups in flight for small matrices (256 x 4096 fp32 x, Q4_0: 9.1 ->
+// 5.9 us) and by loads in flight per lane for large ones (11008 x 4096
+// Type 0: 15.3 -> 12.1 us); 1 row per wave was slower on three of four.
+constexpr int kRows = 2;
 
 template <int FMT, int XT>
 hipError_t launch_t(const void* blocks, int64_t m, int64_t k, const void* x, float* y,
