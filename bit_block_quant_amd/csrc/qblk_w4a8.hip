@@ -67,7 +67,9 @@ __global__ __launch_bounds__(kWavesV * kWave) void k_gemv_w4a8(const uint8_t* __
   const int NG = K >> 7;  // groups per row
   const int64_t rowbytes = K >> 1;
 
-  // (1) the lane's activations, issued first
+  // (1) the lane's activations: chunk 0's issued first, chunk i's just before
+  // the weight groups of chunk i (so the first weight requests are not
+  // queued behind every activation request of the CU's waves)
   uint4 xl[UPL], xh[UPL];
   int cc[UPL];
   bool live[UPL];
@@ -76,10 +78,13 @@ __global__ __launch_bounds__(kWavesV * kWave) void k_gemv_w4a8(const uint8_t* __
     const int c = lane + 64 * i;
     live[i] = c < C;
     cc[i] = min(c, C - 1);
+  }
+  auto load_x = [&](int i) {
     const int8_t* p = xq + 128 * (cc[i] >> 2) + 16 * (cc[i] & 3);
     xl[i] = *reinterpret_cast<const uint4*>(p);
     xh[i] = *reinterpret_cast<const uint4*>(p + 64);
-  }
+  };
+  load_x(0);
   __builtin_amdgcn_sched_barrier(0);
 
   // (2) codes and scales of every (chunk, row), chunk-major
@@ -87,6 +92,10 @@ __global__ __launch_bounds__(kWavesV * kWave) void k_gemv_w4a8(const uint8_t* __
   uint32_t sc[RMAX][UPL];
 #pragma unroll
   for (int i = 0; i < UPL; i++) {
+    if (i > 0) {
+      load_x(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int r = 0; r < RMAX; r++) {
       const int row = min(row0 + wave + kWavesV * r, row_end - 1);
@@ -95,16 +104,14 @@ __global__ __launch_bounds__(kWavesV * kWave) void k_gemv_w4a8(const uint8_t* __
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // nothing may touch the activations before the weight loads are issued
-#pragma unroll
-  for (int i = 0; i < UPL; i++)
+  // (3) -8 * sum(xq) over each chunk's 32 activations, formed for chunk i
+  // just before its products, after an empty asm that "redefines" its
+  // activation registers there (nothing may touch them before every weight
+  // load is issued, and chunk i waits only for its own loads)
+  int corr[UPL];
+  auto chunk_corr = [&](int i) {
     asm volatile("" : "+v"(xl[i].x), "+v"(xl[i].y), "+v"(xl[i].z), "+v"(xl[i].w), "+v"(xh[i].x), "+v"(xh[i].y),
                  "+v"(xh[i].z), "+v"(xh[i].w)::"memory");
-
-  // (3) -8 * sum(xq) over each chunk's 32 activations
-  int corr[UPL];
-#pragma unroll
-  for (int i = 0; i < UPL; i++) {
     int s = dot4(xl[i].x, kOnes8, 0);
     s = dot4(xl[i].y, kOnes8, s);
     s = dot4(xl[i].z, kOnes8, s);
@@ -114,7 +121,7 @@ __global__ __launch_bounds__(kWavesV * kWave) void k_gemv_w4a8(const uint8_t* __
     s = dot4(xh[i].z, kOnes8, s);
     s = dot4(xh[i].w, kOnes8, s);
     corr[i] = -8 * s;
-  }
+  };
 
   // (4) products
   float acc[RMAX];
@@ -122,6 +129,7 @@ __global__ __launch_bounds__(kWavesV * kWave) void k_gemv_w4a8(const uint8_t* __
   for (int r = 0; r < RMAX; r++) acc[r] = 0.0f;
 #pragma unroll
   for (int i = 0; i < UPL; i++) {
+    chunk_corr(i);
 #pragma unroll
     for (int r = 0; r < RMAX; r++) {
       // one (chunk, row) group at a time: the accumulators and this group's
