@@ -51,11 +51,14 @@ def log(*a):
 
 
 class Timer:
-    """Capture `launch(i)` for i in range(n) into a HIP graph; time replays."""
+    """Capture `launch(i % n)` for i in range(n * rot) into a HIP graph (rot
+    passes over the n rotating inputs); time replays.  Short kernels take
+    several passes per graph so that the boundary between two replays is not
+    part of every few launches."""
 
-    def __init__(self, torch, launch, n):
+    def __init__(self, torch, launch, n, rot=1):
         self.torch = torch
-        self.n = n
+        self.n = n * rot
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
@@ -65,8 +68,8 @@ class Timer:
         torch.cuda.synchronize()
         self.g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.g):
-            for i in range(n):
-                launch(i)
+            for i in range(n * rot):
+                launch(i % n)
         torch.cuda.synchronize()
 
     def run(self, reps, warmup=1):
@@ -173,11 +176,14 @@ def main():
     algo_bytes = nbytes + 2 * K + 4 * M
     log(f"gemv sb4 {M}x{K}: {nbytes} B of blocks, {C} rotating copies ({C * nbytes / 2**20:.0f} MiB)")
 
-    # exactly `steps` launches: a graph of C (one per copy) replayed
-    # steps // C times, then a graph of the remaining steps % C
+    # exactly `steps` launches: a graph of G = whole passes over the C copies
+    # (up to 2000 launches) replayed steps // G times, then a graph of the
+    # remaining steps % G.  One graph per 24 launches instead measures the
+    # replay boundary as well (7.34-7.46 against 7.22 us per launch).
     launch = lambda i: q.gemv(copies[i % C], q.SB4, M, K, xd, out=yd)  # noqa: E731
-    full, rem = divmod(args.steps, C)
-    g_full = Timer(torch, launch, C)
+    G = C * max(1, min(args.steps, 2000) // C)
+    full, rem = divmod(args.steps, G)
+    g_full = Timer(torch, launch, C, G // C)
     g_rem = Timer(torch, launch, rem) if rem else None
     for i in range(args.warmup):  # untimed warmup launches
         launch(i)
@@ -316,8 +322,8 @@ def measure_rows(torch, q, WL, np, dev):
         C = n_copies(b0.numel())
         cps = [b0] + [b0.clone() for _ in range(C - 1)]
         y = torch.empty(m, dtype=torch.float32, device=dev)
-        t = Timer(torch, lambda i: q.gemv(cps[i], fmt, m, k, x, out=y), C)
-        ms = t.run(max(1, 400 // C))
+        t = Timer(torch, lambda i: q.gemv(cps[i], fmt, m, k, x, out=y), C, max(1, 400 // C))
+        ms = t.run(1)
         hbm_row(name, ms, b0.numel() + x.numel() * x.element_size() + 4 * m, m=m, k=k)
 
     w, x = WL.sb4_decode("down")
@@ -473,8 +479,8 @@ def w4a8_rows(torch, q, WL, np, dev):
     C = n_copies(b0.numel())
     cps = [b0] + [b0.clone() for _ in range(C - 1)]
     y = torch.empty((1, m), dtype=torch.float32, device=dev)
-    t = Timer(torch, lambda i: q.gemm_w4a8(cps[i], m, k, xq, xs, out=y), C)
-    row(f"gemv_w4a8_{m}x{k}_i8", t.run(max(1, 400 // C)), b0.numel() + k + 4 + 4 * m)
+    t = Timer(torch, lambda i: q.gemm_w4a8(cps[i], m, k, xq, xs, out=y), C, max(1, 400 // C))
+    row(f"gemv_w4a8_{m}x{k}_i8", t.run(1), b0.numel() + k + 4 + 4 * m)
     t = Timer(torch, lambda i: q.quantize_act_i8(xd, out=xq, scale=xs), 50)  # 50 launches per graph
     row(f"quantize_act_i8_1x{k}_f16", t.run(4), k * 2 + k + 4)
     del cps
