@@ -288,25 +288,26 @@ __global__ __launch_bounds__(kThreads) void k_gemv(const uint8_t* __restrict__ b
 // fp16-x kernel: every load of a wave issued up front, no LDS; one barrier
 // at the end when two waves share a row.
 //
-// The rows are split evenly over the workgroups (one 16-wave workgroup per
-// CU).  With one wave per row (KS = 1) wave w of a workgroup takes rows w,
-// w+16, w+32 of its slice (RMAX of them at most) and lane l takes units l,
-// l+64, ... (UPL of them at most) of each row; with KS = 2 waves 2j and
-// 2j+1 take rows j, j+8, ... and split each row's units into two halves.  A
+// The rows are split evenly over the workgroups (one workgroup of W = 12 or
+// 16 waves per CU).  With one wave per row (KS = 1) wave w of a workgroup
+// takes rows w, w+W, w+2W, ... of its slice (RMAX of them at most) and lane
+// l takes units l, l+64, ... (UPL of them at most) of each row; with KS = 2
+// waves 2j and 2j+1 take rows j, j+W/2, ... and split each row's units into
+// two halves.  A
 // lane therefore sees the same units of x in every row: it loads their 32
-// halves once, issued first, and forms the fp16 pairs in registers (v_perm),
-// to be reused for its RMAX rows.  All weight loads follow, group by group
-// -- unit k of row i, unit-major -- with the row base in SGPRs and a fixed
-// 32-bit offset per (lane, unit); the products consume the groups in the
-// same order, so each waits only for its own loads (the load counter drains
-// in issue order).  No wave waits for another before its last product.
+// halves once and forms the fp16 pairs in registers (v_perm), to be reused
+// for its RMAX rows.  The weight loads go out group by group -- unit k of
+// row i, unit-major -- with the row base in SGPRs and a fixed 32-bit offset
+// per (lane, unit), each unit's x just before its first group; the products
+// consume the groups in the same order, so each waits only for its own
+// loads (the load counter drains in issue order).  No wave waits for
+// another before its last product.
 //
 // Code groups of Q4_0 blocks and Type 0 sub-blocks start 2 bytes past a dword
 // boundary every other unit: a dword-aligned 16-byte load from just below,
 // plus the 2 bytes that spill past it, realigned with v_alignbyte.
 // ===================================================================
-constexpr int kWavesH = 16;
-constexpr int kThreadsH = kWavesH * kWave;
+constexpr int kWavesH = 16;  // waves per workgroup unless a launch says otherwise
 
 template <int FMT>
 struct UnitAddr {
@@ -320,16 +321,17 @@ struct UnitAddr {
 };
 
 // KS waves share a row (KS = 2 splits the row's units in two halves whose
-// sums meet in LDS after the only barrier of the kernel).
-template <int FMT, int RMAX, int UPL, int KS>
-__global__ __launch_bounds__(kThreadsH) void k_gemv_h(const uint8_t* __restrict__ blocks,
+// sums meet in LDS after the only barrier of the kernel); WAVES waves per
+// workgroup (one workgroup per CU).
+template <int FMT, int RMAX, int UPL, int KS, int WAVES = kWavesH>
+__global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restrict__ blocks,
                                                       const uint16_t* __restrict__ x,
                                                       float* __restrict__ y, int M, int K,
                                                       int rows_per_wg) {
   constexpr bool AFFINE = affine_fmt(FMT);
   constexpr bool QK = FMT == QBLK_Q4_K;
   constexpr int E = Fmt<FMT>::E, B = Fmt<FMT>::B;
-  constexpr int SLOTS = kWavesH / KS;  // rows in flight per workgroup round
+  constexpr int SLOTS = WAVES / KS;  // rows in flight per workgroup round
   const int S = K >> 5;                // units per row
   const int SP = (S + KS - 1) / KS;    // units per part
   const int lane = threadIdx.x & (kWave - 1);
@@ -538,7 +540,7 @@ __global__ __launch_bounds__(kThreadsH) void k_gemv_h(const uint8_t* __restrict_
       if (lane == kWave - 1 && r < row_end) y[r] = v;
     }
   } else {
-    __shared__ float part_sum[kWavesH][RMAX];
+    __shared__ float part_sum[WAVES][RMAX];
 #pragma unroll
     for (int i = 0; i < RMAX; i++) {
       const float v = wave_sum_dpp(acc[i]);
@@ -600,11 +602,11 @@ int cu_count() {
   return n;
 }
 
-template <int FMT, int RMAX, int UPL, int KS>
+template <int FMT, int RMAX, int UPL, int KS, int WAVES>
 hipError_t launch_h_t(const void* blocks, int64_t m, int64_t k, const void* x, float* y,
                       int rows_per_wg, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>((m + rows_per_wg - 1) / rows_per_wg);
-  hipLaunchKernelGGL((k_gemv_h<FMT, RMAX, UPL, KS>), dim3(grid), dim3(kThreadsH), 0, s,
+  hipLaunchKernelGGL((k_gemv_h<FMT, RMAX, UPL, KS, WAVES>), dim3(grid), dim3(WAVES * kWave), 0, s,
                      static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
                      static_cast<int>(m), static_cast<int>(k), rows_per_wg);
   return hipGetLastError();
@@ -620,20 +622,20 @@ inline int rows_per_wg(int64_t m, int slots, int rmax_cap) {
 }
 
 // Row slots per wave: the smallest template count R >= rmax, up to RCAP.
-template <int FMT, int UPL, int KS, int RCAP, int R = 1>
+template <int FMT, int UPL, int KS, int RCAP, int WAVES, int R = 1>
 hipError_t launch_h_r(int rmax, const void* blocks, int64_t m, int64_t k, const void* x, float* y,
                       int rpw, hipStream_t s) {
   if constexpr (R < RCAP) {
-    if (rmax > R) return launch_h_r<FMT, UPL, KS, RCAP, R + 1>(rmax, blocks, m, k, x, y, rpw, s);
+    if (rmax > R) return launch_h_r<FMT, UPL, KS, RCAP, WAVES, R + 1>(rmax, blocks, m, k, x, y, rpw, s);
   }
-  return launch_h_t<FMT, R, UPL, KS>(blocks, m, k, x, y, rpw, s);
+  return launch_h_t<FMT, R, UPL, KS, WAVES>(blocks, m, k, x, y, rpw, s);
 }
 
-template <int FMT, int UPL, int KS, int RCAP>
+template <int FMT, int UPL, int KS, int RCAP, int WAVES = kWavesH>
 hipError_t launch_h_k(const void* blocks, int64_t m, int64_t k, const void* x, float* y, hipStream_t s) {
-  constexpr int slots = kWavesH / KS;
+  constexpr int slots = WAVES / KS;
   const int rpw = rows_per_wg(m, slots, RCAP);
-  return launch_h_r<FMT, UPL, KS, RCAP>((rpw + slots - 1) / slots, blocks, m, k, x, y, rpw, s);
+  return launch_h_r<FMT, UPL, KS, RCAP, WAVES>((rpw + slots - 1) / slots, blocks, m, k, x, y, rpw, s);
 }
 
 // fp16 x and at most 384 units (12288 weights) per row: the up-front kernel.
@@ -643,18 +645,21 @@ hipError_t launch_h_k(const void* blocks, int64_t m, int64_t k, const void* x, f
 // row S: up to 64 one wave per row and one unit per lane; up to 128 two
 // waves per row with one unit per lane each, up to 6 rows per wave (at
 // 4096 x 4096: 4.8-4.9 -> 4.3-4.5 us; at 11008 x 4096 Q4_0 8.0 -> 7.7,
-// Type 1 7.6 -> 7.4, Q4_K 7.8 -> 7.5 us) -- except Type 0 with more than 32
-// rows per CU, which is as fast with one wave per row and two units per lane
-// (7.44 against 7.48 us at 11008 x 4096); up to 256 two waves per row with
-// two units per lane; up to 384 three.
+// Type 1 7.6 -> 7.4, Q4_K 7.8 -> 7.5 us) -- except Type 0 and Q4_0 with
+// more than 32 rows per CU: one wave per row, two units per lane, 12-wave
+// workgroups with up to 4 rows per wave (11008 x 4096: Type 0 7.05 us
+// against 7.11 with 16 waves and 7.34 with two waves per row; Q4_0 7.56
+// against 7.64); up to 256 two waves per row with two units per lane; up to
+// 384 three.
 template <int FMT>
 bool launch_h(const void* blocks, int64_t m, int64_t k, const void* x, float* y, hipStream_t s,
               hipError_t* err) {
   const int64_t S = k / 32;
   if (S > 6 * 64) return false;
   const int64_t per_cu = (m + cu_count() - 1) / cu_count();
+  constexpr bool kSigned = FMT == QBLK_SB4 || FMT == QBLK_Q4_0;
   if (S <= 64) *err = launch_h_k<FMT, 1, 1, 3>(blocks, m, k, x, y, s);
-  else if (S <= 128 && FMT == QBLK_SB4 && per_cu > 32) *err = launch_h_k<FMT, 2, 1, 3>(blocks, m, k, x, y, s);
+  else if (S <= 128 && kSigned && per_cu > 32) *err = launch_h_k<FMT, 2, 1, 4, 12>(blocks, m, k, x, y, s);
   else if (S <= 128) *err = launch_h_k<FMT, 1, 2, 6>(blocks, m, k, x, y, s);
   else if (S <= 256) *err = launch_h_k<FMT, 2, 2, 3>(blocks, m, k, x, y, s);
   else *err = launch_h_k<FMT, 3, 2, 2>(blocks, m, k, x, y, s);
