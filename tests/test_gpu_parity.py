@@ -477,9 +477,10 @@ def w4a8_case(q, m, k, n, seed, rows=None):
     check_products(Y if rows is None else Y[:, rows], Y_ref, B, f"w4a8 {m}x{k} n={n}")
 
 
-# one token: chunks per lane 1..8 (k = 128 .. 16384) and 1..3 rows per wave;
-# k = 16512 takes the matrix-core path with n = 1
-@pytest.mark.parametrize("shape", [(37, 128), (150, 2304), (300, 4096), (11008, 4096), (77, 11008),
+# one token: chunks per lane 1..8 (k = 128 .. 16384) and 1..3 rows per wave
+# (12-wave workgroups with 3 or 4 rows per wave beyond 32 rows per CU at
+# k = 4096); k = 16512 takes the matrix-core path with n = 1
+@pytest.mark.parametrize("shape", [(37, 128), (150, 2304), (300, 4096), (8704, 4096), (11008, 4096), (12300, 4096), (77, 11008),
                                    (600, 14336), (40, 16384), (20, 16512)], ids=lambda s: f"{s[0]}x{s[1]}")
 def test_gemv_w4a8(q, shape):
     m, k = shape
