@@ -18,8 +18,9 @@
 // nibble into the mantissa of 1024.0 (0x6400) and subtracting 1032 (or, for
 // the high nibbles, which sit 4 bits up, 1024 + 16*8 giving 16*(code-8));
 // v_dot2_f32_f16 then forms exact fp16 x fp16 products and accumulates them in
-// fp32.  To pair codes with x without shuffling the codes, x is staged in LDS
-// in the matching order: for code word t (bytes 4t..4t+3 of a unit) the pairs
+// fp32.  To pair codes with x without shuffling the codes, x is put in the
+// matching order once (in LDS by the generic kernel, in registers with v_perm
+// by the fp16-x kernel below): for code word t (bytes 4t..4t+3 of a unit) the pairs
 // are (x[4t], x[4t+2]), (x[4t+16], x[4t+18]), (x[4t+1], x[4t+3]),
 // (x[4t+17], x[4t+19]).  The unit's fp32 scale multiplies the two partial
 // sums; Type 1 and Q4_K add offset * sum(x over the unit) (Q4_K's offset is
