@@ -287,7 +287,7 @@ def test_gemv_stack_matrices(q):
 # rows than waves on every branch, and a one-unit row (S = 1).
 GEMV_TILINGS = [(300, 2048), (5000, 2048), (11008, 2048), (2048, 4096), (6144, 4096), (8192, 4096), (8704, 4096),
                 (10240, 4096), (12300, 4096), (500, 8192), (4096, 8192), (6200, 8192), (90, 1056),
-                (700, 2336), (3, 1024), (3, 4096), (5, 8192), (2, 11264), (7, 32)]
+                (700, 2336), (9000, 2336), (3, 1024), (3, 4096), (5, 8192), (2, 11264), (7, 32)]
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: NAMES[f])
