@@ -651,7 +651,9 @@ hipError_t launch_h_k(const void* blocks, int64_t m, int64_t k, const void* x, f
 // workgroups with up to 4 rows per wave (11008 x 4096: Type 0 7.05 us
 // against 7.11 with 16 waves and 7.34 with two waves per row; Q4_0 7.56
 // against 7.64); up to 256 two waves per row with two units per lane; up to
-// 384 three.
+// 384 three (Type 0 in 12-wave workgroups with up to 3 rows per wave: 4096 x
+// 11008 7.98 against 8.20 us; the other formats gain 1.4% at most, and Q4_K
+// runs out of registers).
 template <int FMT>
 bool launch_h(const void* blocks, int64_t m, int64_t k, const void* x, float* y, hipStream_t s,
               hipError_t* err) {
@@ -663,6 +665,7 @@ bool launch_h(const void* blocks, int64_t m, int64_t k, const void* x, float* y,
   else if (S <= 128 && kSigned && per_cu > 32) *err = launch_h_k<FMT, 2, 1, 4, 12>(blocks, m, k, x, y, s);
   else if (S <= 128) *err = launch_h_k<FMT, 1, 2, 6>(blocks, m, k, x, y, s);
   else if (S <= 256) *err = launch_h_k<FMT, 2, 2, 3>(blocks, m, k, x, y, s);
+  else if (FMT == QBLK_SB4) *err = launch_h_k<FMT, 3, 2, 3, 12>(blocks, m, k, x, y, s);
   else *err = launch_h_k<FMT, 3, 2, 2>(blocks, m, k, x, y, s);
   return true;
 }

@@ -282,12 +282,12 @@ def test_gemv_stack_matrices(q):
 # S <= 64 one wave per row; S <= 128 two waves per row, one unit per lane
 # (Type 0 and Q4_0 beyond 32 rows per CU: 12-wave workgroups, one wave per
 # row, two units per lane, 3 or 4 row slots per wave); S <= 256 two
-# units per lane; S <= 384 three -- with 1 to 6 row slots per wave (rows per
+# units per lane; S <= 384 three (Type 0 in 12-wave workgroups) -- with 1 to 6 row slots per wave (rows per
 # CU 2 .. 48 and beyond, on 256 CUs), ragged halves (S = 33, 73), fewer
 # rows than waves on every branch, and a one-unit row (S = 1).
 GEMV_TILINGS = [(300, 2048), (5000, 2048), (11008, 2048), (2048, 4096), (6144, 4096), (8192, 4096), (8704, 4096),
                 (10240, 4096), (12300, 4096), (500, 8192), (4096, 8192), (6200, 8192), (90, 1056),
-                (700, 2336), (9000, 2336), (3, 1024), (3, 4096), (5, 8192), (2, 11264), (7, 32)]
+                (700, 2336), (9000, 2336), (2560, 11008), (3, 1024), (3, 4096), (5, 8192), (2, 11264), (7, 32)]
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: NAMES[f])
