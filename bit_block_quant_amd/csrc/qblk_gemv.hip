@@ -323,8 +323,12 @@ struct UnitAddr {
 
 // KS waves share a row (KS = 2 splits the row's units in two halves whose
 // sums meet in LDS after the only barrier of the kernel); WAVES waves per
-// workgroup (one workgroup per CU).
-template <int FMT, int RMAX, int UPL, int KS, int WAVES = kWavesH>
+// workgroup (one workgroup per CU).  XL (one wave per row only): x is loaded
+// once per workgroup -- every thread a few 4-element pieces, ahead of its
+// weight loads -- written to LDS already paired, published with one barrier
+// that waits for LDS only, and read back per unit; for few rows per CU, where
+// every wave re-reading all of x would cost more than the weights.
+template <int FMT, int RMAX, int UPL, int KS, int WAVES = kWavesH, bool XL = false>
 __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restrict__ blocks,
                                                       const uint16_t* __restrict__ x,
                                                       float* __restrict__ y, int M, int K,
@@ -340,7 +344,9 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restr
   const int slot = wave / KS, part = wave % KS;
   const int row0 = blockIdx.x * rows_per_wg;
   const int row_end = min(M, row0 + rows_per_wg);
-  if (KS == 1 && row0 + slot >= row_end) return;  // (KS > 1: every wave meets the barrier)
+  static_assert(!XL || KS == 1, "x through LDS: one wave per row");
+  // (KS > 1 or XL: every wave meets the barrier)
+  if (KS == 1 && !XL && row0 + slot >= row_end) return;
   const int64_t rowbytes = static_cast<int64_t>(K / E) * B;
 
   // per (lane, unit): byte offsets inside a row of the codes, the scale
@@ -367,16 +373,30 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restr
   // (Q4_K with three units per lane, whose groups are not pinned below, keeps
   // the old order -- every x load first, every unit's pairs formed before the
   // first product: the later forms cost it registers it does not have.)
-  constexpr bool kLateX = !(QK && UPL > 2);
+  constexpr bool kLateX = !XL && !(QK && UPL > 2);
   uint4 xr[UPL][4];
+  // XL: this thread's pieces of x (4 elements each) for the LDS copy; units
+  // past the row's last one are written as zeros
+  constexpr int kPieces = XL ? UPL * 64 * 8 : 0;  // 8 pieces per unit
+  constexpr int kPPT = XL ? (kPieces + WAVES * kWave - 1) / (WAVES * kWave) : 1;
+  uint2 xp[kPPT];
+  if constexpr (XL) {
+#pragma unroll
+    for (int j = 0; j < kPPT; j++) {  // unconditional loads (clamped), so the waits stay in order
+      const int pc = min(static_cast<int>(threadIdx.x) + j * WAVES * kWave, 8 * S - 1);
+      xp[j] = *reinterpret_cast<const uint2*>(x + 4 * pc);
+    }
+  }
   auto load_x = [&](int k) {
     const int u = min(part * SP + lane + 64 * k, S - 1);
     const uint4* p = reinterpret_cast<const uint4*>(x + 32 * u);
 #pragma unroll
     for (int c = 0; c < 4; c++) xr[k][c] = p[c];
   };
+  if constexpr (!XL) {
 #pragma unroll
-  for (int k = 0; k < (kLateX ? 1 : UPL); k++) load_x(k);
+    for (int k = 0; k < (kLateX ? 1 : UPL); k++) load_x(k);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // (2) every weight load of this wave, group by group
@@ -426,7 +446,44 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restr
   uint4 X[UPL][4];
   float sx[UPL];
   const half2_t kOne = {1.0f16, 1.0f16};
+  // XL: pairs of unit lane + 64k, word t, at xs[(4k + t) * 64 + lane]
+  __shared__ uint4 xs[XL ? UPL * 4 * 64 : 1];
+  if constexpr (XL) {
+#pragma unroll
+    for (int j = 0; j < kPPT; j++) {
+      const int pc = static_cast<int>(threadIdx.x) + j * WAVES * kWave;
+      uint2 v = xp[j];
+      asm volatile("" : "+v"(v.x), "+v"(v.y)::"memory");  // waits for this piece only
+      if (pc >= 8 * S) v = make_uint2(0u, 0u);  // units past the row's last one
+      if (pc < kPieces) {
+        const int u = pc >> 3, q = pc & 7, t = q & 3, hh = q >> 2;
+        uint32_t* w = reinterpret_cast<uint32_t*>(xs + (4 * (u >> 6) + t) * 64 + (u & 63));
+        w[hh] = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);      // (x0, x2)
+        w[2 + hh] = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);  // (x1, x3)
+      }
+    }
+    // publish: LDS writes done, then the workgroup barrier; the memory clobber
+    // keeps every LDS access on its side (a fence here would also wait for
+    // the weight loads in flight)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (row0 + slot >= row_end) return;
+  }
   auto make_pairs = [&](int k) {
+    if constexpr (XL) {
+#pragma unroll
+      for (int t = 0; t < 4; t++) X[k][t] = xs[(4 * k + t) * 64 + lane];
+      sx[k] = 0.0f;
+      if constexpr (AFFINE) {
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          sx[k] = __builtin_amdgcn_fdot2(as_h2(X[k][t].x), kOne, sx[k], false);
+          sx[k] = __builtin_amdgcn_fdot2(as_h2(X[k][t].y), kOne, sx[k], false);
+          sx[k] = __builtin_amdgcn_fdot2(as_h2(X[k][t].z), kOne, sx[k], false);
+          sx[k] = __builtin_amdgcn_fdot2(as_h2(X[k][t].w), kOne, sx[k], false);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < 4; c++)
       asm volatile("" : "+v"(xr[k][c].x), "+v"(xr[k][c].y), "+v"(xr[k][c].z), "+v"(xr[k][c].w)::"memory");
@@ -444,7 +501,8 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restr
     }
   };
 
-  if constexpr (!kLateX) {
+  constexpr bool kLazyPairs = kLateX || XL;  // each unit's pairs just before its products
+  if constexpr (!kLazyPairs) {
 #pragma unroll
     for (int k = 0; k < UPL; k++) make_pairs(k);
   }
@@ -458,7 +516,7 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restr
   for (int i = 0; i < RMAX; i++) acc[i] = 0.0f;
 #pragma unroll
   for (int k = 0; k < UPL; k++) {
-    if constexpr (kLateX) make_pairs(k);
+    if constexpr (kLazyPairs) make_pairs(k);
 #pragma unroll
     for (int i = 0; i < RMAX; i++) {
       // one group at a time: the accumulators (written by the groups before)
@@ -474,7 +532,9 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restr
       // branch unless the pins below come first, so there the skip follows
       // them; for Type 0 and Q4_0 it does not, and skipping before the pins
       // is a little faster.
-      const bool dup = i == RMAX - 1 && row0 + slot + SLOTS * i >= row_end;
+      // (one slot per wave and one wave per row: a wave without a row has
+      // returned, so there is nothing to skip and no branch to merge)
+      const bool dup = (RMAX > 1 || KS > 1) && i == RMAX - 1 && row0 + slot + SLOTS * i >= row_end;
       if constexpr (!AFFINE) {
         if (dup) continue;
       }
@@ -603,11 +663,11 @@ int cu_count() {
   return n;
 }
 
-template <int FMT, int RMAX, int UPL, int KS, int WAVES>
+template <int FMT, int RMAX, int UPL, int KS, int WAVES, bool XL = false>
 hipError_t launch_h_t(const void* blocks, int64_t m, int64_t k, const void* x, float* y,
                       int rows_per_wg, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>((m + rows_per_wg - 1) / rows_per_wg);
-  hipLaunchKernelGGL((k_gemv_h<FMT, RMAX, UPL, KS, WAVES>), dim3(grid), dim3(WAVES * kWave), 0, s,
+  hipLaunchKernelGGL((k_gemv_h<FMT, RMAX, UPL, KS, WAVES, XL>), dim3(grid), dim3(WAVES * kWave), 0, s,
                      static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
                      static_cast<int>(m), static_cast<int>(k), rows_per_wg);
   return hipGetLastError();
@@ -653,7 +713,11 @@ hipError_t launch_h_k(const void* blocks, int64_t m, int64_t k, const void* x, f
 // against 7.64); up to 256 two waves per row with two units per lane; up to
 // 384 three (Type 0 in 12-wave workgroups with up to 3 rows per wave: 4096 x
 // 11008 7.98 against 8.20 us; the other formats gain 1.4% at most, and Q4_K
-// runs out of registers).
+// runs out of registers).  With at most 16 rows per CU, x read by every wave
+// outweighs the weights; x through LDS (one wave per row) is taken where it
+// measured faster: Q4_0 up to 128 units (4096 x 4096: 4.44 -> 4.00 us) and
+// Type 1 beyond 256 (4096 x 11008: 8.35 -> 7.68 us); for Type 0 and Q4_K it
+// was not (4096 x 4096 within 2%, 4096 x 11008 Type 0 +9%).
 template <int FMT>
 bool launch_h(const void* blocks, int64_t m, int64_t k, const void* x, float* y, hipStream_t s,
               hipError_t* err) {
@@ -661,7 +725,12 @@ bool launch_h(const void* blocks, int64_t m, int64_t k, const void* x, float* y,
   if (S > 6 * 64) return false;
   const int64_t per_cu = (m + cu_count() - 1) / cu_count();
   constexpr bool kSigned = FMT == QBLK_SB4 || FMT == QBLK_Q4_0;
+  const bool few = per_cu <= kWavesH;  // one row per wave at most
   if (S <= 64) *err = launch_h_k<FMT, 1, 1, 3>(blocks, m, k, x, y, s);
+  else if (S <= 128 && FMT == QBLK_Q4_0 && few)
+    *err = launch_h_t<FMT, 1, 2, 1, kWavesH, true>(blocks, m, k, x, y, rows_per_wg(m, kWavesH, 1), s);
+  else if (S > 256 && FMT == QBLK_SB4_AFFINE && few)
+    *err = launch_h_t<FMT, 1, 6, 1, kWavesH, true>(blocks, m, k, x, y, rows_per_wg(m, kWavesH, 1), s);
   else if (S <= 128 && kSigned && per_cu > 32) *err = launch_h_k<FMT, 2, 1, 4, 12>(blocks, m, k, x, y, s);
   else if (S <= 128) *err = launch_h_k<FMT, 1, 2, 6>(blocks, m, k, x, y, s);
   else if (S <= 256) *err = launch_h_k<FMT, 2, 2, 3>(blocks, m, k, x, y, s);
