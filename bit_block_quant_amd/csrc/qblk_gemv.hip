@@ -634,22 +634,31 @@ __global__ __launch_bounds__(256) void k_fill_zero(float* y, int64_t n) {
 // weights): 2 measured faster than 4 at every size tried, by the number of
 // workgroups in flight for small matrices (256 x 4096 fp32 x, Q4_0: 9.1 ->
 // 5.9 us) and by loads in flight per lane for large ones (11008 x 4096
-// Type 0: 15.3 -> 12.1 us); 1 row per wave was slower on three of four.
+// Type 0: 15.3 -> 12.1 us); 1 row per wave was slower on three of four --
+// all but Q4_0 with few rows, which takes it (256 x 4096 fp32 x: 5.9 ->
+// 4.5 us; Type 0 there 4.6 -> 6.0 us, Q4_0 at 4096 rows 6.95 against 7.00).
 constexpr int kRows = 2;
 
-template <int FMT, int XT>
-hipError_t launch_t(const void* blocks, int64_t m, int64_t k, const void* x, float* y,
-                    hipStream_t s) {
+template <int FMT, int XT, int R>
+hipError_t launch_tr(const void* blocks, int64_t m, int64_t k, const void* x, float* y,
+                     hipStream_t s) {
   constexpr bool XH = XT == QBLK_F16;
   constexpr int KC = XH ? kChunkF16 : kChunkF32;
   const int64_t kc = k < KC ? k : KC;
   const size_t lds = (XH ? kc * 2 : kc * 4) + (kc / 32) * 4;
-  const int64_t groups = (m + kRows - 1) / kRows;
+  const int64_t groups = (m + R - 1) / R;
   const unsigned grid = static_cast<unsigned>((groups + kWaves - 1) / kWaves);
-  hipLaunchKernelGGL((k_gemv<FMT, XT, kRows>), dim3(grid), dim3(kThreads), lds, s,
+  hipLaunchKernelGGL((k_gemv<FMT, XT, R>), dim3(grid), dim3(kThreads), lds, s,
                      static_cast<const uint8_t*>(blocks), x, y, static_cast<int>(m),
                      static_cast<int>(k));
   return hipGetLastError();
+}
+
+template <int FMT, int XT>
+hipError_t launch_t(const void* blocks, int64_t m, int64_t k, const void* x, float* y,
+                    hipStream_t s) {
+  if (FMT == QBLK_Q4_0 && m <= 1024) return launch_tr<FMT, XT, 1>(blocks, m, k, x, y, s);
+  return launch_tr<FMT, XT, kRows>(blocks, m, k, x, y, s);
 }
 
 int cu_count() {

@@ -202,7 +202,7 @@ def x_dev(x):
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: NAMES[f])
 @pytest.mark.parametrize("xt", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("shape", [(1, 256), (37, 2304), (130, 11008)], ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("shape", [(1, 256), (37, 2304), (130, 11008), (1500, 1024)], ids=lambda s: f"{s[0]}x{s[1]}")
 def test_gemv_tolerance(q, fmt, xt, shape):
     m, k = shape
     w = mixed_blocks(m, k, 7 + m)
