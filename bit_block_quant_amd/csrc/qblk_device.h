@@ -151,6 +151,14 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t b
   return r;
 }
 
+// a.lo*b.lo + a.hi*b.hi in fp32 (v_dot2_f32_f16 with a zero addend in the
+// instruction itself, so no register has to be zeroed first)
+__device__ __forceinline__ float dot2_first(half2_t a, uint32_t b) {
+  float r;
+  asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // ---------------------------------------------------------------- waves
 // Sum over the 64 lanes of a wave with DPP moves; the total lands in lane 63.
 __device__ __forceinline__ float wave_sum_dpp(float v) {

@@ -323,12 +323,15 @@ struct UnitAddr {
 
 // KS waves share a row (KS = 2 splits the row's units in two halves whose
 // sums meet in LDS after the only barrier of the kernel); WAVES waves per
-// workgroup (one workgroup per CU).  XL (one wave per row only): x is loaded
-// once per workgroup -- every thread a few 4-element pieces, ahead of its
-// weight loads -- written to LDS already paired, published with one barrier
-// that waits for LDS only, and read back per unit; for few rows per CU, where
-// every wave re-reading all of x would cost more than the weights.
-template <int FMT, int RMAX, int UPL, int KS, int WAVES = kWavesH, bool XL = false>
+// workgroup (one workgroup per CU).  XL > 0 (one wave per row only): x is
+// loaded once per workgroup -- every thread a few 4-element pieces, ahead of
+// its weight loads -- written to LDS already paired, published with one
+// barrier and read back per unit, instead of every wave loading the x of its
+// units.  XL = 1 publishes after the weight loads are issued; XL = 2 before
+// any is issued: a barrier passed with loads in flight waits for them on this
+// part (an 11008 x 4096 launch with the barrier after its loads took 8.4 us,
+// one with it before 6.9 us), so XL = 2 pays only the latency of x first.
+template <int FMT, int RMAX, int UPL, int KS, int WAVES = kWavesH, int XL = 0>
 __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restrict__ blocks,
                                                       const uint16_t* __restrict__ x,
                                                       float* __restrict__ y, int M, int K,
@@ -386,6 +389,30 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restr
       const int pc = min(static_cast<int>(threadIdx.x) + j * WAVES * kWave, 8 * S - 1);
       xp[j] = *reinterpret_cast<const uint2*>(x + 4 * pc);
     }
+  }
+  // XL: pairs of unit lane + 64k, word t, at xs[(4k + t) * 64 + lane]
+  __shared__ uint4 xs[XL ? UPL * 4 * 64 : 1];
+  auto publish_x = [&]() {
+#pragma unroll
+    for (int j = 0; j < kPPT; j++) {
+      const int pc = static_cast<int>(threadIdx.x) + j * WAVES * kWave;
+      uint2 v = xp[j];
+      asm volatile("" : "+v"(v.x), "+v"(v.y)::"memory");  // waits for this piece only
+      if (pc >= 8 * S) v = make_uint2(0u, 0u);  // units past the row's last one
+      if (pc < kPieces) {
+        const int u = pc >> 3, q = pc & 7, t = q & 3, hh = q >> 2;
+        uint32_t* w = reinterpret_cast<uint32_t*>(xs + (4 * (u >> 6) + t) * 64 + (u & 63));
+        w[hh] = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);      // (x0, x2)
+        w[2 + hh] = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);  // (x1, x3)
+      }
+    }
+    // LDS writes done, then the workgroup barrier; the memory clobber keeps
+    // every LDS access on its side
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  if constexpr (XL == 2) {
+    publish_x();
+    if (row0 + slot >= row_end) return;
   }
   auto load_x = [&](int k) {
     const int u = min(part * SP + lane + 64 * k, S - 1);
@@ -446,26 +473,8 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restr
   uint4 X[UPL][4];
   float sx[UPL];
   const half2_t kOne = {1.0f16, 1.0f16};
-  // XL: pairs of unit lane + 64k, word t, at xs[(4k + t) * 64 + lane]
-  __shared__ uint4 xs[XL ? UPL * 4 * 64 : 1];
-  if constexpr (XL) {
-#pragma unroll
-    for (int j = 0; j < kPPT; j++) {
-      const int pc = static_cast<int>(threadIdx.x) + j * WAVES * kWave;
-      uint2 v = xp[j];
-      asm volatile("" : "+v"(v.x), "+v"(v.y)::"memory");  // waits for this piece only
-      if (pc >= 8 * S) v = make_uint2(0u, 0u);  // units past the row's last one
-      if (pc < kPieces) {
-        const int u = pc >> 3, q = pc & 7, t = q & 3, hh = q >> 2;
-        uint32_t* w = reinterpret_cast<uint32_t*>(xs + (4 * (u >> 6) + t) * 64 + (u & 63));
-        w[hh] = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);      // (x0, x2)
-        w[2 + hh] = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);  // (x1, x3)
-      }
-    }
-    // publish: LDS writes done, then the workgroup barrier; the memory clobber
-    // keeps every LDS access on its side (a fence here would also wait for
-    // the weight loads in flight)
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if constexpr (XL == 1) {
+    publish_x();
     if (row0 + slot >= row_end) return;
   }
   auto make_pairs = [&](int k) {
@@ -558,7 +567,7 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restr
         c[2] = __builtin_amdgcn_alignbyte(q[i][k][3], q[i][k][2], a);
         c[3] = __builtin_amdgcn_alignbyte(q[i][k][4], q[i][k][3], a);
       }
-      float lo = 0.0f, hi = 0.0f;
+      float lo, hi;
 #pragma unroll
       for (int t = 0; t < 4; t++) {
         const uint32_t b = c[t] >> 8;
@@ -566,8 +575,13 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restr
         const half2_t v1 = as_h2(and_or(c[t], 0x00F000F0u, kMagic)) + kHi;
         const half2_t v2 = as_h2(and_or(b, 0x000F000Fu, kMagic)) + kLo;
         const half2_t v3 = as_h2(and_or(b, 0x00F000F0u, kMagic)) + kHi;
-        lo = __builtin_amdgcn_fdot2(v0, as_h2(X[k][t].x), lo, false);
-        hi = __builtin_amdgcn_fdot2(v1, as_h2(X[k][t].y), hi, false);
+        if (t == 0) {  // each chain starts from its first product (no zeroed accumulator to move)
+          lo = dot2_first(v0, X[k][t].x);
+          hi = dot2_first(v1, X[k][t].y);
+        } else {
+          lo = __builtin_amdgcn_fdot2(v0, as_h2(X[k][t].x), lo, false);
+          hi = __builtin_amdgcn_fdot2(v1, as_h2(X[k][t].y), hi, false);
+        }
         lo = __builtin_amdgcn_fdot2(v2, as_h2(X[k][t].z), lo, false);
         hi = __builtin_amdgcn_fdot2(v3, as_h2(X[k][t].w), hi, false);
       }
@@ -672,7 +686,7 @@ int cu_count() {
   return n;
 }
 
-template <int FMT, int RMAX, int UPL, int KS, int WAVES, bool XL = false>
+template <int FMT, int RMAX, int UPL, int KS, int WAVES, int XL = 0>
 hipError_t launch_h_t(const void* blocks, int64_t m, int64_t k, const void* x, float* y,
                       int rows_per_wg, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>((m + rows_per_wg - 1) / rows_per_wg);
@@ -692,20 +706,20 @@ inline int rows_per_wg(int64_t m, int slots, int rmax_cap) {
 }
 
 // Row slots per wave: the smallest template count R >= rmax, up to RCAP.
-template <int FMT, int UPL, int KS, int RCAP, int WAVES, int R = 1>
+template <int FMT, int UPL, int KS, int RCAP, int WAVES, int XL, int R = 1>
 hipError_t launch_h_r(int rmax, const void* blocks, int64_t m, int64_t k, const void* x, float* y,
                       int rpw, hipStream_t s) {
   if constexpr (R < RCAP) {
-    if (rmax > R) return launch_h_r<FMT, UPL, KS, RCAP, WAVES, R + 1>(rmax, blocks, m, k, x, y, rpw, s);
+    if (rmax > R) return launch_h_r<FMT, UPL, KS, RCAP, WAVES, XL, R + 1>(rmax, blocks, m, k, x, y, rpw, s);
   }
-  return launch_h_t<FMT, R, UPL, KS, WAVES>(blocks, m, k, x, y, rpw, s);
+  return launch_h_t<FMT, R, UPL, KS, WAVES, XL>(blocks, m, k, x, y, rpw, s);
 }
 
-template <int FMT, int UPL, int KS, int RCAP, int WAVES = kWavesH>
+template <int FMT, int UPL, int KS, int RCAP, int WAVES = kWavesH, int XL = 0>
 hipError_t launch_h_k(const void* blocks, int64_t m, int64_t k, const void* x, float* y, hipStream_t s) {
   constexpr int slots = WAVES / KS;
   const int rpw = rows_per_wg(m, slots, RCAP);
-  return launch_h_r<FMT, UPL, KS, RCAP, WAVES>((rpw + slots - 1) / slots, blocks, m, k, x, y, rpw, s);
+  return launch_h_r<FMT, UPL, KS, RCAP, WAVES, XL>((rpw + slots - 1) / slots, blocks, m, k, x, y, rpw, s);
 }
 
 // fp16 x and at most 384 units (12288 weights) per row: the up-front kernel.
@@ -716,17 +730,22 @@ hipError_t launch_h_k(const void* blocks, int64_t m, int64_t k, const void* x, f
 // waves per row with one unit per lane each, up to 6 rows per wave (at
 // 4096 x 4096: 4.8-4.9 -> 4.3-4.5 us; at 11008 x 4096 Q4_0 8.0 -> 7.7,
 // Type 1 7.6 -> 7.4, Q4_K 7.8 -> 7.5 us) -- except Type 0 and Q4_0 with
-// more than 32 rows per CU: one wave per row, two units per lane, 12-wave
-// workgroups with up to 4 rows per wave (11008 x 4096: Type 0 7.05 us
-// against 7.11 with 16 waves and 7.34 with two waves per row; Q4_0 7.56
-// against 7.64); up to 256 two waves per row with two units per lane; up to
+// more than 32 rows per CU: one wave per row, two units per lane, up to 3
+// rows per wave of 16-wave workgroups, x staged once per workgroup through
+// LDS before any weight load is issued (11008 x 4096 Type 0: 7.03 us with
+// every wave loading its own x in 12-wave workgroups, 6.66 us with x staged,
+// 6.60 us with x staged in 16-wave workgroups; Q4_0 7.42 -> 7.13 us; the
+// affine formats staged so were slower, 7.18 -> 7.20 us and 7.28 -> 7.36
+// us); up to 256 two waves per row with two units per lane; up to
 // 384 three (Type 0 in 12-wave workgroups with up to 3 rows per wave: 4096 x
 // 11008 7.98 against 8.20 us; the other formats gain 1.4% at most, and Q4_K
 // runs out of registers).  With at most 16 rows per CU, x read by every wave
 // outweighs the weights; x through LDS (one wave per row) is taken where it
 // measured faster: Q4_0 up to 128 units (4096 x 4096: 4.44 -> 4.00 us) and
 // Type 1 beyond 256 (4096 x 11008: 8.35 -> 7.68 us); for Type 0 and Q4_K it
-// was not (4096 x 4096 within 2%, 4096 x 11008 Type 0 +9%).
+// was not (4096 x 4096 within 2%, 4096 x 11008 Type 0 +9%).  These two keep
+// the barrier after the weight loads (staging before them: 4.00 -> 4.09 and
+// 7.71 -> 7.99 us).
 template <int FMT>
 bool launch_h(const void* blocks, int64_t m, int64_t k, const void* x, float* y, hipStream_t s,
               hipError_t* err) {
@@ -737,10 +756,10 @@ bool launch_h(const void* blocks, int64_t m, int64_t k, const void* x, float* y,
   const bool few = per_cu <= kWavesH;  // one row per wave at most
   if (S <= 64) *err = launch_h_k<FMT, 1, 1, 3>(blocks, m, k, x, y, s);
   else if (S <= 128 && FMT == QBLK_Q4_0 && few)
-    *err = launch_h_t<FMT, 1, 2, 1, kWavesH, true>(blocks, m, k, x, y, rows_per_wg(m, kWavesH, 1), s);
+    *err = launch_h_t<FMT, 1, 2, 1, kWavesH, 1>(blocks, m, k, x, y, rows_per_wg(m, kWavesH, 1), s);
   else if (S > 256 && FMT == QBLK_SB4_AFFINE && few)
-    *err = launch_h_t<FMT, 1, 6, 1, kWavesH, true>(blocks, m, k, x, y, rows_per_wg(m, kWavesH, 1), s);
-  else if (S <= 128 && kSigned && per_cu > 32) *err = launch_h_k<FMT, 2, 1, 4, 12>(blocks, m, k, x, y, s);
+    *err = launch_h_t<FMT, 1, 6, 1, kWavesH, 1>(blocks, m, k, x, y, rows_per_wg(m, kWavesH, 1), s);
+  else if (S <= 128 && kSigned && per_cu > 32) *err = launch_h_k<FMT, 2, 1, 3, kWavesH, 2>(blocks, m, k, x, y, s);
   else if (S <= 128) *err = launch_h_k<FMT, 1, 2, 6>(blocks, m, k, x, y, s);
   else if (S <= 256) *err = launch_h_k<FMT, 2, 2, 3>(blocks, m, k, x, y, s);
   else if (FMT == QBLK_SB4) *err = launch_h_k<FMT, 3, 2, 3, 12>(blocks, m, k, x, y, s);
