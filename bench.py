@@ -10,8 +10,9 @@ A step is one GEMV launch.  The weights rotate through enough distinct copies
 (> 2x the 256 MB last-level cache) that every step streams them from HBM.  The
 K timed steps are captured in HIP graphs (no host launch gaps) and timed with
 HIP events on the replay stream; the average launch duration is the timed
-region / K.  Beside the nominal 8 TB/s, "hbm_reference" gives what torch's
-plain device copy reaches on the same GPU.
+region / K.  Beside the nominal 8 TB/s, "hbm_reference" gives what a plain
+streaming read of the same bytes (and of 1 GiB) reaches on the same GPU, the
+launch cost of an empty kernel in the same kind of graph, and torch's copy.
 
 Also measured (field "rows"): every other step of the hot path at the shapes
 of the synthetic workloads -- quantization (Q4_0, super-block Type 0 and
@@ -97,17 +98,49 @@ def time_region(torch, fn):
     return a.elapsed_time(b)
 
 
+def _hbmref_lib():
+    """libqblk_hbmref.so: a plain streaming read and an empty kernel, built
+    beside libqblk but not part of it."""
+    import ctypes as C
+    path = os.path.join(ROOT, "bit_block_quant_amd", "libqblk_hbmref.so")
+    L = C.CDLL(path)
+    L.hbmref_read.argtypes, L.hbmref_read.restype = [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p], C.c_int
+    L.hbmref_empty.argtypes, L.hbmref_empty.restype = [C.c_uint, C.c_void_p, C.c_void_p], C.c_int
+    return L
+
+
 def hbm_reference(torch, dev, nbytes, C):
-    """What torch's own copy kernel reaches on this GPU, beside the nominal
-    8 TB/s: over the headline's byte count (C rotating buffers, so reads come
-    from HBM) and over 1 GiB; bytes = read + write."""
+    """What the memory system delivers to kernels that only move bytes, beside
+    the nominal 8 TB/s: a plain 16-byte-per-thread read of the headline's byte
+    count over C rotating buffers (so every launch reads HBM) and of 1 GiB;
+    torch's copy kernel over the same (bytes = read + write); and the launch
+    cost of an empty kernel of 256 workgroups in the same kind of graph."""
+    import ctypes as Cty
     out = {}
+    L = _hbmref_lib()
+    sink = torch.zeros(64, dtype=torch.int32, device=dev)
 
     def rec(name, ms, nb):
-        gbs = nb / (ms * 1e-3) / 1e9
-        out[name] = {"us": round(ms * 1e3, 2), "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
-        log(f"  reference {name}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s")
+        gbs = nb / (ms * 1e-3) / 1e9 if nb else 0.0
+        out[name] = {"us": round(ms * 1e3, 3), "GBps": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        log(f"  reference {name}: {ms * 1e3:.2f} us" + (f", {gbs:.0f} GB/s" if nb else ""))
 
+    def stream_ptr():
+        return Cty.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    for name, nb, n in (("read_24MB_rotating", nbytes, C), ("read_1GiB", 1 << 30, 2)):
+        nb16 = nb // 16 * 16
+        bufs = [torch.ones(nb16 // 4, dtype=torch.float32, device=dev) for _ in range(n)]
+
+        def launch(i, bufs=bufs, nb16=nb16):
+            rc = L.hbmref_read(Cty.c_void_p(bufs[i % len(bufs)].data_ptr()), nb16,
+                               Cty.c_void_p(sink.data_ptr()), stream_ptr())
+            assert rc == 0, rc
+        t = Timer(torch, launch, n, max(1, 480 // n) if nb16 < (1 << 28) else 4)
+        rec(name, t.run(2), nb16)
+        del bufs
+    t = Timer(torch, lambda i: L.hbmref_empty(256, Cty.c_void_p(sink.data_ptr()), stream_ptr()), 480)
+    rec("empty_kernel_256wg", t.run(2), 0)
     for name, nb, n in (("copy_24MB_rotating", nbytes, C), ("copy_1GiB", 1 << 30, 1)):
         n_el = nb // 4
         src = [torch.empty(n_el, dtype=torch.float32, device=dev) for _ in range(n)]
@@ -185,8 +218,11 @@ def main():
     full, rem = divmod(args.steps, G)
     g_full = Timer(torch, launch, C, G // C)
     g_rem = Timer(torch, launch, rem) if rem else None
-    for i in range(args.warmup):  # untimed warmup launches
-        launch(i)
+    # untimed warmup launches on the copies the timed region reads last (or
+    # not at all), so none of the first timed launches finds its weights
+    # still in the 256 MB last-level cache
+    for i in range(args.warmup):
+        launch((C - args.warmup % C + i) % C)
 
     def region():
         for _ in range(full):
@@ -374,12 +410,22 @@ def measure_rows(torch, q, WL, np, dev):
             outs.append(torch.empty(q.packed_bytes(q.SB4_AFFINE, r, k), dtype=torch.uint8, device=dev))
             xs.append(randn((k,), 1.0, sx, torch.float16))
     n = len(mats)
+    # the stack is drawn on the device with torch's generator (the numpy recipe
+    # would take minutes on the host for 6.5e9 weights); its fingerprint: the
+    # SHA-256 over the first 65536 values of every matrix and every x, in order
+    fp = hashlib.sha256()
+    for mt, xx in zip(mats, xs):
+        fp.update(mt.reshape(-1)[:65536].cpu().numpy().tobytes())
+        fp.update(xx.reshape(-1)[:65536].cpu().numpy().tobytes())
+    stack_inputs = {"generator": f"torch {torch.__version__} default CUDA generator, manual_seed per matrix",
+                    "sha256_first64k_each": fp.hexdigest()}
     t = Timer(torch, lambda i: q.quantize(mats[i], q.SB4_AFFINE, out=outs[i]), n)
     ms = t.run(2) * n
     src = sum(m.numel() * 2 for m in mats)
     dst = sum(o.numel() for o in outs)
     hbm_row("quantize_sb4a_stack_32x7_f16", ms, src + dst,
-            weights=sum(m.numel() for m in mats), weights_per_s=round(sum(m.numel() for m in mats) / (ms * 1e-3), 1))
+            weights=sum(m.numel() for m in mats), weights_per_s=round(sum(m.numel() for m in mats) / (ms * 1e-3), 1),
+            inputs=stack_inputs)
     del mats
     ys = [torch.empty(WL.STACK_PROJ[i % 7][1], dtype=torch.float32, device=dev) for i in range(n)]
 
@@ -390,13 +436,15 @@ def measure_rows(torch, q, WL, np, dev):
     t = Timer(torch, stack_gemv, n)
     ms = t.run(3) * n
     nb = dst + sum(xx.numel() * 2 for xx in xs) + sum(yy.numel() * 4 for yy in ys)
-    hbm_row("gemv_sb4a_stack_32x7_f16", ms, nb, tokens_per_s_equivalent=round(1.0 / (ms * 1e-3), 1))
+    hbm_row("gemv_sb4a_stack_32x7_f16", ms, nb, tokens_per_s_equivalent=round(1.0 / (ms * 1e-3), 1),
+            inputs=stack_inputs)
     del outs, xs, ys
 
     # prefill GEMM
     for shape in ("up", "down"):
         w, _ = WL.sb4_prefill(shape, 16)
         m, k = w.shape
+        w_sha = WL.sha256(w)
         b0 = q.quantize(torch.from_numpy(w).to(dev), q.SB4)
         C = n_copies(b0.numel())
         cps = [b0] + [b0.clone() for _ in range(C - 1)]
@@ -413,7 +461,8 @@ def measure_rows(torch, q, WL, np, dev):
             name = f"gemm_sb4_{m}x{k}_n{n_tok}_bf16"
             rows[name] = dict(us=round(ms * 1e3, 3), bytes=nb, GBps=round(gbs, 1),
                               frac_hbm=round(gbs / HBM_PEAK_GBS, 4), TFLOPs=round(tf, 2),
-                              frac_mfma_bf16=round(tf / BF16_PEAK_TFLOPS, 4))
+                              frac_mfma_bf16=round(tf / BF16_PEAK_TFLOPS, 4),
+                              inputs={"w_f32_sha256": w_sha, "x_bf16_sha256": WL.sha256(X)})
             log(f"  {name}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s, {tf:.1f} TFLOP/s")
         del cps
     # the same product for the other formats (14336x4096)
@@ -507,19 +556,33 @@ def w4a8_rows(torch, q, WL, np, dev):
 
 
 # --------------------------------------------------------------- CPU oracle
+def cpu_threads():
+    """Threads for the all-cores legs: the CPUs this process may run on, but no
+    more than the box's share per GPU, which it states in OMP_NUM_THREADS (16
+    for one GPU on the GPU machines); more workers than that share would oversubscribe it."""
+    n = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS")
+    if share and share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return max(1, n)
+
+
 def cpu_baseline(np, WL, w, x, algo_bytes, budget_s):
-    """The oracle GEMV on the host: first on one thread, then on every host
-    core (row chunks on a thread pool; the C oracle runs with the GIL
-    released).  `value` is the all-cores rate; each leg gets half the budget."""
+    """The oracle (plain C: per-row fp32 dequant, fp64 sums; scalar
+    quantizers) on this host, on the same workloads: the headline GEMV (the
+    `value`), and the Type 0 / Type 1 quantizers of the same 11008 x 4096
+    matrix and the 16-token prefill GEMM at 14336 x 4096 ("legs").  Each leg is
+    timed on one thread and on every allowed core (row chunks on a thread
+    pool; the C oracle runs with the GIL released)."""
     import oracle as O
     from concurrent.futures import ThreadPoolExecutor
 
-    m, k = w.shape
-    blocks = O.quantize_sb4(w)  # the oracle quantizes its own input (untimed)
-    xd = x.astype(np.float64)
-    threads = max(1, min(len(os.sched_getaffinity(0)), 16))
-    chunks = [np.arange(r0, min(m, r0 + (m + threads - 1) // threads), dtype=np.int64)
-              for r0 in range(0, m, (m + threads - 1) // threads)]
+    threads = cpu_threads()
+    pool = ThreadPoolExecutor(threads)
+
+    def chunks(m):
+        step = (m + threads - 1) // threads
+        return [np.arange(r0, min(m, r0 + step), dtype=np.int64) for r0 in range(0, m, step)]
 
     def timed(fn, budget):
         reps, t0 = 0, time.perf_counter()
@@ -528,14 +591,43 @@ def cpu_baseline(np, WL, w, x, algo_bytes, budget_s):
             reps += 1
             el = time.perf_counter() - t0
             if el >= budget or reps >= 1000:
-                return reps, el
+                return el / reps, reps
 
-    r1, e1 = timed(lambda: O.gemv(O.SB4, blocks, m, k, xd), budget_s / 2)
-    with ThreadPoolExecutor(threads) as pool:
-        def all_cores():
-            list(pool.map(lambda rows: O.gemv(O.SB4, blocks, m, k, xd, rows=rows), chunks))
-        rt, et = timed(all_cores, budget_s / 2)
-    per1, pert = e1 / r1, et / rt
+    leg_budget = budget_s / 8
+    m, k = w.shape
+    # headline GEMV (the oracle quantizes its own input, untimed)
+    blocks = O.quantize_sb4(w)
+    xd = x.astype(np.float64)
+    ck = chunks(m)
+    g1, r1 = timed(lambda: O.gemv(O.SB4, blocks, m, k, xd), 2 * leg_budget)
+    gt, rt = timed(lambda: list(pool.map(lambda rows: O.gemv(O.SB4, blocks, m, k, xd, rows=rows), ck)), 2 * leg_budget)
+    legs = {}
+
+    # quantizers of the same matrix (f32 in): one thread on a 1024-row slice, all cores on the whole matrix
+    for name, affine in (("quantize_sb4_11008x4096_f32", False), ("quantize_sb4a_11008x4096_f32", True)):
+        fmt = O.SB4_AFFINE if affine else O.SB4
+        nb_out = O.packed_bytes(fmt, m, k)
+        s1, _ = timed(lambda: O.quantize_sb4(w[:1024], affine=affine), leg_budget)
+        s1 *= m / 1024
+        sl = [w[r[0]:r[-1] + 1] for r in ck]
+        st, _ = timed(lambda: list(pool.map(lambda a: O.quantize_sb4(a, affine=affine), sl)), leg_budget)
+        nb = w.nbytes + nb_out
+        legs[name] = {"GBps": round(nb / st / 1e9, 3), "weights_per_s": round(m * k / st, 1),
+                      "single_thread_GBps": round(nb / s1 / 1e9, 3), "ms": round(st * 1e3, 2)}
+    # 16-token prefill product
+    wp, X = WL.sb4_prefill("up", 16)
+    mp, kp = wp.shape
+    bp = O.quantize_sb4(wp)
+    Xv = WL.bf16_values(X).astype(np.float64)
+    ckp = chunks(mp)
+    p1, _ = timed(lambda: O.gemm(O.SB4, bp, mp, kp, Xv, rows=np.arange(512, dtype=np.int64)), leg_budget)
+    p1 *= mp / 512
+    pt, _ = timed(lambda: list(pool.map(lambda rows: O.gemm(O.SB4, bp, mp, kp, Xv, rows=rows), ckp)), leg_budget)
+    nbp = bp.nbytes + X.size * 2 + 16 * mp * 4
+    legs[f"gemm_sb4_{mp}x{kp}_n16"] = {"GBps": round(nbp / pt / 1e9, 3),
+                                      "GFLOPs": round(2.0 * mp * kp * 16 / pt / 1e9, 2),
+                                      "single_thread_GBps": round(nbp / p1 / 1e9, 3), "ms": round(pt * 1e3, 2)}
+    pool.shutdown()
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as fh:
@@ -543,15 +635,18 @@ def cpu_baseline(np, WL, w, x, algo_bytes, budget_s):
     except OSError:
         pass
     return {
-        "value": round(algo_bytes / pert / 1e9, 3),
+        "value": round(algo_bytes / gt / 1e9, 3),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
         "sample": f"full {m}x{k} super-block GEMVs (C oracle: per-row fp32 dequant, fp64 sums); "
-                  f"{rt} on {threads} threads in {et:.1f} s ({pert * 1e3:.1f} ms each), "
-                  f"{r1} on 1 thread in {e1:.1f} s ({per1 * 1e3:.1f} ms each)",
-        "single_thread": {"value": round(algo_bytes / per1 / 1e9, 3), "unit": "GB/s", "cores": 1},
+                  f"{rt} on {threads} threads ({gt * 1e3:.1f} ms each), "
+                  f"{r1} on 1 thread ({g1 * 1e3:.1f} ms each); legs: the quantizers of the same matrix "
+                  f"(one thread on 1024 rows, scaled) and the 16-token GEMM at {mp}x{kp} (one thread on 512 rows)",
+        "single_thread": {"value": round(algo_bytes / g1 / 1e9, 3), "unit": "GB/s", "cores": 1},
+        "legs": legs,
         "host_cpu": cpu,
+        "threads_rule": "allowed CPUs, at most OMP_NUM_THREADS (the host's CPU share per GPU)",
     }
 
 

@@ -1,7 +1,10 @@
 """Python binding of libqblk (the gfx950 C-ABI library), via ctypes.
 
 Argument marshalling only: every step runs in the library's HIP kernels.
-PyTorch supplies device memory and the stream; tensors must live on a GPU.
+PyTorch supplies device memory and the stream; tensors must live on the
+current GPU and be contiguous, and every buffer must be large enough for the
+call -- the C ABI cannot see extents, so these are checked here and a bad
+argument raises ValueError/TypeError before anything is launched.
 If the library is not built this module raises on import -- there is no CPU
 fallback.  Build with ``python bit_block_quant_amd/build.py`` (or ``__graft_entry__.build()``).
 
@@ -100,6 +103,58 @@ def _ptr(t):
     return C.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else C.c_void_p(0)
 
 
+# ---------------------------------------------------------------- checks
+# The C ABI sees raw pointers only, so the extents of every buffer are checked
+# here, before any call: a short or strided tensor would make a kernel read or
+# write past its allocation.  Each check raises ValueError (or TypeError for
+# an element type) and nothing is launched.
+_FLOAT_IN = (torch.float32, torch.float16, torch.bfloat16)
+
+
+def _need(t, name, dtypes=None, min_numel=None, numel=None, ndim=None, dim1=None, device=None):
+    """Validate one tensor argument; returns its device.  `device`: the device
+    every other argument of the call lives on (None for the first one)."""
+    if not isinstance(t, torch.Tensor) and not hasattr(t, "is_cuda"):
+        raise TypeError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor (got device {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, the other arguments on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous (the kernels index it as a dense row-major array)")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name}: element type {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dimensions, got shape {tuple(t.shape)}")
+    if dim1 is not None and t.shape[1] != dim1:
+        raise ValueError(f"{name}: expected {dim1} columns, got shape {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name}: holds {t.numel()} elements, the call needs {min_numel}")
+    return t.device
+
+
+def _need_current(dev):
+    """Kernels launch on the current device: the tensors must live there."""
+    cur = torch.cuda.current_device()
+    if dev.index is not None and dev.index != cur:
+        raise ValueError(f"tensors on {dev}, but the current device is cuda:{cur}")
+
+
+def _need_dims(**dims):
+    for name, v in dims.items():
+        if int(v) != v or v < 0:
+            raise ValueError(f"{name} must be a non-negative integer, got {v!r}")
+
+
+def _packed(fmt, rows, k):
+    """Bytes of a packed rows x k matrix; 0 for a shape the format cannot
+    hold (the library itself rejects those with QBLK_ERR_SHAPE/FORMAT before
+    touching memory)."""
+    return packed_bytes(fmt, rows, k)
+
+
 def _stream(stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
     return C.c_void_p(s.cuda_stream)
@@ -121,10 +176,13 @@ def quantize(w, fmt, out=None, stream=None, ref=False):
     """Quantize a (rows, k) device tensor into a uint8 tensor of packed blocks.
 
     ref=True (Q4_0 only) uses the Q4_0 chapter's signed max/-8 quantizer."""
+    dev = _need(w, "w", _FLOAT_IN, ndim=2)
     rows, k = w.shape
-    nbytes = packed_bytes(fmt, rows, k)
+    nbytes = _packed(fmt, rows, k)
     if out is None:
         out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=w.device)
+    _need(out, "out", (torch.uint8,), min_numel=nbytes, device=dev)
+    _need_current(dev)
     if fmt == Q4_0:
         f = _lib.qblk_quantize_q4_0_ref if ref else _lib.qblk_quantize_q4_0
         _check(f(_ptr(w), _dtype(w), rows, k, _ptr(out), _stream(stream)), "qblk_quantize_q4_0")
@@ -141,25 +199,39 @@ def quantize(w, fmt, out=None, stream=None, ref=False):
 
 
 def dequant(blocks, fmt, rows, k, dtype=torch.float32, out=None, stream=None):
+    _need_dims(rows=rows, k=k)
+    dev = _need(blocks, "blocks", (torch.uint8,), min_numel=_packed(fmt, rows, k))
     if out is None:
         out = torch.empty((rows, k), dtype=dtype, device=blocks.device)
+    _need(out, "out", _FLOAT_IN, min_numel=rows * k, device=dev)
+    _need_current(dev)
     _check(_lib.qblk_dequant(fmt, _ptr(blocks), rows, k, _ptr(out), _dtype(out), _stream(stream)),
            "qblk_dequant")
     return out
 
 
 def gemv(blocks, fmt, m, k, x, out=None, stream=None):
+    _need_dims(m=m, k=k)
+    dev = _need(x, "x", _FLOAT_IN, numel=k)
+    _need(blocks, "blocks", (torch.uint8,), min_numel=_packed(fmt, m, k), device=dev)
     if out is None:
         out = torch.empty(m, dtype=torch.float32, device=x.device)
+    _need(out, "out", (torch.float32,), min_numel=m, device=dev)
+    _need_current(dev)
     _check(_lib.qblk_gemv(fmt, _ptr(blocks), m, k, _ptr(x), _dtype(x), _ptr(out), _stream(stream)),
            "qblk_gemv")
     return out
 
 
 def gemm(blocks, fmt, m, k, X, out=None, stream=None):
+    _need_dims(m=m, k=k)
+    dev = _need(X, "X", _FLOAT_IN, ndim=2, dim1=k)
     n = X.shape[0]
+    _need(blocks, "blocks", (torch.uint8,), min_numel=_packed(fmt, m, k), device=dev)
     if out is None:
         out = torch.empty((n, m), dtype=torch.float32, device=X.device)
+    _need(out, "out", (torch.float32,), min_numel=n * m, device=dev)
+    _need_current(dev)
     _check(_lib.qblk_gemm(fmt, _ptr(blocks), m, k, _ptr(X), _dtype(X), n, _ptr(out),
                           _stream(stream)), "qblk_gemm")
     return out
@@ -167,11 +239,15 @@ def gemm(blocks, fmt, m, k, X, out=None, stream=None):
 
 def quantize_act_i8(x, out=None, scale=None, stream=None):
     """8-bit activations: (n, k) f32/f16/bf16 -> (int8 codes (n, k), fp32 scales (n,))."""
+    dev = _need(x, "x", _FLOAT_IN, ndim=2)
     n, k = x.shape
     if out is None:
         out = torch.empty((n, k), dtype=torch.int8, device=x.device)
     if scale is None:
         scale = torch.empty(n, dtype=torch.float32, device=x.device)
+    _need(out, "out", (torch.int8,), min_numel=n * k, device=dev)
+    _need(scale, "scale", (torch.float32,), min_numel=n, device=dev)
+    _need_current(dev)
     _check(_lib.qblk_quantize_act_i8(_ptr(x), _dtype(x), n, k, _ptr(out), _ptr(scale), _stream(stream)),
            "qblk_quantize_act_i8")
     return out, scale
@@ -179,9 +255,15 @@ def quantize_act_i8(x, out=None, scale=None, stream=None):
 
 def gemm_w4a8(blocks, m, k, xq, scale, out=None, stream=None):
     """Y (n, m) fp32 = the W4A8 product of QBLK_W4G128 blocks and int8 activations."""
+    _need_dims(m=m, k=k)
+    dev = _need(xq, "xq", (torch.int8,), ndim=2, dim1=k)
     n = xq.shape[0]
+    _need(scale, "scale", (torch.float32,), min_numel=n, device=dev)
+    _need(blocks, "blocks", (torch.uint8,), min_numel=_packed(W4G128, m, k), device=dev)
     if out is None:
         out = torch.empty((n, m), dtype=torch.float32, device=xq.device)
+    _need(out, "out", (torch.float32,), min_numel=n * m, device=dev)
+    _need_current(dev)
     _check(_lib.qblk_gemm_w4a8(_ptr(blocks), m, k, _ptr(xq), _ptr(scale), n, _ptr(out), _stream(stream)),
            "qblk_gemm_w4a8")
     return out
