@@ -90,6 +90,33 @@ def near_ties(rows, k, seed):
     return w * np.float32(2.0 ** -8)
 
 
+def affine_near_ties(rows, k, seed, dtype=np.float32):
+    """Type 1 sub-blocks whose code quotients (w - a) / s sit on, or one ulp of
+    the input type either side of, a half-integer: each 32-weight sub-block
+    holds its min a and its max a + 15 s (s and a exact in fp16, so the stored
+    offset and scale are a and s), and the other weights a + (c + 1/2) s,
+    c = 0..14, each left alone or moved one ulp up or down."""
+    rng = np.random.default_rng(seed)
+    choices = [(-1.0, 0.125), (-0.25, 0.1875), (0.5, 3.0 / 256), (-3.0, 0.375), (-0.0625, 1.0 / 64)]
+    w = np.empty((rows, k), dtype=np.float64)
+    for r in range(rows):
+        for j in range(k // 32):
+            a, sc = choices[rng.integers(len(choices))]
+            blk = a + (rng.integers(0, 15, 32) + 0.5) * sc
+            blk[rng.integers(32)] = a
+            blk[rng.integers(32)] = a + 15 * sc
+            w[r, 32 * j:32 * j + 32] = blk
+    w = w.astype(dtype)
+    up, down = np.nextafter(w, dtype(np.inf)), np.nextafter(w, dtype(-np.inf))
+    flip = rng.integers(-1, 2, w.shape)
+    # keep each sub-block's extremes: only interior values move
+    lo = w.reshape(rows, -1, 32).min(axis=2, keepdims=True)
+    hi = w.reshape(rows, -1, 32).max(axis=2, keepdims=True)
+    inner = ((w.reshape(rows, -1, 32) > lo) & (w.reshape(rows, -1, 32) < hi)).reshape(rows, k)
+    w = np.where(inner & (flip > 0), up, np.where(inner & (flip < 0), down, w))
+    return w.astype(dtype)
+
+
 # ----------------------------------------------------------------- quantize
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: NAMES[f])
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
@@ -102,6 +129,35 @@ def test_quantize_bit_exact(q, fmt, dtype):
         ref = O.quantize(fmt, h)
         assert got.shape == ref.shape
         assert np.array_equal(got, ref), f"first mismatch at byte {np.argmax(got != ref)}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_quantize_affine_near_ties(q, dtype):
+    # quotients (w - a) / s on and one ulp around every half-integer code boundary
+    w = affine_near_ties(9, 2304, 41, np.float32 if dtype == "f32" else np.float16)
+    d = dev(w)
+    got = host(q.quantize(d, q.SB4_AFFINE))
+    ref = O.quantize(O.SB4_AFFINE, w)
+    assert np.array_equal(got, ref), f"first mismatch at byte {np.argmax(got != ref)}"
+
+
+def test_quantize_q4_0_listing_fixture_blocks(q):
+    # the hand-derived blocks of the Q4_0 chapter's 4.4 quantizer (cap at 15,
+    # the first extreme fixing the sign of d, codes from the fp32 reciprocal)
+    import ast
+    from test_oracle_pins import read_golden_raw
+    g = read_golden_raw("q4_0_listing_cap_and_ties.txt")
+    w = np.zeros((3, 32), dtype=np.float32)
+    for r, name in enumerate(("cap", "first")):
+        for i, v in ast.literal_eval(g[f"{name}_values"]).items():
+            w[r, i] = v
+    w[2, 0] = np.array([int(g["recip_e_bits"], 16)], np.uint32).view(np.float32)[0]
+    w[2, 7] = np.array([int(g["recip_x_bits"], 16)], np.uint32).view(np.float32)[0]
+    got = host(q.quantize(dev(w), q.Q4_0, ref=True))
+    for r, name in enumerate(("cap", "first")):
+        assert got[18 * r:18 * r + 18].tobytes() == bytes.fromhex(g[f"{name}_bytes"].replace(" ", ""))
+    assert got[36 + 2 + 7] & 0x0F == int(g["recip_code_x"])
+    assert np.array_equal(got, O.quantize_q4_0_ref(w))
 
 
 def test_quantize_extreme_f16_inputs(q):
@@ -385,6 +441,25 @@ def test_gemm_single_super_block(q, fmt, n):
     check_products(Y, Y_ref, B, f"gemm {NAMES[fmt]} k=256 n={n}")
 
 
+_DEQ = {}
+
+
+def dequant_f64(fmt, blocks, m, k, key):
+    """The oracle's rebuilt weights as float64 (cached per workload: the
+    full-size prefill matrices are rebuilt once per format and shape)."""
+    if key not in _DEQ:
+        _DEQ.clear()
+        _DEQ[key] = O.dequant(fmt, blocks, m, k).astype(np.float64)
+    return _DEQ[key]
+
+
+def check_all_rows(Y, Xv, Wd, what):
+    """Every output of a product against numpy's float64 matmul of the
+    rebuilt weights (a textbook routine on the oracle's dequantized values)
+    and the bound sum |x| |w| of the same shape."""
+    check_products(Y, Xv @ Wd.T, np.abs(Xv) @ np.abs(Wd).T, what + " (all rows)")
+
+
 @pytest.mark.parametrize("shape", ["up", "down"])
 @pytest.mark.parametrize("n", [16, 64, 512])
 def test_gemm_prefill_config(q, shape, n):
@@ -396,8 +471,10 @@ def test_gemm_prefill_config(q, shape, n):
     Y = host(q.gemm(bd, q.SB4, m, k, dev_bf16(X)))
     rows = np.random.default_rng(n).choice(m, size=64 if n == 512 else 256, replace=False)
     rows = np.concatenate([rows, [0, m - 1]])
-    Y_ref, B = O.gemm(O.SB4, blocks, m, k, WL.bf16_values(X).astype(np.float64), rows=rows)
+    Xv = WL.bf16_values(X).astype(np.float64)
+    Y_ref, B = O.gemm(O.SB4, blocks, m, k, Xv, rows=rows)
     check_products(Y[:, rows], Y_ref, B, f"gemm {shape} n={n}")
+    check_all_rows(Y, Xv, dequant_f64(O.SB4, blocks, m, k, ("sb4", shape)), f"gemm {shape} n={n}")
 
 
 @pytest.mark.parametrize("n", [16, 64, 512])
@@ -410,8 +487,10 @@ def test_gemm_q4_k_prefill_shape(q, n):
     Y = host(q.gemm(bd, q.Q4_K, m, k, dev_bf16(X)))
     rows = np.random.default_rng(n + 1).choice(m, size=64 if n == 512 else 256, replace=False)
     rows = np.concatenate([rows, [0, m - 1]])
-    Y_ref, B = O.gemm(O.Q4_K, blocks, m, k, WL.bf16_values(X).astype(np.float64), rows=rows)
+    Xv = WL.bf16_values(X).astype(np.float64)
+    Y_ref, B = O.gemm(O.Q4_K, blocks, m, k, Xv, rows=rows)
     check_products(Y[:, rows], Y_ref, B, f"gemm q4k n={n}")
+    check_all_rows(Y, Xv, dequant_f64(O.Q4_K, blocks, m, k, ("q4k", "up")), f"gemm q4k n={n}")
 
 
 # ------------------------------------------- group-128 W4 weights, int8 activations
@@ -529,6 +608,9 @@ def test_gemm_w4a8_prefill_shape(q, n):
     rows = np.concatenate([rows, [0, m - 1]])
     Y_ref, B = O.gemm_w4a8(blocks, m, k, xq_ref, s_ref, rows=rows)
     check_products(Y[:, rows], Y_ref, B, f"w4a8 prefill n={n}")
+    # every row: the rebuilt int8 activations (code times the token's scale, R31)
+    Xv = xq_ref.astype(np.float64) * s_ref.astype(np.float64)[:, None]
+    check_all_rows(Y, Xv, dequant_f64(O.W4G128, blocks, m, k, ("w4g128", "up")), f"w4a8 prefill n={n}")
 
 
 def test_w4a8_token_slices(q):

@@ -277,6 +277,42 @@ def test_q4_0_outlier_example():
     assert np.all(y[:31] == 0) and abs(y[31] - 10.0) < 10.0 / 7 / 2
 
 
+def read_golden_raw(name):
+    """key = value lines as strings (for fixtures holding dicts and hex bytes)."""
+    vals = {}
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                key, _, rest = line.partition("=")
+                vals[key.strip()] = rest.strip()
+    return vals
+
+
+def _listing_block(values):
+    w = np.zeros((1, 32), dtype=np.float32)
+    for i, v in values.items():
+        w[0, int(i)] = v
+    return w
+
+
+def test_q4_0_listing_cap_first_extreme_and_reciprocal():
+    # "GGUF 量化内幕 第4章 Q4_0" 4.4: hand-derived bytes for the parts of the
+    # listing no printed example reaches (tests/golden/q4_0_listing_cap_and_ties.txt)
+    import ast
+    g = read_golden_raw("q4_0_listing_cap_and_ties.txt")
+    for name in ("cap", "first"):
+        got = O.quantize_q4_0_ref(_listing_block(ast.literal_eval(g[f"{name}_values"])))
+        want = bytes.fromhex(g[f"{name}_bytes"].replace(" ", ""))
+        assert got.tobytes() == want, f"block {name}: {got.tobytes().hex()} != {want.hex()}"
+    E = np.array([int(g["recip_e_bits"], 16)], np.uint32).view(np.float32)[0]
+    X = np.array([int(g["recip_x_bits"], 16)], np.uint32).view(np.float32)[0]
+    got = O.quantize_q4_0_ref(_listing_block({0: E, 7: X}))
+    codes = nibbles(got[2:18])
+    assert codes[0] == 0 and codes[7] == int(g["recip_code_x"])
+    assert codes[7] != int(g["recip_code_if_divided"])
+
+
 # --------------------------------------------------------------------------
 # brute force: every stored code is the best admissible one
 # --------------------------------------------------------------------------
