@@ -1,9 +1,56 @@
 // qblk_abi.hip -- the C ABI of libqblk (declared in include/qblk.h): argument
 // checks on the host, then one kernel launch on the caller's stream.
+#include <stdarg.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <atomic>
 
 #include "../../include/qblk.h"
 #include "qblk_launch.h"
+
+namespace qblk {
+
+// per device ordinal; 0 = not queried yet.  Concurrent first calls may both
+// query and store the same value.
+static std::atomic<int> g_cus[64];
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  std::atomic<int>& slot = g_cus[dev < 64 ? dev : 63];
+  int n = slot.load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) slot.store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// -1 unknown, 0 off, 1 on
+static std::atomic<int> g_log{-1};
+
+bool log_enabled() {
+  int v = g_log.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char* e = getenv("QBLK_LOG");
+    v = (e && e[0] == '1') ? 1 : 0;
+    g_log.store(v, std::memory_order_relaxed);
+  }
+  return v == 1;
+}
+
+void log_launch(const char* fmt, ...) {
+  if (!log_enabled()) return;
+  char line[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(line, sizeof line, fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "qblk: %s\n", line);
+}
+
+}  // namespace qblk
 
 namespace {
 

@@ -438,16 +438,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_w(const uint8_t* __restric
   }
 }
 
-int cu_count_gemm() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-  }
-  return n;
-}
 
 template <int FMT, int T32>
 hipError_t launch_w(const void* blocks, int64_t m, int64_t k, const void* x, int64_t n, float* y,
@@ -457,7 +447,7 @@ hipError_t launch_w(const void* blocks, int64_t m, int64_t k, const void* x, int
   const int nsb = static_cast<int>(k / 256);
   // split K when the tiles alone leave CUs idle (two workgroups fit per CU)
   const int64_t tiles = static_cast<int64_t>(gx) * gy;
-  const int cus = cu_count_gemm();
+  const int cus = cu_count();
   int split = 1;
   if (tiles < cus) {
     split = static_cast<int>((2 * cus + tiles - 1) / tiles);
@@ -466,6 +456,9 @@ hipError_t launch_w(const void* blocks, int64_t m, int64_t k, const void* x, int
   }
   const int per = (nsb + split - 1) / split;
   split = (nsb + per - 1) / per;
+  if (log_enabled())
+    log_launch("gemm k_gemm_w fmt=%d tile=128x%d m=%lld k=%lld n=%lld grid=%ux%ux%d super-blocks/piece=%d", FMT,
+               32 * T32, (long long)m, (long long)k, (long long)n, gx, gy, split, split > 1 ? per : nsb);
   if (split > 1) {
     const hipError_t e = launch_fill_zero(y, m * n, s);
     if (e != hipSuccess) return e;
@@ -900,6 +893,9 @@ hipError_t launch_u(const void* blocks, int64_t m, int64_t k, const void* x, int
   const unsigned gy = static_cast<unsigned>((n + 16 * T16 - 1) / (16 * T16));
   const int nsb = static_cast<int>(k / 256);
   const unsigned gz = static_cast<unsigned>((nsb + NSB - 1) / NSB);
+  if (log_enabled())
+    log_launch("gemm k_gemm_u fmt=%d tile=%dx%d waves/tile=%d m=%lld k=%lld n=%lld grid=%ux%ux%u super-blocks/piece=%d",
+               FMT, 64 * R16, 16 * T16, KW, (long long)m, (long long)k, (long long)n, gx, gy, gz, NSB);
   if (gz > 1) {
     const hipError_t e = launch_fill_zero(y, m * n, s);
     if (e != hipSuccess) return e;
@@ -925,13 +921,17 @@ hipError_t launch_st(const void* blocks, int64_t m, int64_t k, const void* x, in
   const int nsb = static_cast<int>(k / 256);
   const int64_t tiles = static_cast<int64_t>(gx) * gy;
   int split = 1;
-  if (tiles < cu_count_gemm()) {
-    split = static_cast<int>((2 * cu_count_gemm() + tiles - 1) / tiles);
+  if (tiles < cu_count()) {
+    split = static_cast<int>((2 * cu_count() + tiles - 1) / tiles);
     const int max_split = nsb / (2 * NSB) > 1 ? nsb / (2 * NSB) : 1;  // >= 2 stages per piece
     split = split > max_split ? max_split : split;
   }
   const int per = (nsb + split - 1) / split;
   split = (nsb + per - 1) / per;
+  if (log_enabled())
+    log_launch("gemm k_gemm_s fmt=%d tile=%dx%d waves/tile=%d stage=%d m=%lld k=%lld n=%lld grid=%ux%ux%d "
+               "super-blocks/piece=%d", FMT, 64 * R16, 16 * T16, KW, NSB, (long long)m, (long long)k, (long long)n,
+               gx, gy, split, split > 1 ? per : nsb);
   if (split > 1) {
     const hipError_t e = launch_fill_zero(y, m * n, s);
     if (e != hipSuccess) return e;

@@ -662,6 +662,9 @@ hipError_t launch_tr(const void* blocks, int64_t m, int64_t k, const void* x, fl
   const size_t lds = (XH ? kc * 2 : kc * 4) + (kc / 32) * 4;
   const int64_t groups = (m + R - 1) / R;
   const unsigned grid = static_cast<unsigned>((groups + kWaves - 1) / kWaves);
+  if (log_enabled())
+    log_launch("gemv k_gemv fmt=%d x=%d rows/wave=%d m=%lld k=%lld grid=%u block=%d lds=%zu", FMT, XT, R,
+               (long long)m, (long long)k, grid, kThreads, lds);
   hipLaunchKernelGGL((k_gemv<FMT, XT, R>), dim3(grid), dim3(kThreads), lds, s,
                      static_cast<const uint8_t*>(blocks), x, y, static_cast<int>(m),
                      static_cast<int>(k));
@@ -675,21 +678,13 @@ hipError_t launch_t(const void* blocks, int64_t m, int64_t k, const void* x, flo
   return launch_tr<FMT, XT, kRows>(blocks, m, k, x, y, s);
 }
 
-int cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-  }
-  return n;
-}
-
 template <int FMT, int RMAX, int UPL, int KS, int WAVES, int XL = 0>
 hipError_t launch_h_t(const void* blocks, int64_t m, int64_t k, const void* x, float* y,
                       int rows_per_wg, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>((m + rows_per_wg - 1) / rows_per_wg);
+  if (log_enabled())
+    log_launch("gemv k_gemv_h fmt=%d row-slots/wave=%d units/lane=%d waves/row=%d waves=%d x-lds=%d m=%lld k=%lld "
+               "rows/wg=%d grid=%u", FMT, RMAX, UPL, KS, WAVES, XL, (long long)m, (long long)k, rows_per_wg, grid);
   hipLaunchKernelGGL((k_gemv_h<FMT, RMAX, UPL, KS, WAVES, XL>), dim3(grid), dim3(WAVES * kWave), 0, s,
                      static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
                      static_cast<int>(m), static_cast<int>(k), rows_per_wg);

@@ -32,4 +32,13 @@ hipError_t launch_gemm(int fmt, const void* blocks, int64_t m, int64_t k, const 
                        int64_t n, float* y, hipStream_t s);
 hipError_t launch_fill_zero(float* y, int64_t n, hipStream_t s);
 
+// Compute units of the current device (queried once per device, then cached;
+// 256 if the query fails).  Every launcher sizes its grid from this.
+int cu_count();
+
+// QBLK_LOG=1 in the environment: every launch writes one line to stderr
+// naming the kernel and the tiling it picked (read once per process).
+bool log_enabled();
+void log_launch(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+
 }  // namespace qblk

@@ -779,11 +779,13 @@ hipError_t launch_quantize_q4_0(const void* w, int wt, int64_t rows, int64_t k, 
   uint8_t* out = static_cast<uint8_t*>(blocks);
   if (wt == QBLK_F32) {  // 8 weights per thread: 32-byte coalesced loads
     const unsigned g = grid_for(rows * k);
+    if (log_enabled()) log_launch("quantize k_quant_q4_0 in=%d rows=%lld k=%lld grid=%u", wt, (long long)rows, (long long)k, g);
     hipLaunchKernelGGL(k_quant_q4_0<QBLK_F32>, dim3(g), dim3(kThreads), 0, s, w, out, nb);
     return hipGetLastError();
   }
   // 16-bit inputs: one 32-weight block per thread (64-byte loads)
   const unsigned g = static_cast<unsigned>((nb + kThreads - 1) / kThreads);
+  if (log_enabled()) log_launch("quantize k_quant_q4_0_g in=%d rows=%lld k=%lld grid=%u", wt, (long long)rows, (long long)k, g);
   if (wt == QBLK_F16) hipLaunchKernelGGL(k_quant_q4_0_g<QBLK_F16>, dim3(g), dim3(kThreads), 0, s, w, out, nb);
   else hipLaunchKernelGGL(k_quant_q4_0_g<QBLK_BF16>, dim3(g), dim3(kThreads), 0, s, w, out, nb);
   return hipGetLastError();
@@ -791,6 +793,8 @@ hipError_t launch_quantize_q4_0(const void* w, int wt, int64_t rows, int64_t k, 
 
 hipError_t launch_quantize_q4_0_ref(const float* w, int64_t rows, int64_t k, void* blocks,
                                     hipStream_t s) {
+  if (log_enabled())
+    log_launch("quantize k_quant_q4_0_ref rows=%lld k=%lld grid=%u", (long long)rows, (long long)k, grid_for(rows * k));
   hipLaunchKernelGGL(k_quant_q4_0_ref, dim3(grid_for(rows * k)), dim3(kThreads), 0, s, w,
                      static_cast<uint8_t*>(blocks), rows * k / 32);
   return hipGetLastError();
@@ -813,6 +817,10 @@ hipError_t launch_quantize_sb4(const void* w, int wt, int64_t rows, int64_t k, i
                                void* blocks, hipStream_t s) {
   const int64_t nsb = rows * k / 256;
   uint8_t* out = static_cast<uint8_t*>(blocks);
+  if (log_enabled())
+    log_launch("quantize %s affine=%d in=%d rows=%lld k=%lld super-blocks=%lld",
+               wt == QBLK_F32 ? "k_quant_sb4" : "k_quant_sb4_g", affine, wt, (long long)rows, (long long)k,
+               (long long)nsb);
   if (affine) launch_sb4_t<true>(w, wt, nsb, out, s);
   else launch_sb4_t<false>(w, wt, nsb, out, s);
   return hipGetLastError();
@@ -824,6 +832,7 @@ hipError_t launch_quantize_w4g128(const void* w, int wt, int64_t rows, int64_t k
   uint8_t* codes = static_cast<uint8_t*>(blocks);
   uint8_t* scales = codes + rows * k / 2;
   const unsigned g = static_cast<unsigned>((ng + kThreads / 16 - 1) / (kThreads / 16));
+  if (log_enabled()) log_launch("quantize k_quant_w4g128 in=%d rows=%lld k=%lld grid=%u", wt, (long long)rows, (long long)k, g);
   if (wt == QBLK_F32) hipLaunchKernelGGL(k_quant_w4g128<QBLK_F32>, dim3(g), dim3(kThreads), 0, s, w, codes, scales, ng);
   else if (wt == QBLK_F16) hipLaunchKernelGGL(k_quant_w4g128<QBLK_F16>, dim3(g), dim3(kThreads), 0, s, w, codes, scales, ng);
   else hipLaunchKernelGGL(k_quant_w4g128<QBLK_BF16>, dim3(g), dim3(kThreads), 0, s, w, codes, scales, ng);
@@ -833,6 +842,7 @@ hipError_t launch_quantize_w4g128(const void* w, int wt, int64_t rows, int64_t k
 hipError_t launch_quantize_act_i8(const void* x, int xt, int64_t n, int64_t k, int8_t* xq, float* scale,
                                   hipStream_t s) {
   const dim3 g(static_cast<unsigned>(n));
+  if (log_enabled()) log_launch("quantize k_quant_act_i8 in=%d n=%lld k=%lld grid=%lld", xt, (long long)n, (long long)k, (long long)n);
   if (xt == QBLK_F32) hipLaunchKernelGGL(k_quant_act_i8<QBLK_F32>, g, dim3(kThreads), 0, s, x, xq, scale, k);
   else if (xt == QBLK_F16) hipLaunchKernelGGL(k_quant_act_i8<QBLK_F16>, g, dim3(kThreads), 0, s, x, xq, scale, k);
   else hipLaunchKernelGGL(k_quant_act_i8<QBLK_BF16>, g, dim3(kThreads), 0, s, x, xq, scale, k);
@@ -843,6 +853,9 @@ hipError_t launch_quantize_q4_k(const void* w, int wt, int64_t rows, int64_t k, 
                                 hipStream_t s) {
   const int64_t nsb = rows * k / 256;
   uint8_t* out = static_cast<uint8_t*>(blocks);
+  if (log_enabled())
+    log_launch("quantize %s in=%d rows=%lld k=%lld super-blocks=%lld", wt == QBLK_F32 ? "k_quant_q4k" : "k_quant_q4k_g",
+               wt, (long long)rows, (long long)k, (long long)nsb);
   if (wt == QBLK_F32) {
     hipLaunchKernelGGL(k_quant_q4k<QBLK_F32>, dim3(static_cast<unsigned>((nsb + 7) / 8)), dim3(kThreads), 0, s,
                        w, out, nsb);
@@ -864,6 +877,9 @@ static void launch_deq_t(const uint8_t* b, int64_t nblk, void* out, int ot, unsi
 hipError_t launch_dequant(int fmt, const void* blocks, int64_t rows, int64_t k, void* out, int ot,
                           hipStream_t s) {
   const uint8_t* b = static_cast<const uint8_t*>(blocks);
+  if (log_enabled())
+    log_launch("dequant %s fmt=%d out=%d rows=%lld k=%lld", fmt == QBLK_W4G128 ? "k_dequant_w4g128" : "k_dequant", fmt,
+               ot, (long long)rows, (long long)k);
   if (fmt == QBLK_W4G128) {
     const int64_t ng = rows * k / 128;
     const uint8_t* sc = b + rows * k / 2;

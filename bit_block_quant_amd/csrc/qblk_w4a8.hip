@@ -27,16 +27,6 @@ __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
   return __builtin_amdgcn_sdot4(static_cast<int>(a), static_cast<int>(b), c, false);
 }
 
-int cu_count_w4() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-  }
-  return n;
-}
 
 // ===================================================================
 // One token: every load of a wave issued up front.
@@ -536,6 +526,9 @@ template <int RMAX, int UPL, int WAVES = kWavesV>
 hipError_t launch_v_t(const uint8_t* codes, const uint16_t* scales, int64_t m, int64_t k, const int8_t* xq,
                       const float* xs, float* y, int rpw, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>((m + rpw - 1) / rpw);
+  if (log_enabled())
+    log_launch("w4a8 k_gemv_w4a8 row-slots/wave=%d chunks/lane=%d waves=%d m=%lld k=%lld rows/wg=%d grid=%u", RMAX,
+               UPL, WAVES, (long long)m, (long long)k, rpw, grid);
   hipLaunchKernelGGL((k_gemv_w4a8<RMAX, UPL, WAVES>), dim3(grid), dim3(WAVES * kWave), 0, s, codes, scales, xq, xs, y,
                      static_cast<int>(m), static_cast<int>(k), rpw);
   return hipGetLastError();
@@ -552,7 +545,7 @@ template <int UPL>
 hipError_t launch_v_u(const uint8_t* codes, const uint16_t* scales, int64_t m, int64_t k, const int8_t* xq,
                       const float* xs, float* y, hipStream_t s) {
   constexpr int kRcap = UPL <= 5 ? 3 : (UPL == 6 ? 2 : 1);
-  int64_t per = (m + cu_count_w4() - 1) / cu_count_w4();  // an even share of the rows over the CUs
+  int64_t per = (m + cu_count() - 1) / cu_count();  // an even share of the rows over the CUs
   if (UPL == 2 && per > 32) {
     const int rpw = static_cast<int>(per > 48 ? 48 : per);
     if (rpw > 36) return launch_v_t<4, UPL, 12>(codes, scales, m, k, xq, xs, y, rpw, s);
@@ -586,6 +579,9 @@ hipError_t launch_mu(const uint8_t* codes, const uint16_t* scales, int64_t m, in
   const unsigned gx = static_cast<unsigned>((m + 63) / 64);
   const unsigned gy = static_cast<unsigned>((n + 15) / 16);
   const unsigned gz = static_cast<unsigned>((k / 128 + NG - 1) / NG);
+  if (log_enabled())
+    log_launch("w4a8 k_gemm_w4a8_u tile=64x16 groups/piece=%d waves/tile=%d m=%lld k=%lld n=%lld grid=%ux%ux%u", NG,
+               KW, (long long)m, (long long)k, (long long)n, gx, gy, gz);
   if (gz > 1) {
     const hipError_t e = launch_fill_zero(y, m * n, s);
     if (e != hipSuccess) return e;
@@ -610,11 +606,17 @@ hipError_t launch_w(const uint8_t* codes, const uint16_t* scales, int64_t m, int
     split = split > ns ? ns : split;
     const int per = (ns + split - 1) / split;
     const unsigned gz = static_cast<unsigned>((ns + per - 1) / per);
+    if (log_enabled())
+      log_launch("w4a8 k_gemm_w4a8_w tile=128x%d groups/stage=%d m=%lld k=%lld n=%lld grid=%ux%ux%u stages/piece=%d",
+                 32 * T32, SG, (long long)m, (long long)k, (long long)n, gx, gy, gz, per);
     const hipError_t e = launch_fill_zero(y, m * n, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_gemm_w4a8_w<T32, SG, true>), dim3(gx, gy, gz), dim3(kThreadsM), 0, s, codes, scales, xq,
                        xs, y, static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), per);
   } else {
+    if (log_enabled())
+      log_launch("w4a8 k_gemm_w4a8_w tile=128x%d groups/stage=%d m=%lld k=%lld n=%lld grid=%ux%ux1 stages/piece=%d",
+                 32 * T32, SG, (long long)m, (long long)k, (long long)n, gx, gy, ns);
     hipLaunchKernelGGL((k_gemm_w4a8_w<T32, SG, false>), dim3(gx, gy, 1), dim3(kThreadsM), 0, s, codes, scales, xq,
                        xs, y, static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), ns);
   }
@@ -638,7 +640,7 @@ hipError_t launch_gemm_w4a8(const void* blocks, int64_t m, int64_t k, const int8
   // N = 256 (N = 200: 40 us against 61 for 128-token tiles, which leave CUs
   // idle at 14336 rows), 128 tokens beyond (N = 512: 69 us against 80; two
   // groups per stage spill at 128 tokens and lose at 64)
-  const int64_t cus = cu_count_w4();
+  const int64_t cus = cu_count();
   if (n <= 32) return launch_mu<4, 2>(codes, scales, m, k, xq, xs, n, y, s);
   if (n <= 64) {
     if ((k / 128) % 2 == 0) return launch_w<1, 2>(codes, scales, m, k, xq, xs, n, y, cus, s);
