@@ -8,11 +8,14 @@ bytes (blocks + x + y = 24,357,888 B) / time per GEMV.
 
 A step is one GEMV launch.  The weights rotate through enough distinct copies
 (> 2x the 256 MB last-level cache) that every step streams them from HBM.  The
-K timed steps are captured in HIP graphs (no host launch gaps) and timed with
-HIP events on the replay stream; the average launch duration is the timed
-region / K.  Beside the nominal 8 TB/s, "hbm_reference" gives what a plain
-streaming read of the same bytes (and of 1 GiB) reaches on the same GPU, the
-launch cost of an empty kernel in the same kind of graph, and torch's copy.
+K timed steps are launched eagerly and back to back and timed with HIP
+events, the start event queued behind a device-side wait longer than the
+host needs to submit them (so the GPU runs them with no host gaps, and
+without the fixed ~10 us a HIP graph replay adds); the average launch
+duration is the timed region / K.  Beside the nominal 8 TB/s,
+"hbm_reference" gives what a plain streaming read of the same bytes (and of
+1 GiB) reaches on the same GPU, the launch cost of an empty kernel timed the
+same way, and torch's copy.
 
 Also measured (field "rows"): every other step of the hot path at the shapes
 of the synthetic workloads -- quantization (Q4_0, super-block Type 0 and
@@ -52,45 +55,60 @@ def log(*a):
 
 
 class Timer:
-    """Capture `launch(i % n)` for i in range(n * rot) into a HIP graph (rot
-    passes over the n rotating inputs); time replays.  Short kernels take
-    several passes per graph so that the boundary between two replays is not
-    part of every few launches."""
+    """Time `launch(i % n)` for i in range(n * rot) (rot passes over the n
+    rotating inputs), launched eagerly and back to back: the timed launches
+    are queued behind a device-side wait longer than the host needs to
+    submit them, so the GPU runs them without host gaps.  (A HIP graph of
+    the same launches costs a fixed ~10 us per replay on top: 20 headline
+    GEMVs averaged 7.1-7.4 us per launch from a graph, 6.62 us eagerly.)"""
 
     def __init__(self, torch, launch, n, rot=1):
         self.torch = torch
+        self.launch = launch
+        self.n_in = n
         self.n = n * rot
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            for i in range(n):  # eager pass (also loads the kernels)
-                launch(i)
-        torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
-        self.g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(self.g):
-            for i in range(n * rot):
-                launch(i % n)
+        t0 = time.perf_counter()
+        for i in range(n):  # first pass: loads the kernels, measures the host's cost per launch
+            launch(i)
+        self.host_us = (time.perf_counter() - t0) * 1e6 / n
         torch.cuda.synchronize()
+
+    def pass_(self, count):
+        for i in range(count):
+            self.launch(i % self.n_in)
 
     def run(self, reps, warmup=1):
         t = self.torch
         for _ in range(warmup):
-            self.g.replay()
+            self.pass_(self.n)
         t.cuda.synchronize()
         a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        lead_in(t, 200.0 + 2.0 * self.host_us * reps * self.n)
         a.record()
         for _ in range(reps):
-            self.g.replay()
+            self.pass_(self.n)
         b.record()
         t.cuda.synchronize()
         return a.elapsed_time(b) / (reps * self.n)  # ms per launch
 
 
-def time_region(torch, fn):
-    """ms for fn() on the current stream, HIP events, synchronized both sides."""
+def lead_in(torch, us=300.0):
+    """Queue a wait of about `us` on the current stream (one wave polling the
+    device clock) just before a timed region's start event, so that the
+    region starts with its work already queued instead of measuring the
+    host's submission as well."""
+    import ctypes as Cty
+    rc = _hbmref_lib().hbmref_spin(us, Cty.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0, rc
+
+
+def time_region(torch, fn, lead_us=300.0):
+    """ms for fn() on the current stream, HIP events, synchronized both sides;
+    the region starts after a lead-in wait of lead_us, with fn's work queued."""
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    lead_in(torch, lead_us)
     a.record()
     fn()
     b.record()
@@ -98,12 +116,19 @@ def time_region(torch, fn):
     return a.elapsed_time(b)
 
 
+_HBMREF = []
+
+
 def _hbmref_lib():
-    """libqblk_hbmref.so: a plain streaming read and an empty kernel, built
-    beside libqblk but not part of it."""
+    """libqblk_hbmref.so: a plain streaming read, an empty kernel and a timed
+    wait, built beside libqblk but not part of it."""
     import ctypes as C
+    if _HBMREF:
+        return _HBMREF[0]
     path = os.path.join(ROOT, "bit_block_quant_amd", "libqblk_hbmref.so")
     L = C.CDLL(path)
+    L.hbmref_spin.argtypes, L.hbmref_spin.restype = [C.c_double, C.c_void_p], C.c_int
+    _HBMREF.append(L)
     L.hbmref_read.argtypes, L.hbmref_read.restype = [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p], C.c_int
     L.hbmref_empty.argtypes, L.hbmref_empty.restype = [C.c_uint, C.c_void_p, C.c_void_p], C.c_int
     return L
@@ -114,7 +139,7 @@ def hbm_reference(torch, dev, nbytes, C):
     the nominal 8 TB/s: a plain 16-byte-per-thread read of the headline's byte
     count over C rotating buffers (so every launch reads HBM) and of 1 GiB;
     torch's copy kernel over the same (bytes = read + write); and the launch
-    cost of an empty kernel of 256 workgroups in the same kind of graph."""
+    cost of an empty kernel of 256 workgroups timed the same way."""
     import ctypes as Cty
     out = {}
     L = _hbmref_lib()
@@ -168,6 +193,8 @@ def main():
                     help="traffic: a 256 MiB device copy (counter calibration) then a few "
                          "headline GEMV launches, for rocprofv3 --pmc runs; gemm: three "
                          "launches of one prefill GEMM (--gemm-shape, --gemm-n), for counters")
+    ap.add_argument("--gemv-case", choices=tuple(GEMV_CASES), default="sb4_11008x4096",
+                    help="decode GEMV of the --mode traffic launches")
     ap.add_argument("--gemm-shape", choices=("up", "down"), default="up")
     ap.add_argument("--gemm-n", type=int, default=512)
     ap.add_argument("--gemm-fmt", choices=("sb4", "q4_0", "sb4a", "q4k", "w4a8"), default="sb4",
@@ -191,7 +218,7 @@ def main():
     dev = torch.device("cuda:0")
 
     if args.mode == "traffic":
-        traffic_run(torch, q, WL, dev)
+        traffic_run(torch, q, WL, dev, args.gemv_case)
         return
     if args.mode == "gemm":
         gemm_run(torch, q, WL, np, dev, args.gemm_shape, args.gemm_n, args.gemm_fmt)
@@ -209,15 +236,10 @@ def main():
     algo_bytes = nbytes + 2 * K + 4 * M
     log(f"gemv sb4 {M}x{K}: {nbytes} B of blocks, {C} rotating copies ({C * nbytes / 2**20:.0f} MiB)")
 
-    # exactly `steps` launches: a graph of G = whole passes over the C copies
-    # (up to 2000 launches) replayed steps // G times, then a graph of the
-    # remaining steps % G.  One graph per 24 launches instead measures the
-    # replay boundary as well (7.34-7.46 against 7.22 us per launch).
+    # exactly `steps` launches, eager and back to back (see Timer), copy
+    # i % C for step i
     launch = lambda i: q.gemv(copies[i % C], q.SB4, M, K, xd, out=yd)  # noqa: E731
-    G = C * max(1, min(args.steps, 2000) // C)
-    full, rem = divmod(args.steps, G)
-    g_full = Timer(torch, launch, C, G // C)
-    g_rem = Timer(torch, launch, rem) if rem else None
+    t_first = Timer(torch, launch, C)  # loads the kernel, measures the host's cost per launch
     # untimed warmup launches on the copies the timed region reads last (or
     # not at all), so none of the first timed launches finds its weights
     # still in the 256 MB last-level cache
@@ -225,13 +247,11 @@ def main():
         launch((C - args.warmup % C + i) % C)
 
     def region():
-        for _ in range(full):
-            g_full.g.replay()
-        if g_rem is not None:
-            g_rem.g.replay()
+        for i in range(args.steps):
+            launch(i)
 
     steps = args.steps
-    ms = time_region(torch, region) / steps
+    ms = time_region(torch, region, 300.0 + 2.0 * t_first.host_us * steps) / steps
     gbs = algo_bytes / (ms * 1e-3) / 1e9
     log(f"  {ms * 1e3:.2f} us per GEMV, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
     achievable = hbm_reference(torch, dev, nbytes, C)
@@ -261,7 +281,7 @@ def main():
             "m": M, "k": K, "x": "f16", "y": "f32",
             "algorithmic_bytes": algo_bytes,
             "rotating_copies": C,
-            "timing": "HIP graph of back-to-back launches, HIP events",
+            "timing": "back-to-back eager launches queued behind a device-side wait, HIP events",
         },
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {
@@ -290,28 +310,46 @@ def main():
 CALIB_BYTES = 256 << 20
 
 
-def traffic_run(torch, q, WL, dev):
+# decode GEMVs that --mode traffic can run: (format name, workload, x dtype)
+GEMV_CASES = {
+    "sb4_11008x4096": ("SB4", "sb4_up"),
+    "sb4_4096x11008": ("SB4", "sb4_down"),
+    "q4_0_4096x4096": ("Q4_0", "q4_0_decode"),
+    "sb4a_11008x4096": ("SB4_AFFINE", "sb4_up"),
+    "sb4a_4096x11008": ("SB4_AFFINE", "sb4_down"),
+    "sb4a_4096x4096": ("SB4_AFFINE", "q4_0_decode"),
+}
+
+
+def traffic_run(torch, q, WL, dev, case="sb4_11008x4096"):
     """A known-size streaming kernel (fp32 multiply: reads and writes
-    CALIB_BYTES once each), then 8 GEMV launches on distinct copies of the
-    headline blocks."""
+    CALIB_BYTES once each), then 8 launches of one decode GEMV on distinct
+    copies of its blocks (every launch reads HBM)."""
     src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     torch.mul(src, 2.0, out=dst)
     torch.cuda.synchronize()
     del src, dst
-    w, x = WL.sb4_decode("up")
+    fmt_name, wl = GEMV_CASES[case]
+    fmt = getattr(q, fmt_name)
+    if wl == "sb4_up":
+        w, x = WL.sb4_decode("up")
+    elif wl == "sb4_down":
+        w, x = WL.sb4_decode("down")
+    else:
+        w, x = WL.q4_0_decode()
     M, K = w.shape
-    b0 = q.quantize(torch.from_numpy(w).to(dev), q.SB4)
+    b0 = q.quantize(torch.from_numpy(w).to(dev), fmt)
     C = n_copies(b0.numel())
     cps = [b0] + [b0.clone() for _ in range(C - 1)]
     xd = torch.from_numpy(x).to(dev)
     y = torch.empty(M, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     for i in range(8):
-        q.gemv(cps[(i + 1) % C], q.SB4, M, K, xd, out=y)
+        q.gemv(cps[(i + 1) % C], fmt, M, K, xd, out=y)
     torch.cuda.synchronize()
-    log("traffic run done")
+    log(f"traffic run done ({case})")
 
 
 def gemm_run(torch, q, WL, np, dev, shape, n_tok, fmt_name="sb4"):
@@ -360,7 +398,18 @@ def measure_rows(torch, q, WL, np, dev):
         y = torch.empty(m, dtype=torch.float32, device=dev)
         t = Timer(torch, lambda i: q.gemv(cps[i], fmt, m, k, x, out=y), C, max(1, 400 // C))
         ms = t.run(1)
-        hbm_row(name, ms, b0.numel() + x.numel() * x.element_size() + 4 * m, m=m, k=k)
+        # the plain 16-byte read of the same blocks, timed the same way: what a
+        # kernel that only reads them reaches at this size
+        import ctypes as Cty
+        L = _hbmref_lib()
+        sink = torch.zeros(64, dtype=torch.int32, device=dev)
+        nb16 = b0.numel() // 16 * 16
+        tr = Timer(torch, lambda i: L.hbmref_read(Cty.c_void_p(cps[i].data_ptr()), nb16, Cty.c_void_p(sink.data_ptr()),
+                                                  Cty.c_void_p(torch.cuda.current_stream().cuda_stream)),
+                   C, max(1, 400 // C))
+        read_ms = tr.run(1)
+        hbm_row(name, ms, b0.numel() + x.numel() * x.element_size() + 4 * m, m=m, k=k,
+                read_ref_us=round(read_ms * 1e3, 3), read_ref_over_gemv=round(read_ms / ms, 3))
 
     w, x = WL.sb4_decode("down")
     gemv_row("gemv_sb4_4096x11008_f16", q.SB4, torch.from_numpy(w).to(dev), torch.from_numpy(x).to(dev))
@@ -373,7 +422,7 @@ def measure_rows(torch, q, WL, np, dev):
 
     # quantizers
     def quant_row(name, fmt, w):
-        # rotating input copies (past the last-level cache), one graph of C launches
+        # rotating input copies (past the last-level cache), C launches per pass
         out = torch.empty(q.packed_bytes(fmt, *w.shape), dtype=torch.uint8, device=dev)
         C = n_copies(w.numel() * w.element_size())
         ws = [w] + [w.clone() for _ in range(C - 1)]
@@ -530,7 +579,7 @@ def w4a8_rows(torch, q, WL, np, dev):
     y = torch.empty((1, m), dtype=torch.float32, device=dev)
     t = Timer(torch, lambda i: q.gemm_w4a8(cps[i], m, k, xq, xs, out=y), C, max(1, 400 // C))
     row(f"gemv_w4a8_{m}x{k}_i8", t.run(1), b0.numel() + k + 4 + 4 * m)
-    t = Timer(torch, lambda i: q.quantize_act_i8(xd, out=xq, scale=xs), 50)  # 50 launches per graph
+    t = Timer(torch, lambda i: q.quantize_act_i8(xd, out=xq, scale=xs), 50)  # 50 launches per pass
     row(f"quantize_act_i8_1x{k}_f16", t.run(4), k * 2 + k + 4)
     del cps
 

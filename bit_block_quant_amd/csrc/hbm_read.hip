@@ -26,6 +26,18 @@ __global__ __launch_bounds__(kThreads) void k_empty(uint32_t* sink, int flag) {
   if (flag == 0x5bd1e995 && threadIdx.x == 0) sink[blockIdx.x] = 1u;
 }
 
+// One wave that waits until `ticks` periods of the constant-rate device clock
+// have passed (at most 2^22 polls, so it always ends).  Launched just before
+// a timed region's start event: the GPU is then busy while the host submits
+// the timed work, and the region starts with that work already queued.
+__global__ __launch_bounds__(64) void k_spin(uint64_t ticks) {
+  const uint64_t t0 = wall_clock64();
+  for (int i = 0; i < (1 << 22); ++i) {
+    if (wall_clock64() - t0 >= ticks) break;
+    __builtin_amdgcn_s_sleep(4);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -45,6 +57,19 @@ int hbmref_read(const void* p, int64_t nbytes, void* sink, void* stream) {
 int hbmref_empty(unsigned grid, void* sink, void* stream) {
   hipLaunchKernelGGL(k_empty, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                      static_cast<uint32_t*>(sink), 0);
+  return hipGetLastError();
+}
+
+// Keep the GPU busy for about `us` microseconds (one wave polling the
+// device's constant-rate clock).  Returns a hipError_t.
+int hbmref_spin(double us, void* stream) {
+  int dev = 0, khz = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+  if (e != hipSuccess) return e;
+  if (khz <= 0 || us <= 0) return hipSuccess;
+  const uint64_t ticks = static_cast<uint64_t>(us * 1e-3 * khz);
+  hipLaunchKernelGGL(k_spin, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), ticks);
   return hipGetLastError();
 }
 

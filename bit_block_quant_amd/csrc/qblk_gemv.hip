@@ -323,7 +323,7 @@ struct UnitAddr {
 
 // KS waves share a row (KS = 2 splits the row's units in two halves whose
 // sums meet in LDS after the only barrier of the kernel); WAVES waves per
-// workgroup (one workgroup per CU).  XL > 0 (one wave per row only): x is
+// workgroup (one workgroup per CU).  XL > 0: x is
 // loaded once per workgroup -- every thread a few 4-element pieces, ahead of
 // its weight loads -- written to LDS already paired, published with one
 // barrier and read back per unit, instead of every wave loading the x of its
@@ -331,6 +331,10 @@ struct UnitAddr {
 // any is issued: a barrier passed with loads in flight waits for them on this
 // part (an 11008 x 4096 launch with the barrier after its loads took 8.4 us,
 // one with it before 6.9 us), so XL = 2 pays only the latency of x first.
+// (Publishing without the barrier does not help: with every wave's weight
+// loads issued behind its piece of x, each wave counting itself in LDS once
+// its piece is written and waiting for the count, 11008 x 4096 took 8.40 us
+// against 6.61: the last pieces of x arrive behind the weight loads.)
 template <int FMT, int RMAX, int UPL, int KS, int WAVES = kWavesH, int XL = 0>
 __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restrict__ blocks,
                                                       const uint16_t* __restrict__ x,
@@ -347,7 +351,6 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restr
   const int slot = wave / KS, part = wave % KS;
   const int row0 = blockIdx.x * rows_per_wg;
   const int row_end = min(M, row0 + rows_per_wg);
-  static_assert(!XL || KS == 1, "x through LDS: one wave per row");
   // (KS > 1 or XL: every wave meets the barrier)
   if (KS == 1 && !XL && row0 + slot >= row_end) return;
   const int64_t rowbytes = static_cast<int64_t>(K / E) * B;
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restr
   uint4 xr[UPL][4];
   // XL: this thread's pieces of x (4 elements each) for the LDS copy; units
   // past the row's last one are written as zeros
-  constexpr int kPieces = XL ? UPL * 64 * 8 : 0;  // 8 pieces per unit
+  constexpr int kPieces = XL ? KS * UPL * 64 * 8 : 0;  // 8 pieces per unit, every part's units
   constexpr int kPPT = XL ? (kPieces + WAVES * kWave - 1) / (WAVES * kWave) : 1;
   uint2 xp[kPPT];
   if constexpr (XL) {
@@ -390,8 +393,11 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restr
       xp[j] = *reinterpret_cast<const uint2*>(x + 4 * pc);
     }
   }
-  // XL: pairs of unit lane + 64k, word t, at xs[(4k + t) * 64 + lane]
-  __shared__ uint4 xs[XL ? UPL * 4 * 64 : 1];
+  // XL: pairs of unit u, word t, at xs[(4 (u / 64) + t) * 64 + (u + 8t) % 64]
+  // (the rotation by 8t puts the four words of a unit, written by
+  // neighbouring threads, in different banks: 4-way conflicts on the writes
+  // become 2-way; the reads stay conflict-free)
+  __shared__ uint4 xs[XL ? KS * UPL * 4 * 64 : 1];
   auto publish_x = [&]() {
 #pragma unroll
     for (int j = 0; j < kPPT; j++) {
@@ -401,7 +407,7 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restr
       if (pc >= 8 * S) v = make_uint2(0u, 0u);  // units past the row's last one
       if (pc < kPieces) {
         const int u = pc >> 3, q = pc & 7, t = q & 3, hh = q >> 2;
-        uint32_t* w = reinterpret_cast<uint32_t*>(xs + (4 * (u >> 6) + t) * 64 + (u & 63));
+        uint32_t* w = reinterpret_cast<uint32_t*>(xs + (4 * (u >> 6) + t) * 64 + ((u + 8 * t) & 63));
         w[hh] = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);      // (x0, x2)
         w[2 + hh] = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);  // (x1, x3)
       }
@@ -412,7 +418,7 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restr
   };
   if constexpr (XL == 2) {
     publish_x();
-    if (row0 + slot >= row_end) return;
+    if (KS == 1 && row0 + slot >= row_end) return;
   }
   auto load_x = [&](int k) {
     const int u = min(part * SP + lane + 64 * k, S - 1);
@@ -475,12 +481,13 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restr
   const half2_t kOne = {1.0f16, 1.0f16};
   if constexpr (XL == 1) {
     publish_x();
-    if (row0 + slot >= row_end) return;
+    if (KS == 1 && row0 + slot >= row_end) return;
   }
   auto make_pairs = [&](int k) {
     if constexpr (XL) {
+      const int uu = part * SP + lane + 64 * k;  // < KS * UPL * 64
 #pragma unroll
-      for (int t = 0; t < 4; t++) X[k][t] = xs[(4 * k + t) * 64 + lane];
+      for (int t = 0; t < 4; t++) X[k][t] = xs[(4 * (uu >> 6) + t) * 64 + ((uu + 8 * t) & 63)];
       sx[k] = 0.0f;
       if constexpr (AFFINE) {
 #pragma unroll
@@ -734,7 +741,10 @@ hipError_t launch_h_k(const void* blocks, int64_t m, int64_t k, const void* x, f
 // us); up to 256 two waves per row with two units per lane; up to
 // 384 three (Type 0 in 12-wave workgroups with up to 3 rows per wave: 4096 x
 // 11008 7.98 against 8.20 us; the other formats gain 1.4% at most, and Q4_K
-// runs out of registers).  With at most 16 rows per CU, x read by every wave
+// runs out of registers; Type 0 with at most 16 rows per CU stages x through
+// LDS before its loads, 4096 x 11008: 7.96 -> 7.00 us; for Type 1 and Q4_K,
+// and Q4_0 at 4096 x 4096, staging so was slower: 7.71 -> 7.75, 7.27 -> 7.36,
+// 4.00 -> 4.23 us).  With at most 16 rows per CU, x read by every wave
 // outweighs the weights; x through LDS (one wave per row) is taken where it
 // measured faster: Q4_0 up to 128 units (4096 x 4096: 4.44 -> 4.00 us) and
 // Type 1 beyond 256 (4096 x 11008: 8.35 -> 7.68 us); for Type 0 and Q4_K it
@@ -757,6 +767,7 @@ bool launch_h(const void* blocks, int64_t m, int64_t k, const void* x, float* y,
   else if (S <= 128 && kSigned && per_cu > 32) *err = launch_h_k<FMT, 2, 1, 3, kWavesH, 2>(blocks, m, k, x, y, s);
   else if (S <= 128) *err = launch_h_k<FMT, 1, 2, 6>(blocks, m, k, x, y, s);
   else if (S <= 256) *err = launch_h_k<FMT, 2, 2, 3>(blocks, m, k, x, y, s);
+  else if (FMT == QBLK_SB4 && few) *err = launch_h_k<FMT, 3, 2, 2, kWavesH, 2>(blocks, m, k, x, y, s);
   else if (FMT == QBLK_SB4) *err = launch_h_k<FMT, 3, 2, 3, 12>(blocks, m, k, x, y, s);
   else *err = launch_h_k<FMT, 3, 2, 2>(blocks, m, k, x, y, s);
   return true;
