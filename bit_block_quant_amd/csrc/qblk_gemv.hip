@@ -334,7 +334,9 @@ struct UnitAddr {
 // (Publishing without the barrier does not help: with every wave's weight
 // loads issued behind its piece of x, each wave counting itself in LDS once
 // its piece is written and waiting for the count, 11008 x 4096 took 8.40 us
-// against 6.61: the last pieces of x arrive behind the weight loads.)
+// against 6.61 -- 8.44 us even with every piece of x requested, behind one
+// barrier, before any weight request of the workgroup: x is then fetched
+// while every CU's weight requests are in flight, and arrives late.)
 template <int FMT, int RMAX, int UPL, int KS, int WAVES = kWavesH, int XL = 0>
 __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restrict__ blocks,
                                                       const uint16_t* __restrict__ x,
