@@ -296,8 +296,8 @@ struct GroupW<QBLK_Q4_K> {
   }
 };
 
-template <int FMT, int T32, bool SPLIT>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm_w(const uint8_t* __restrict__ W,
+template <int FMT, int T32, int OCC, bool SPLIT>
+__global__ __launch_bounds__(kThreads, OCC) void k_gemm_w(const uint8_t* __restrict__ W,
                                                           const uint16_t* __restrict__ X,
                                                           float* __restrict__ Y, int M, int K, int N,
                                                           int sb_per_split) {
@@ -320,20 +320,20 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_w(const uint8_t* __restric
   const uint8_t* rowp = W + (m < M ? m : M - 1) * rowbytes;
 
   // stage q = 2*b + half: thread t moves pieces t, t+256, ...; piece i of the
-  // stage is token i/16, 16-byte piece i%16 of that token's 128 k.  Tokens
-  // past N read the last token's row instead: their products are never stored.
-  uint32_t xoff[kPer];  // byte offset of the thread's pieces from token n0, k 0
-#pragma unroll
-  for (int i = 0; i < kPer; i++) {
-    const int c = threadIdx.x + i * kThreads;
-    const int t = min(c >> 4, N - 1 - n0), pc = c & 15;
-    xoff[i] = static_cast<uint32_t>(t) * static_cast<uint32_t>(K) * 2u + 16u * pc;
-  }
-  const uint8_t* xtile = reinterpret_cast<const uint8_t*>(X + static_cast<int64_t>(n0) * K);
+  // stage is token i/16, 16-byte piece i%16 of that token's 128 k, so the
+  // thread's piece i is token (t >> 4) + 16 i, piece t & 15 (token offsets in
+  // 64 bits: a row of K bf16 is up to 4 GiB).  Tokens past N read the last
+  // token's row instead: their products are never stored.
+  const int tlast = N - 1 - n0;
+  const uint8_t* xtile =
+      reinterpret_cast<const uint8_t*>(X + static_cast<int64_t>(n0) * K) + 16 * (threadIdx.x & 15);
   auto load_x = [&](int q, uint4 xv[kPer]) {
     const uint8_t* xq = xtile + 256 * q;
 #pragma unroll
-    for (int i = 0; i < kPer; i++) xv[i] = *reinterpret_cast<const uint4*>(xq + xoff[i]);
+    for (int i = 0; i < kPer; i++) {
+      const int t = min(static_cast<int>(threadIdx.x >> 4) + 16 * i, tlast);
+      xv[i] = *reinterpret_cast<const uint4*>(xq + static_cast<uint64_t>(t) * (2u * static_cast<uint32_t>(K)));
+    }
   };
   auto store_x = [&](int buf, const uint4 xv[kPer]) {
 #pragma unroll
@@ -439,38 +439,68 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm_w(const uint8_t* __restric
 }
 
 
-template <int FMT, int T32>
-hipError_t launch_w(const void* blocks, int64_t m, int64_t k, const void* x, int64_t n, float* y,
-                    hipStream_t s) {
-  const unsigned gx = static_cast<unsigned>((m + 127) / 128);
-  const unsigned gy = static_cast<unsigned>((n + 32 * T32 - 1) / (32 * T32));
-  const int nsb = static_cast<int>(k / 256);
-  // split K when the tiles alone leave CUs idle (two workgroups fit per CU)
-  const int64_t tiles = static_cast<int64_t>(gx) * gy;
-  const int cus = cu_count();
-  int split = 1;
-  if (tiles < cus) {
-    split = static_cast<int>((2 * cus + tiles - 1) / tiles);
-    const int max_split = nsb / 2 > 1 ? nsb / 2 : 1;  // keep >= 2 super-blocks per piece
+// Grid of the wide kernel: 128-row by nt-token tiles, K split into pieces
+// when the tiles alone leave workgroup slots (slots = workgroups resident at
+// once) idle -- floor(slots / tiles) pieces, so that the grid still fits one
+// round, of at least two super-blocks each.
+struct WideGrid {
+  unsigned gx, gy;
+  int split, per;  // K pieces and super-blocks per piece
+};
+
+WideGrid wide_grid(int64_t m, int64_t n, int nsb, int nt, int64_t slots) {
+  WideGrid g;
+  g.gx = static_cast<unsigned>((m + 127) / 128);
+  g.gy = static_cast<unsigned>((n + nt - 1) / nt);
+  const int64_t tiles = static_cast<int64_t>(g.gx) * g.gy;
+  int64_t split = 1;
+  if (tiles < slots) {
+    split = slots / tiles;
+    const int64_t max_split = nsb / 2 > 1 ? nsb / 2 : 1;
     split = split > max_split ? max_split : split;
   }
-  const int per = (nsb + split - 1) / split;
-  split = (nsb + per - 1) / per;
+  g.per = static_cast<int>((nsb + split - 1) / split);
+  g.split = (nsb + g.per - 1) / g.per;
+  return g;
+}
+
+template <int FMT, int T32, int OCC>
+hipError_t launch_w_t(const void* blocks, int64_t m, int64_t k, const void* x, int64_t n, float* y,
+                      const WideGrid& g, hipStream_t s) {
+  const int nsb = static_cast<int>(k / 256);
   if (log_enabled())
-    log_launch("gemm k_gemm_w fmt=%d tile=128x%d m=%lld k=%lld n=%lld grid=%ux%ux%d super-blocks/piece=%d", FMT,
-               32 * T32, (long long)m, (long long)k, (long long)n, gx, gy, split, split > 1 ? per : nsb);
-  if (split > 1) {
+    log_launch("gemm k_gemm_w fmt=%d tile=128x%d (%d per CU) m=%lld k=%lld n=%lld grid=%ux%ux%d "
+               "super-blocks/piece=%d", FMT, 32 * T32, OCC, (long long)m, (long long)k, (long long)n, g.gx, g.gy,
+               g.split, g.per);
+  if (g.split > 1) {
     const hipError_t e = launch_fill_zero(y, m * n, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_gemm_w<FMT, T32, true>), dim3(gx, gy, split), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((k_gemm_w<FMT, T32, OCC, true>), dim3(g.gx, g.gy, g.split), dim3(kThreads), 0, s,
                        static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
-                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), per);
+                       static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), g.per);
   } else {
-    hipLaunchKernelGGL((k_gemm_w<FMT, T32, false>), dim3(gx, gy, 1), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((k_gemm_w<FMT, T32, OCC, false>), dim3(g.gx, g.gy, 1), dim3(kThreads), 0, s,
                        static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
                        static_cast<int>(m), static_cast<int>(k), static_cast<int>(n), nsb);
   }
   return hipGetLastError();
+}
+
+// 128-token tiles, two workgroups per CU.  The affine formats switch to
+// 64-token tiles, three workgroups per CU (their registers allow it), when
+// 128-token tiles would fill under 3/4 of the slots without splitting K.
+template <int FMT>
+hipError_t launch_w(const void* blocks, int64_t m, int64_t k, const void* x, int64_t n, float* y,
+                    hipStream_t s) {
+  constexpr bool AFFINE = FMT == QBLK_SB4_AFFINE || FMT == QBLK_Q4_K;
+  const int nsb = static_cast<int>(k / 256);
+  const int64_t cus = cu_count();
+  const WideGrid g4 = wide_grid(m, n, nsb, 128, 2 * cus);
+  if constexpr (AFFINE) {
+    if (static_cast<int64_t>(g4.gx) * g4.gy * 4 < 3 * 2 * cus)
+      return launch_w_t<FMT, 2, 3>(blocks, m, k, x, n, y, wide_grid(m, n, nsb, 64, 3 * cus), s);
+  }
+  return launch_w_t<FMT, 4, 2>(blocks, m, k, x, n, y, g4, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -973,10 +1003,10 @@ hipError_t launch_gemm(int fmt, const void* blocks, int64_t m, int64_t k, const 
     }
     return launch_st<QBLK_SB4_AFFINE, 1, 2, 2, 2>(blocks, m, k, x, n, y, s);
   }
-  if (fmt == QBLK_SB4) return launch_w<QBLK_SB4, 4>(blocks, m, k, x, n, y, s);
-  if (fmt == QBLK_Q4_0) return launch_w<QBLK_Q4_0, 4>(blocks, m, k, x, n, y, s);
-  if (fmt == QBLK_Q4_K) return launch_w<QBLK_Q4_K, 4>(blocks, m, k, x, n, y, s);
-  return launch_w<QBLK_SB4_AFFINE, 4>(blocks, m, k, x, n, y, s);
+  if (fmt == QBLK_SB4) return launch_w<QBLK_SB4>(blocks, m, k, x, n, y, s);
+  if (fmt == QBLK_Q4_0) return launch_w<QBLK_Q4_0>(blocks, m, k, x, n, y, s);
+  if (fmt == QBLK_Q4_K) return launch_w<QBLK_Q4_K>(blocks, m, k, x, n, y, s);
+  return launch_w<QBLK_SB4_AFFINE>(blocks, m, k, x, n, y, s);
 }
 
 }  // namespace qblk

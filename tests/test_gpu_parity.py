@@ -427,6 +427,24 @@ def test_gemm_other_formats_split_k(q, fmt, n):
     check_products(Y, Y_ref, B, f"gemm {fmt} split-K")
 
 
+@pytest.mark.parametrize("fmt", ["sb4a", "q4k"])
+def test_gemm_affine_64_token_tiles_unsplit(q, fmt):
+    # 12400 x 512, 200 tokens: 128-token tiles would fill under 3/4 of the
+    # workgroup slots, so the affine formats take 64-token tiles (4 per column
+    # of row tiles, the last one ragged), 388 tiles on 256 CUs: K not split
+    m, k, n = 12400, 512, 200
+    f, of = gemm_fmt(q, fmt)
+    w = mixed_blocks(m, k, 25)
+    blocks = O.quantize(of, w)
+    X = WL.bf16_bits(np.random.default_rng(26).standard_normal((n, k)).astype(np.float32))
+    Y = host(q.gemm(dev(blocks), f, m, k, dev_bf16(X)))
+    rows = np.concatenate([np.random.default_rng(27).choice(m, size=128, replace=False), [0, m - 1]])
+    Xv = WL.bf16_values(X).astype(np.float64)
+    Y_ref, B = O.gemm(of, blocks, m, k, Xv, rows=rows)
+    check_products(Y[:, rows], Y_ref, B, f"gemm {fmt} 64-token tiles")
+    check_all_rows(Y, Xv, O.dequant(of, blocks, m, k).astype(np.float64), f"gemm {fmt} 64-token tiles")
+
+
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: NAMES[f])
 @pytest.mark.parametrize("n", [3, 24, 40, 130])
 def test_gemm_single_super_block(q, fmt, n):
