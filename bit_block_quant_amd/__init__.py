@@ -38,7 +38,7 @@ EXPORTS = (
     "qblk_block_bytes", "qblk_block_elems", "qblk_packed_bytes", "qblk_quantize_q4_0",
     "qblk_quantize_q4_0_ref", "qblk_quantize_sb4", "qblk_quantize_q4_k", "qblk_quantize_w4g128",
     "qblk_quantize_act_i8", "qblk_dequant", "qblk_gemv", "qblk_gemm", "qblk_gemm_w4a8",
-    "qblk_status_string", "qblk_version",
+    "qblk_set_deterministic", "qblk_deterministic", "qblk_status_string", "qblk_version",
 )
 
 
@@ -73,6 +73,8 @@ def _load():
         getattr(L, f).restype = i32
     L.qblk_status_string.argtypes, L.qblk_status_string.restype = [i32], C.c_char_p
     L.qblk_version.argtypes, L.qblk_version.restype = [], C.c_char_p
+    L.qblk_set_deterministic.argtypes, L.qblk_set_deterministic.restype = [i32], i32
+    L.qblk_deterministic.argtypes, L.qblk_deterministic.restype = [], i32
     return L
 
 
@@ -85,6 +87,16 @@ def lib():
 
 def version():
     return _lib.qblk_version().decode()
+
+
+def set_deterministic(on=True):
+    """Reproducible products (qblk_set_deterministic): gemm and gemm_w4a8 stop
+    splitting K over workgroups, so equal inputs give bitwise equal outputs."""
+    _check(_lib.qblk_set_deterministic(1 if on else 0), "qblk_set_deterministic")
+
+
+def deterministic():
+    return bool(_lib.qblk_deterministic())
 
 
 def block_bytes(fmt):

@@ -27,6 +27,11 @@ int cu_count() {
   return n;
 }
 
+// qblk_set_deterministic: 0 off (the default), 1 on
+static std::atomic<int> g_det{0};
+
+bool deterministic() { return g_det.load(std::memory_order_relaxed) != 0; }
+
 // -1 unknown, 0 off, 1 on
 static std::atomic<int> g_log{-1};
 
@@ -275,6 +280,13 @@ const char* qblk_status_string(qblk_status_t st) {
   }
   return "unknown status";
 }
+
+qblk_status_t qblk_set_deterministic(int on) {
+  qblk::g_det.store(on != 0 ? 1 : 0, std::memory_order_relaxed);
+  return QBLK_OK;
+}
+
+int qblk_deterministic(void) { return qblk::deterministic() ? 1 : 0; }
 
 const char* qblk_version(void) { return "0.1.0"; }
 

@@ -495,10 +495,11 @@ hipError_t launch_w(const void* blocks, int64_t m, int64_t k, const void* x, int
   constexpr bool AFFINE = FMT == QBLK_SB4_AFFINE || FMT == QBLK_Q4_K;
   const int nsb = static_cast<int>(k / 256);
   const int64_t cus = cu_count();
-  const WideGrid g4 = wide_grid(m, n, nsb, 128, 2 * cus);
+  const int64_t split_ok = deterministic() ? 0 : 1;  // slots 0: K never split
+  const WideGrid g4 = wide_grid(m, n, nsb, 128, split_ok * 2 * cus);
   if constexpr (AFFINE) {
     if (static_cast<int64_t>(g4.gx) * g4.gy * 4 < 3 * 2 * cus)
-      return launch_w_t<FMT, 2, 3>(blocks, m, k, x, n, y, wide_grid(m, n, nsb, 64, 3 * cus), s);
+      return launch_w_t<FMT, 2, 3>(blocks, m, k, x, n, y, wide_grid(m, n, nsb, 64, split_ok * 3 * cus), s);
   }
   return launch_w_t<FMT, 4, 2>(blocks, m, k, x, n, y, g4, s);
 }
@@ -951,7 +952,7 @@ hipError_t launch_st(const void* blocks, int64_t m, int64_t k, const void* x, in
   const int nsb = static_cast<int>(k / 256);
   const int64_t tiles = static_cast<int64_t>(gx) * gy;
   int split = 1;
-  if (tiles < cu_count()) {
+  if (tiles < cu_count() && !deterministic()) {
     split = static_cast<int>((2 * cu_count() + tiles - 1) / tiles);
     const int max_split = nsb / (2 * NSB) > 1 ? nsb / (2 * NSB) : 1;  // >= 2 stages per piece
     split = split > max_split ? max_split : split;
@@ -988,7 +989,8 @@ hipError_t launch_gemm(int fmt, const void* blocks, int64_t m, int64_t k, const 
   // up to 32 tokens), N = 32: 19.9-22.3 us against 24.1-26.8 us for the
   // double-buffered kernel it replaced, N = 64: 27.2-29.8 us against
   // 35.1-44.9 us; 64-token tiles were 29-36 us at N = 64)
-  if (n <= 16) {
+  // (reproducible products: the streaming kernel up to 64 tokens, K whole)
+  if (n <= 16 && !deterministic()) {
     if (fmt == QBLK_SB4) return launch_u<QBLK_SB4, 1, 1, 2>(blocks, m, k, x, n, y, s);
     if (fmt == QBLK_Q4_0) return launch_u<QBLK_Q4_0, 1, 1, 2>(blocks, m, k, x, n, y, s);
     if (fmt == QBLK_Q4_K) return launch_u<QBLK_Q4_K, 1, 1, 2, 2>(blocks, m, k, x, n, y, s);

@@ -36,6 +36,10 @@ hipError_t launch_fill_zero(float* y, int64_t n, hipStream_t s);
 // 256 if the query fails).  Every launcher sizes its grid from this.
 int cu_count();
 
+// qblk_set_deterministic: when on, the product launchers never split the k
+// range over workgroups (no atomic sums).
+bool deterministic();
+
 // QBLK_LOG=1 in the environment: every launch writes one line to stderr
 // naming the kernel and the tiling it picked (read once per process).
 bool log_enabled();

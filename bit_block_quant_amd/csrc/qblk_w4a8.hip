@@ -640,8 +640,10 @@ hipError_t launch_gemm_w4a8(const void* blocks, int64_t m, int64_t k, const int8
   // N = 256 (N = 200: 40 us against 61 for 128-token tiles, which leave CUs
   // idle at 14336 rows), 128 tokens beyond (N = 512: 69 us against 80; two
   // groups per stage spill at 128 tokens and lose at 64)
-  const int64_t cus = cu_count();
-  if (n <= 32) return launch_mu<4, 2>(codes, scales, m, k, xq, xs, n, y, s);
+  // (reproducible products: no K split, the wide kernel from 2 tokens on)
+  const bool det = deterministic();
+  const int64_t cus = det ? 0 : cu_count();  // tiles wanted before K is split
+  if (n <= 32 && !det) return launch_mu<4, 2>(codes, scales, m, k, xq, xs, n, y, s);
   if (n <= 64) {
     if ((k / 128) % 2 == 0) return launch_w<1, 2>(codes, scales, m, k, xq, xs, n, y, cus, s);
     return launch_w<1, 1>(codes, scales, m, k, xq, xs, n, y, cus, s);

@@ -216,10 +216,24 @@ qblk_status_t qblk_gemv(qblk_format_t fmt, const void* blocks, int64_t m,
  * QBLK_ERR_UNSUPPORTED.  Same error bound as qblk_gemv, per output element.
  * When k spans many groups and m*n is small the k range is split over the
  * grid and partial sums are added into Y (zeroed first by this call), so the
- * summation order, not the bound, varies between tilings. */
+ * summation order, not the bound, varies between tilings and between runs
+ * (qblk_set_deterministic turns the split off). */
 qblk_status_t qblk_gemm(qblk_format_t fmt, const void* blocks, int64_t m,
                         int64_t k, const void* x, qblk_dtype_t xt, int64_t n,
                         float* y, qblk_stream_t stream);
+
+/* Reproducible products.  With on != 0, qblk_gemm and qblk_gemm_w4a8 never
+ * split the k range over workgroups: every output is summed by one
+ * workgroup in a fixed order, so identical inputs and sizes give bitwise
+ * identical Y on the same device, run after run (split sums are added into
+ * Y with fp32 atomics, whose order varies).  Slower where the split paid: few
+ * tokens, or few rows with a long k.  The setting is process-wide, applies to
+ * calls made after it, and is off at load.  Always returns QBLK_OK.  (Not an
+ * operation of the pages: a property of this implementation's sums.) */
+qblk_status_t qblk_set_deterministic(int on);
+
+/* 1 when reproducible products are on (qblk_set_deterministic), else 0. */
+int qblk_deterministic(void);
 
 /* Static English text for a status code (never NULL). */
 const char* qblk_status_string(qblk_status_t st);

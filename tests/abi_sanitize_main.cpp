@@ -238,6 +238,10 @@ int main() {
   for (int st = 0; st <= 7; ++st) EXPECT(strlen(qblk_status_string(static_cast<qblk_status_t>(st))) > 0);
   EXPECT(strcmp(qblk_status_string(static_cast<qblk_status_t>(99)), "unknown status") == 0);
   EXPECT(strlen(qblk_version()) > 0);
+  // the reproducible-products switch: off at load, set and cleared
+  EXPECT(qblk_deterministic() == 0);
+  EXPECT(qblk_set_deterministic(7) == QBLK_OK && qblk_deterministic() == 1);
+  EXPECT(qblk_set_deterministic(0) == QBLK_OK && qblk_deterministic() == 0);
 
   // device queries that fail fall back to 256 compute units
   EXPECT(qblk::cu_count() == 256);

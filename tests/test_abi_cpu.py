@@ -121,3 +121,13 @@ def test_empty_calls_succeed_without_launch(q):
     assert L.qblk_gemv(1, NUL, 0, 256, NUL, 1, NUL, S) == 0
     assert L.qblk_gemm(1, NUL, 0, 256, NUL, 2, 8, NUL, S) == 0
     assert L.qblk_gemm(1, NUL, 8, 256, NUL, 2, 0, NUL, S) == 0
+
+
+def test_deterministic_switch(q):
+    assert q.deterministic() is False  # off at load
+    try:
+        q.set_deterministic(True)
+        assert q.deterministic() is True
+    finally:
+        q.set_deterministic(False)
+    assert q.deterministic() is False

@@ -648,6 +648,45 @@ def test_w4a8_token_slices(q):
 
 
 # ------------------------------------------------------- streams and graphs
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: NAMES[f])
+@pytest.mark.parametrize("m,k,n", [(150, 2304, 16), (40, 14336, 20), (40, 14336, 130), (150, 2304, 100)])
+def test_gemm_deterministic(q, fmt, m, k, n):
+    # reproducible products: shapes whose K is split over the grid by default
+    # (one stage per workgroup, the streaming and the wide kernels) give
+    # bitwise equal outputs over repeated calls, within the bound
+    w = mixed_blocks(m, k, 41)
+    blocks = O.quantize(fmt, w)
+    X = WL.bf16_bits(np.random.default_rng(42).standard_normal((n, k)).astype(np.float32))
+    bd, Xd = dev(blocks), dev_bf16(X)
+    try:
+        q.set_deterministic(True)
+        runs = [host(q.gemm(bd, fmt, m, k, Xd)) for _ in range(4)]
+    finally:
+        q.set_deterministic(False)
+    for Y in runs[1:]:
+        assert np.array_equal(Y.view(np.uint32), runs[0].view(np.uint32))
+    Y_ref, B = O.gemm(fmt, blocks, m, k, WL.bf16_values(X).astype(np.float64))
+    check_products(runs[0], Y_ref, B, f"deterministic gemm {NAMES[fmt]} n={n}")
+
+
+@pytest.mark.parametrize("m,k,n", [(150, 2304, 16), (40, 14336, 40), (40, 14336, 130)])
+def test_gemm_w4a8_deterministic(q, m, k, n):
+    w = mixed_blocks(m, k, 43)
+    blocks = O.quantize_w4g128(w)
+    x = np.random.default_rng(44).standard_normal((n, k)).astype(np.float32)
+    xq, s = O.quantize_act_i8(x)
+    bd, xqd, sd = dev(blocks), dev(xq), dev(s)
+    try:
+        q.set_deterministic(True)
+        runs = [host(q.gemm_w4a8(bd, m, k, xqd, sd)) for _ in range(4)]
+    finally:
+        q.set_deterministic(False)
+    for Y in runs[1:]:
+        assert np.array_equal(Y.view(np.uint32), runs[0].view(np.uint32))
+    Y_ref, B = O.gemm_w4a8(blocks, m, k, xq, s)
+    check_products(runs[0], Y_ref, B, f"deterministic gemm_w4a8 n={n}")
+
+
 def test_side_stream(q):
     # every step enqueues on the stream it is handed: the same calls on a
     # second stream give the oracle's bytes and products
