@@ -487,7 +487,26 @@ def measure_rows(torch, q, WL, np, dev):
     nb = dst + sum(xx.numel() * 2 for xx in xs) + sum(yy.numel() * 4 for yy in ys)
     hbm_row("gemv_sb4a_stack_32x7_f16", ms, nb, tokens_per_s_equivalent=round(1.0 / (ms * 1e-3), 1),
             inputs=stack_inputs)
-    del outs, xs, ys
+
+    # the same pass with each layer's matrices of equal k in one qblk_gemv_batch
+    # call (k = 4096: q, k, v, o, gate, up; k = 11008: down): 2 launches a layer
+    groups = []
+    for layer in range(WL.STACK_LAYERS):
+        by_k = {}
+        for p, (_, r, k) in enumerate(WL.STACK_PROJ):
+            by_k.setdefault(k, []).append(layer * len(WL.STACK_PROJ) + p)
+        for k, idx in by_k.items():
+            groups.append((k, [(outs[i], WL.STACK_PROJ[i % 7][1], xs[i]) for i in idx], [ys[i] for i in idx]))
+
+    def stack_batch(g):
+        k, prods, yo = groups[g]
+        q.gemv_batch(q.SB4_AFFINE, k, prods, outs=yo)
+
+    t = Timer(torch, stack_batch, len(groups))
+    ms = t.run(3) * len(groups)
+    hbm_row("gemv_sb4a_stack_32x7_f16_batched", ms, nb, launches=len(groups),
+            tokens_per_s_equivalent=round(1.0 / (ms * 1e-3), 1), inputs=stack_inputs)
+    del outs, xs, ys, groups
 
     # prefill GEMM
     for shape in ("up", "down"):

@@ -37,7 +37,7 @@ STATUS = {
 EXPORTS = (
     "qblk_block_bytes", "qblk_block_elems", "qblk_packed_bytes", "qblk_quantize_q4_0",
     "qblk_quantize_q4_0_ref", "qblk_quantize_sb4", "qblk_quantize_q4_k", "qblk_quantize_w4g128",
-    "qblk_quantize_act_i8", "qblk_dequant", "qblk_gemv", "qblk_gemm", "qblk_gemm_w4a8",
+    "qblk_quantize_act_i8", "qblk_dequant", "qblk_gemv", "qblk_gemv_batch", "qblk_gemm", "qblk_gemm_w4a8",
     "qblk_set_deterministic", "qblk_deterministic", "qblk_status_string", "qblk_version",
 )
 
@@ -66,6 +66,7 @@ def _load():
     L.qblk_gemm_w4a8.argtypes = [p, i64, i64, p, p, i64, p, p]
     L.qblk_dequant.argtypes = [i32, p, i64, i64, p, i32, p]
     L.qblk_gemv.argtypes = [i32, p, i64, i64, p, i32, p, p]
+    L.qblk_gemv_batch.argtypes = [i32, i64, i32, p, i32, p]
     L.qblk_gemm.argtypes = [i32, p, i64, i64, p, i32, i64, p, p]
     for f in ("qblk_quantize_q4_0", "qblk_quantize_q4_0_ref", "qblk_quantize_sb4", "qblk_quantize_q4_k",
               "qblk_quantize_w4g128", "qblk_quantize_act_i8", "qblk_dequant", "qblk_gemv", "qblk_gemm",
@@ -233,6 +234,44 @@ def gemv(blocks, fmt, m, k, x, out=None, stream=None):
     _check(_lib.qblk_gemv(fmt, _ptr(blocks), m, k, _ptr(x), _dtype(x), _ptr(out), _stream(stream)),
            "qblk_gemv")
     return out
+
+
+class _GemvItem(C.Structure):
+    """qblk_gemv_item_t"""
+    _fields_ = [("blocks", C.c_void_p), ("m", C.c_int64), ("x", C.c_void_p), ("y", C.c_void_p)]
+
+
+GEMV_BATCH_MAX = 32
+
+
+def gemv_batch(fmt, k, products, outs=None, stream=None):
+    """Several batch-1 products of equal k and x type in one call:
+    products = [(blocks, m, x), ...]; returns [y, ...] (fp32, m each)."""
+    _need_dims(k=k)
+    if len(products) > GEMV_BATCH_MAX:
+        raise ValueError(f"at most {GEMV_BATCH_MAX} products per call, got {len(products)}")
+    if outs is not None and len(outs) != len(products):
+        raise ValueError("outs: one output per product")
+    items = (_GemvItem * max(1, len(products)))()
+    ys, dev, xt = [], None, None
+    for i, (blocks, m, x) in enumerate(products):
+        _need_dims(m=m)
+        dev = _need(x, f"x[{i}]", _FLOAT_IN, numel=k, device=dev)
+        if xt is None:
+            xt = x.dtype
+        elif x.dtype != xt:
+            raise TypeError(f"x[{i}]: element type {x.dtype}, the batch's first is {xt}")
+        _need(blocks, f"blocks[{i}]", (torch.uint8,), min_numel=_packed(fmt, m, k), device=dev)
+        y = outs[i] if outs is not None else torch.empty(m, dtype=torch.float32, device=x.device)
+        _need(y, f"out[{i}]", (torch.float32,), min_numel=m, device=dev)
+        items[i] = _GemvItem(_ptr(blocks).value, m, _ptr(x).value, _ptr(y).value)
+        ys.append(y)
+    if not products:
+        return ys
+    _need_current(dev)
+    _check(_lib.qblk_gemv_batch(fmt, k, _DT[xt], C.cast(items, C.c_void_p), len(products), _stream(stream)),
+           "qblk_gemv_batch")
+    return ys
 
 
 def gemm(blocks, fmt, m, k, X, out=None, stream=None):

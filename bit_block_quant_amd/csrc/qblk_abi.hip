@@ -249,6 +249,34 @@ qblk_status_t qblk_gemv(qblk_format_t fmt, const void* blocks, int64_t m, int64_
   return from_hip(qblk::launch_gemv(fmt, blocks, m, k, x, xt, y, s));
 }
 
+qblk_status_t qblk_gemv_batch(qblk_format_t fmt, int64_t k, qblk_dtype_t xt,
+                              const qblk_gemv_item_t* items, int count, qblk_stream_t stream) {
+  if (count < 0 || count > QBLK_GEMV_BATCH_MAX) return QBLK_ERR_SHAPE;
+  if (count > 0 && items == nullptr) return QBLK_ERR_NULL;
+  if (!dtype_ok(xt)) return QBLK_ERR_DTYPE;
+  for (int i = 0; i < count; i++) {
+    const qblk_gemv_item_t& it = items[i];
+    QBLK_TRY(check_shape(fmt, it.m, k));
+    QBLK_TRY(check_ptr(it.blocks, it.m > 0 && k > 0));
+    QBLK_TRY(check_ptr(it.x, it.m > 0 && k > 0));
+    QBLK_TRY(check_ptr(it.y, it.m > 0));
+  }
+  if (fmt == QBLK_W4G128) return QBLK_ERR_UNSUPPORTED;  // its product is qblk_gemm_w4a8
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (k == 0) {
+    for (int i = 0; i < count; i++)
+      if (items[i].m > 0) QBLK_TRY(from_hip(qblk::launch_fill_zero(items[i].y, items[i].m, s)));
+    return QBLK_OK;
+  }
+  // the items that have rows, in order
+  qblk_gemv_item_t live[QBLK_GEMV_BATCH_MAX];
+  int n = 0;
+  for (int i = 0; i < count; i++)
+    if (items[i].m > 0) live[n++] = items[i];
+  if (n == 0) return QBLK_OK;
+  return from_hip(qblk::launch_gemv_batch(fmt, k, xt, live, n, s));
+}
+
 qblk_status_t qblk_gemm(qblk_format_t fmt, const void* blocks, int64_t m, int64_t k,
                         const void* x, qblk_dtype_t xt, int64_t n, float* y,
                         qblk_stream_t stream) {

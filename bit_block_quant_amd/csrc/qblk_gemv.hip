@@ -337,11 +337,10 @@ struct UnitAddr {
 // against 6.61 -- 8.44 us even with every piece of x requested, behind one
 // barrier, before any weight request of the workgroup: x is then fetched
 // while every CU's weight requests are in flight, and arrives late.)
-template <int FMT, int RMAX, int UPL, int KS, int WAVES = kWavesH, int XL = 0>
-__global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restrict__ blocks,
-                                                      const uint16_t* __restrict__ x,
-                                                      float* __restrict__ y, int M, int K,
-                                                      int rows_per_wg) {
+// The kernel's body; wg is the workgroup's index among those of its matrix.
+template <int FMT, int RMAX, int UPL, int KS, int WAVES, int XL>
+__device__ __forceinline__ void gemv_h_body(const uint8_t* __restrict__ blocks, const uint16_t* __restrict__ x,
+                                            float* __restrict__ y, int M, int K, int rows_per_wg, unsigned wg) {
   constexpr bool AFFINE = affine_fmt(FMT);
   constexpr bool QK = FMT == QBLK_Q4_K;
   constexpr int E = Fmt<FMT>::E, B = Fmt<FMT>::B;
@@ -351,7 +350,7 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restr
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int slot = wave / KS, part = wave % KS;
-  const int row0 = blockIdx.x * rows_per_wg;
+  const int row0 = wg * rows_per_wg;
   const int row_end = min(M, row0 + rows_per_wg);
   // (KS > 1 or XL: every wave meets the barrier)
   if (KS == 1 && !XL && row0 + slot >= row_end) return;
@@ -644,6 +643,34 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restr
   }
 }
 
+template <int FMT, int RMAX, int UPL, int KS, int WAVES = kWavesH, int XL = 0>
+__global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restrict__ blocks,
+                                                      const uint16_t* __restrict__ x,
+                                                      float* __restrict__ y, int M, int K,
+                                                      int rows_per_wg) {
+  gemv_h_body<FMT, RMAX, UPL, KS, WAVES, XL>(blocks, x, y, M, K, rows_per_wg, blockIdx.x);
+}
+
+// Several matrices of equal k in one grid: matrix i takes workgroups
+// [wg_end[i-1], wg_end[i]) (kernel arguments, read with scalar loads).
+struct GemvBatch {
+  const uint8_t* blocks[QBLK_GEMV_BATCH_MAX];
+  const uint16_t* x[QBLK_GEMV_BATCH_MAX];
+  float* y[QBLK_GEMV_BATCH_MAX];
+  int m[QBLK_GEMV_BATCH_MAX];
+  unsigned wg_end[QBLK_GEMV_BATCH_MAX];
+  int count;
+};
+
+template <int FMT, int RMAX, int UPL, int KS, int WAVES = kWavesH, int XL = 0>
+__global__ __launch_bounds__(WAVES * kWave) void k_gemv_hb(const GemvBatch b, int K, int rows_per_wg) {
+  const unsigned w = blockIdx.x;
+  int i = 0;
+  while (i + 1 < b.count && w >= b.wg_end[i]) i++;
+  const unsigned first = i > 0 ? b.wg_end[i - 1] : 0u;
+  gemv_h_body<FMT, RMAX, UPL, KS, WAVES, XL>(b.blocks[i], b.x[i], b.y[i], b.m[i], K, rows_per_wg, w - first);
+}
+
 // y[0, n) = 0: 16-byte stores (y is 16-byte aligned), a scalar tail.
 __global__ __launch_bounds__(256) void k_fill_zero(float* y, int64_t n) {
   const int64_t n4 = n >> 2;
@@ -687,16 +714,48 @@ hipError_t launch_t(const void* blocks, int64_t m, int64_t k, const void* x, flo
   return launch_tr<FMT, XT, kRows>(blocks, m, k, x, y, s);
 }
 
+// What one launch of the fp16-x kernel multiplies: one matrix (items ==
+// nullptr), or a batch of matrices of equal k.  m sets the tiling: the
+// matrix's rows, or the batch's rows together.
+struct GemvJob {
+  const void* blocks;
+  const void* x;
+  float* y;
+  int64_t m;
+  const qblk_gemv_item_t* items;
+  int count;
+};
+
 template <int FMT, int RMAX, int UPL, int KS, int WAVES, int XL = 0>
-hipError_t launch_h_t(const void* blocks, int64_t m, int64_t k, const void* x, float* y,
-                      int rows_per_wg, hipStream_t s) {
-  const unsigned grid = static_cast<unsigned>((m + rows_per_wg - 1) / rows_per_wg);
+hipError_t launch_h_t(const GemvJob& j, int64_t k, int rows_per_wg, hipStream_t s) {
+  if (j.items == nullptr) {
+    const unsigned grid = static_cast<unsigned>((j.m + rows_per_wg - 1) / rows_per_wg);
+    if (log_enabled())
+      log_launch("gemv k_gemv_h fmt=%d row-slots/wave=%d units/lane=%d waves/row=%d waves=%d x-lds=%d m=%lld "
+                 "k=%lld rows/wg=%d grid=%u", FMT, RMAX, UPL, KS, WAVES, XL, (long long)j.m, (long long)k,
+                 rows_per_wg, grid);
+    hipLaunchKernelGGL((k_gemv_h<FMT, RMAX, UPL, KS, WAVES, XL>), dim3(grid), dim3(WAVES * kWave), 0, s,
+                       static_cast<const uint8_t*>(j.blocks), static_cast<const uint16_t*>(j.x), j.y,
+                       static_cast<int>(j.m), static_cast<int>(k), rows_per_wg);
+    return hipGetLastError();
+  }
+  GemvBatch b;
+  unsigned grid = 0;
+  for (int i = 0; i < j.count; i++) {
+    b.blocks[i] = static_cast<const uint8_t*>(j.items[i].blocks);
+    b.x[i] = static_cast<const uint16_t*>(j.items[i].x);
+    b.y[i] = j.items[i].y;
+    b.m[i] = static_cast<int>(j.items[i].m);
+    grid += static_cast<unsigned>((j.items[i].m + rows_per_wg - 1) / rows_per_wg);
+    b.wg_end[i] = grid;
+  }
+  b.count = j.count;
   if (log_enabled())
-    log_launch("gemv k_gemv_h fmt=%d row-slots/wave=%d units/lane=%d waves/row=%d waves=%d x-lds=%d m=%lld k=%lld "
-               "rows/wg=%d grid=%u", FMT, RMAX, UPL, KS, WAVES, XL, (long long)m, (long long)k, rows_per_wg, grid);
-  hipLaunchKernelGGL((k_gemv_h<FMT, RMAX, UPL, KS, WAVES, XL>), dim3(grid), dim3(WAVES * kWave), 0, s,
-                     static_cast<const uint8_t*>(blocks), static_cast<const uint16_t*>(x), y,
-                     static_cast<int>(m), static_cast<int>(k), rows_per_wg);
+    log_launch("gemv k_gemv_hb fmt=%d row-slots/wave=%d units/lane=%d waves/row=%d waves=%d x-lds=%d matrices=%d "
+               "rows=%lld k=%lld rows/wg=%d grid=%u", FMT, RMAX, UPL, KS, WAVES, XL, j.count, (long long)j.m,
+               (long long)k, rows_per_wg, grid);
+  hipLaunchKernelGGL((k_gemv_hb<FMT, RMAX, UPL, KS, WAVES, XL>), dim3(grid), dim3(WAVES * kWave), 0, s, b,
+                     static_cast<int>(k), rows_per_wg);
   return hipGetLastError();
 }
 
@@ -711,19 +770,18 @@ inline int rows_per_wg(int64_t m, int slots, int rmax_cap) {
 
 // Row slots per wave: the smallest template count R >= rmax, up to RCAP.
 template <int FMT, int UPL, int KS, int RCAP, int WAVES, int XL, int R = 1>
-hipError_t launch_h_r(int rmax, const void* blocks, int64_t m, int64_t k, const void* x, float* y,
-                      int rpw, hipStream_t s) {
+hipError_t launch_h_r(int rmax, const GemvJob& j, int64_t k, int rpw, hipStream_t s) {
   if constexpr (R < RCAP) {
-    if (rmax > R) return launch_h_r<FMT, UPL, KS, RCAP, WAVES, XL, R + 1>(rmax, blocks, m, k, x, y, rpw, s);
+    if (rmax > R) return launch_h_r<FMT, UPL, KS, RCAP, WAVES, XL, R + 1>(rmax, j, k, rpw, s);
   }
-  return launch_h_t<FMT, R, UPL, KS, WAVES, XL>(blocks, m, k, x, y, rpw, s);
+  return launch_h_t<FMT, R, UPL, KS, WAVES, XL>(j, k, rpw, s);
 }
 
 template <int FMT, int UPL, int KS, int RCAP, int WAVES = kWavesH, int XL = 0>
-hipError_t launch_h_k(const void* blocks, int64_t m, int64_t k, const void* x, float* y, hipStream_t s) {
+hipError_t launch_h_k(const GemvJob& j, int64_t k, hipStream_t s) {
   constexpr int slots = WAVES / KS;
-  const int rpw = rows_per_wg(m, slots, RCAP);
-  return launch_h_r<FMT, UPL, KS, RCAP, WAVES, XL>((rpw + slots - 1) / slots, blocks, m, k, x, y, rpw, s);
+  const int rpw = rows_per_wg(j.m, slots, RCAP);
+  return launch_h_r<FMT, UPL, KS, RCAP, WAVES, XL>((rpw + slots - 1) / slots, j, k, rpw, s);
 }
 
 // fp16 x and at most 384 units (12288 weights) per row: the up-front kernel.
@@ -754,24 +812,24 @@ hipError_t launch_h_k(const void* blocks, int64_t m, int64_t k, const void* x, f
 // the barrier after the weight loads (staging before them: 4.00 -> 4.09 and
 // 7.71 -> 7.99 us).
 template <int FMT>
-bool launch_h(const void* blocks, int64_t m, int64_t k, const void* x, float* y, hipStream_t s,
-              hipError_t* err) {
+bool launch_h(const GemvJob& j, int64_t k, hipStream_t s, hipError_t* err) {
   const int64_t S = k / 32;
   if (S > 6 * 64) return false;
+  const int64_t m = j.m;
   const int64_t per_cu = (m + cu_count() - 1) / cu_count();
   constexpr bool kSigned = FMT == QBLK_SB4 || FMT == QBLK_Q4_0;
   const bool few = per_cu <= kWavesH;  // one row per wave at most
-  if (S <= 64) *err = launch_h_k<FMT, 1, 1, 3>(blocks, m, k, x, y, s);
+  if (S <= 64) *err = launch_h_k<FMT, 1, 1, 3>(j, k, s);
   else if (S <= 128 && FMT == QBLK_Q4_0 && few)
-    *err = launch_h_t<FMT, 1, 2, 1, kWavesH, 1>(blocks, m, k, x, y, rows_per_wg(m, kWavesH, 1), s);
+    *err = launch_h_t<FMT, 1, 2, 1, kWavesH, 1>(j, k, rows_per_wg(m, kWavesH, 1), s);
   else if (S > 256 && FMT == QBLK_SB4_AFFINE && few)
-    *err = launch_h_t<FMT, 1, 6, 1, kWavesH, 1>(blocks, m, k, x, y, rows_per_wg(m, kWavesH, 1), s);
-  else if (S <= 128 && kSigned && per_cu > 32) *err = launch_h_k<FMT, 2, 1, 3, kWavesH, 2>(blocks, m, k, x, y, s);
-  else if (S <= 128) *err = launch_h_k<FMT, 1, 2, 6>(blocks, m, k, x, y, s);
-  else if (S <= 256) *err = launch_h_k<FMT, 2, 2, 3>(blocks, m, k, x, y, s);
-  else if (FMT == QBLK_SB4 && few) *err = launch_h_k<FMT, 3, 2, 2, kWavesH, 2>(blocks, m, k, x, y, s);
-  else if (FMT == QBLK_SB4) *err = launch_h_k<FMT, 3, 2, 3, 12>(blocks, m, k, x, y, s);
-  else *err = launch_h_k<FMT, 3, 2, 2>(blocks, m, k, x, y, s);
+    *err = launch_h_t<FMT, 1, 6, 1, kWavesH, 1>(j, k, rows_per_wg(m, kWavesH, 1), s);
+  else if (S <= 128 && kSigned && per_cu > 32) *err = launch_h_k<FMT, 2, 1, 3, kWavesH, 2>(j, k, s);
+  else if (S <= 128) *err = launch_h_k<FMT, 1, 2, 6>(j, k, s);
+  else if (S <= 256) *err = launch_h_k<FMT, 2, 2, 3>(j, k, s);
+  else if (FMT == QBLK_SB4 && few) *err = launch_h_k<FMT, 3, 2, 2, kWavesH, 2>(j, k, s);
+  else if (FMT == QBLK_SB4) *err = launch_h_k<FMT, 3, 2, 3, 12>(j, k, s);
+  else *err = launch_h_k<FMT, 3, 2, 2>(j, k, s);
   return true;
 }
 
@@ -779,13 +837,36 @@ template <int FMT>
 hipError_t launch_fmt(const void* blocks, int64_t m, int64_t k, const void* x, int xt, float* y,
                       hipStream_t s) {
   hipError_t err = hipSuccess;
-  if (xt == QBLK_F16 && launch_h<FMT>(blocks, m, k, x, y, s, &err)) return err;
+  if (xt == QBLK_F16 && launch_h<FMT>(GemvJob{blocks, x, y, m, nullptr, 0}, k, s, &err)) return err;
   if (xt == QBLK_F16) return launch_t<FMT, QBLK_F16>(blocks, m, k, x, y, s);
   if (xt == QBLK_F32) return launch_t<FMT, QBLK_F32>(blocks, m, k, x, y, s);
   return launch_t<FMT, QBLK_BF16>(blocks, m, k, x, y, s);
 }
 
 }  // namespace
+
+namespace {
+template <int FMT>
+hipError_t launch_batch_fmt(int64_t k, int xt, const qblk_gemv_item_t* items, int count, hipStream_t s) {
+  int64_t rows = 0;
+  for (int i = 0; i < count; i++) rows += items[i].m;
+  hipError_t err = hipSuccess;
+  if (xt == QBLK_F16 && launch_h<FMT>(GemvJob{nullptr, nullptr, nullptr, rows, items, count}, k, s, &err))
+    return err;
+  // other x types, or rows past 12288 weights: one launch per matrix
+  for (int i = 0; i < count && err == hipSuccess; i++)
+    err = launch_fmt<FMT>(items[i].blocks, items[i].m, k, items[i].x, xt, items[i].y, s);
+  return err;
+}
+}  // namespace
+
+hipError_t launch_gemv_batch(int fmt, int64_t k, int xt, const qblk_gemv_item_t* items, int count,
+                             hipStream_t s) {
+  if (fmt == QBLK_Q4_0) return launch_batch_fmt<QBLK_Q4_0>(k, xt, items, count, s);
+  if (fmt == QBLK_SB4) return launch_batch_fmt<QBLK_SB4>(k, xt, items, count, s);
+  if (fmt == QBLK_Q4_K) return launch_batch_fmt<QBLK_Q4_K>(k, xt, items, count, s);
+  return launch_batch_fmt<QBLK_SB4_AFFINE>(k, xt, items, count, s);
+}
 
 hipError_t launch_gemv(int fmt, const void* blocks, int64_t m, int64_t k, const void* x, int xt,
                        float* y, hipStream_t s) {

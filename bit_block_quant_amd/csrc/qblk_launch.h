@@ -28,6 +28,9 @@ hipError_t launch_dequant(int fmt, const void* blocks, int64_t rows, int64_t k, 
                           hipStream_t s);
 hipError_t launch_gemv(int fmt, const void* blocks, int64_t m, int64_t k, const void* x, int xt,
                        float* y, hipStream_t s);
+// items: 1..QBLK_GEMV_BATCH_MAX products with m > 0, validated
+hipError_t launch_gemv_batch(int fmt, int64_t k, int xt, const qblk_gemv_item_t* items, int count,
+                             hipStream_t s);
 hipError_t launch_gemm(int fmt, const void* blocks, int64_t m, int64_t k, const void* x, int xt,
                        int64_t n, float* y, hipStream_t s);
 hipError_t launch_fill_zero(float* y, int64_t n, hipStream_t s);

@@ -123,6 +123,18 @@ typedef enum {
 
 typedef void* qblk_stream_t; /* hipStream_t */
 
+/* One product of qblk_gemv_batch: y (m fp32) = W x with W (m x k) in blocks
+ * and x (k elements); device pointers owned by the caller. */
+typedef struct {
+  const void* blocks;
+  int64_t m;
+  const void* x;
+  float* y;
+} qblk_gemv_item_t;
+
+/* Most products one qblk_gemv_batch call takes. */
+#define QBLK_GEMV_BATCH_MAX 32
+
 /* Geometry.  qblk_block_bytes/elems return 0 for an unknown format;
  * qblk_packed_bytes returns 0 if k is not a multiple of the block size or a
  * size is negative. */
@@ -209,6 +221,18 @@ qblk_status_t qblk_dequant(qblk_format_t fmt, const void* blocks, int64_t rows,
 qblk_status_t qblk_gemv(qblk_format_t fmt, const void* blocks, int64_t m,
                         int64_t k, const void* x, qblk_dtype_t xt, float* y,
                         qblk_stream_t stream);
+
+/* Several batch-1 products that share the format, k and the type of x, in
+ * one launch: items[i].y = W_i x_i for i < count (count <= 32, the items
+ * read during the call only).  Each product is the one qblk_gemv computes,
+ * with the same bound; a layer's matrices of equal k (a transformer's q, k, v
+ * and o projections, or gate and up) then share one grid instead of paying a
+ * kernel boundary each.  Items with m = 0 are skipped; argument errors in any
+ * item are returned before any launch.  fp16 x with k <= 12288 runs as one
+ * launch; other x types or longer rows run one launch per item. */
+qblk_status_t qblk_gemv_batch(qblk_format_t fmt, int64_t k, qblk_dtype_t xt,
+                              const qblk_gemv_item_t* items, int count,
+                              qblk_stream_t stream);
 
 /* Small-batch product Y = X W^T: X is n x k row-major (token-major) of type xt,
  * Y is n x m row-major fp32.  All four formats run on the bf16 matrix cores

@@ -76,6 +76,12 @@ hipError_t launch_gemm_w4a8(const void* blocks, int64_t m, int64_t k, const int8
   rec("gemm_w4a8", blocks, m, k, n, QBLK_W4G128, -1);
   return g_ret;
 }
+hipError_t launch_gemv_batch(int fmt, int64_t k, int xt, const qblk_gemv_item_t* items, int count, hipStream_t) {
+  int64_t rows = 0;
+  for (int i = 0; i < count; i++) rows += items[i].m;  // reads every item it is given
+  rec("gemv_batch", items[0].blocks, rows, k, count, fmt, xt);
+  return g_ret;
+}
 hipError_t launch_dequant(int fmt, const void* blocks, int64_t rows, int64_t k, void*, int ot, hipStream_t) {
   rec("dequant", blocks, rows, k, -1, fmt, ot);
   return g_ret;
@@ -206,6 +212,35 @@ int main() {
   EXPECT(g_call.a == 5 && g_call.p0 == Y);
   LAUNCHES(qblk_gemv(QBLK_Q4_K, A, 7, 512, B, QBLK_F32, Y, s), "gemv");
   EXPECT(g_call.fmt == QBLK_Q4_K && g_call.a == 7 && g_call.b == 512 && g_call.type == QBLK_F32);
+
+  // GEMV batches: at most QBLK_GEMV_BATCH_MAX items, each checked before any
+  // launch, items with m = 0 dropped
+  {
+    qblk_gemv_item_t it[QBLK_GEMV_BATCH_MAX + 1];
+    for (auto& e : it) e = qblk_gemv_item_t{A, 4, B, Y};
+    REJECTS(qblk_gemv_batch(QBLK_SB4, 256, QBLK_F16, it, -1, s), QBLK_ERR_SHAPE);
+    REJECTS(qblk_gemv_batch(QBLK_SB4, 256, QBLK_F16, it, QBLK_GEMV_BATCH_MAX + 1, s), QBLK_ERR_SHAPE);
+    REJECTS(qblk_gemv_batch(QBLK_SB4, 256, QBLK_F16, nullptr, 2, s), QBLK_ERR_NULL);
+    REJECTS(qblk_gemv_batch(QBLK_SB4, 256, QBLK_F16, nullptr, 0, s), QBLK_OK);
+    REJECTS(qblk_gemv_batch(QBLK_SB4, 256, static_cast<qblk_dtype_t>(9), it, 2, s), QBLK_ERR_DTYPE);
+    REJECTS(qblk_gemv_batch(QBLK_W4G128, 256, QBLK_F16, it, 2, s), QBLK_ERR_UNSUPPORTED);
+    REJECTS(qblk_gemv_batch(QBLK_SB4, 100, QBLK_F16, it, 2, s), QBLK_ERR_SHAPE);
+    it[2].x = MIS;  // a bad item anywhere stops the whole call
+    REJECTS(qblk_gemv_batch(QBLK_SB4, 256, QBLK_F16, it, 3, s), QBLK_ERR_ALIGN);
+    it[2].x = B;
+    it[2].y = nullptr;
+    REJECTS(qblk_gemv_batch(QBLK_SB4, 256, QBLK_F16, it, 3, s), QBLK_ERR_NULL);
+    it[2].y = Y;
+    it[1].m = -3;
+    REJECTS(qblk_gemv_batch(QBLK_SB4, 256, QBLK_F16, it, 3, s), QBLK_ERR_SHAPE);
+    it[1] = qblk_gemv_item_t{nullptr, 0, nullptr, nullptr};
+    LAUNCHES(qblk_gemv_batch(QBLK_SB4, 256, QBLK_F16, it, 3, s), "gemv_batch");
+    EXPECT(g_call.a == 8 && g_call.b == 256 && g_call.c == 2 && g_call.p0 == A && g_call.type == QBLK_F16);
+    LAUNCHES(qblk_gemv_batch(QBLK_SB4, 0, QBLK_F16, it, 2, s), "fill_zero");  // the m = 0 item has nothing to fill
+    EXPECT(g_call.a == 4 && g_call.p0 == Y);
+    LAUNCHES(qblk_gemv_batch(QBLK_Q4_K, 512, QBLK_F32, it + 2, QBLK_GEMV_BATCH_MAX - 1, s), "gemv_batch");
+    EXPECT(g_call.c == QBLK_GEMV_BATCH_MAX - 1 && g_call.a == 4 * (QBLK_GEMV_BATCH_MAX - 1));
+  }
 
   // GEMM: bf16 activations and k a multiple of 256 only; k = 0 zero-fills m * n
   REJECTS(qblk_gemm(QBLK_SB4, A, 4, 256, B, QBLK_F16, 2, Y, s), QBLK_ERR_UNSUPPORTED);

@@ -272,6 +272,46 @@ def test_gemv_tolerance(q, fmt, xt, shape):
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: NAMES[f])
+@pytest.mark.parametrize("k", [2304, 4096, 11008, 13056])
+@pytest.mark.parametrize("xt", ["f16", "f32"])
+def test_gemv_batch(q, fmt, k, xt):
+    # several products in one call: ragged row counts (one empty), each its
+    # own x; fp16 x up to 12288 weights per row shares one grid, the rest runs
+    # per matrix -- every y against the oracle's product of its own matrix
+    ms = [37, 4096, 0, 1000, 300]
+    rng = np.random.default_rng(60 + k)
+    cases = []
+    for i, m in enumerate(ms):
+        blocks = O.quantize(fmt, mixed_blocks(m, k, 61 + i)) if m else np.zeros(16, np.uint8)
+        x = rng.standard_normal(k).astype(np.float16 if xt == "f16" else np.float32)
+        cases.append((blocks, m, x))
+    ys = q.gemv_batch(fmt, k, [(dev(b), m, dev(x)) for b, m, x in cases])
+    for (blocks, m, x), y in zip(cases, ys):
+        y = host(y)
+        assert y.shape == (m,)
+        if m:
+            y_ref, bound = O.gemv(fmt, blocks, m, k, x.astype(np.float64))
+            check_products(y, y_ref, bound, f"batch {NAMES[fmt]} {m}x{k} {xt}")
+
+
+def test_gemv_batch_matches_single_calls(q):
+    # the headline shape inside a batch: each y agrees with the single call
+    # (the batch's tiling follows its total rows, so the summation order may
+    # differ: compared to 1e-4 of the largest output)
+    k = 4096
+    mats = [(11008, 70), (4096, 71), (4096, 72), (33, 73)]
+    prods, singles = [], []
+    for m, seed in mats:
+        b = dev(O.quantize(O.SB4, mixed_blocks(m, k, seed)))
+        x = dev(np.random.default_rng(seed).standard_normal(k).astype(np.float16))
+        prods.append((b, m, x))
+    ys = q.gemv_batch(O.SB4, k, prods)
+    for (b, m, x), y in zip(prods, ys):
+        y1 = host(q.gemv(b, O.SB4, m, k, x))
+        assert np.allclose(host(y), y1, rtol=0, atol=1e-4 * max(1e-30, float(np.max(np.abs(y1)))))
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: NAMES[f])
 @pytest.mark.parametrize("xt", ["f32", "f16"])
 def test_gemv_unit_vector_is_a_column(q, fmt, xt):
     m, k = 70, 2048

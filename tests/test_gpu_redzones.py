@@ -115,6 +115,25 @@ def test_gemv_margins(q, fmt, m, k, xt):
 
 
 @pytest.mark.parametrize("fmt", [Q4_0, SB4, SB4_AFFINE, Q4_K])
+@pytest.mark.parametrize("k,xt", [(4096, torch.float16), (11008, torch.float16), (2304, torch.float32)],
+                         ids=["4096-f16", "11008-f16", "2304-f32"])
+def test_gemv_batch_margins(q, fmt, k, xt):
+    ms = [300, 37, 4096, 1]
+    prods, refs, pads = [], [], []
+    for i, m in enumerate(ms):
+        blocks = q.quantize(weights(m, k, 209 + i), fmt)
+        x = torch.from_numpy(WL.normal((k,), 1.0, 213 + i)).cuda().to(xt)
+        refs.append(q.gemv(blocks, fmt, m, k, x))
+        pb, px, py = padded_like(blocks), padded_like(x), Padded((m,), torch.float32)
+        pads += [pb, px, py]
+        prods.append((pb.t, m, px.t))
+    q.gemv_batch(fmt, k, prods, outs=[p.t for p in pads[2::3]])
+    assert all(p.margins_intact() for p in pads)
+    for py, ref in zip(pads[2::3], refs):
+        assert same(py.t, ref, exact=False)
+
+
+@pytest.mark.parametrize("fmt", [Q4_0, SB4, SB4_AFFINE, Q4_K])
 @pytest.mark.parametrize("m,k,n", [(150, 2304, 1), (150, 2304, 16), (150, 2304, 40), (150, 2304, 100),
                                    (150, 2304, 200), (40, 14336, 130), (2000, 1024, 300)])
 def test_gemm_margins(q, fmt, m, k, n):
