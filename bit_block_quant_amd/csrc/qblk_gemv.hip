@@ -652,7 +652,8 @@ __global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restr
 }
 
 // Several matrices of equal k in one grid: matrix i takes workgroups
-// [wg_end[i-1], wg_end[i]) (kernel arguments, read with scalar loads).
+// [wg_end[i-1], wg_end[i]) (kernel arguments, 1 KB at most, read with scalar
+// loads).
 struct GemvBatch {
   const uint8_t* blocks[QBLK_GEMV_BATCH_MAX];
   const uint16_t* x[QBLK_GEMV_BATCH_MAX];
