@@ -294,6 +294,26 @@ def test_gemv_batch(q, fmt, k, xt):
             check_products(y, y_ref, bound, f"batch {NAMES[fmt]} {m}x{k} {xt}")
 
 
+def test_gemv_batch_full(q):
+    # the most products one call takes, row counts 1..~300 (the workgroup
+    # ranges of 32 matrices in one grid, several matrices per workgroup round)
+    k = 2304
+    rng = np.random.default_rng(80)
+    prods, cases = [], []
+    for i in range(q.GEMV_BATCH_MAX):
+        m = int(rng.integers(1, 300)) if i % 5 else 1
+        blocks = O.quantize(O.SB4, mixed_blocks(m, k, 81 + i))
+        x = rng.standard_normal(k).astype(np.float16)
+        cases.append((blocks, m, x))
+        prods.append((dev(blocks), m, dev(x)))
+    ys = q.gemv_batch(O.SB4, k, prods)
+    for (blocks, m, x), y in zip(cases, ys):
+        y_ref, bound = O.gemv(O.SB4, blocks, m, k, x.astype(np.float64))
+        check_products(host(y), y_ref, bound, f"full batch m={m}")
+    with pytest.raises(ValueError):
+        q.gemv_batch(O.SB4, k, prods + prods[:1])
+
+
 def test_gemv_batch_matches_single_calls(q):
     # the headline shape inside a batch: each y agrees with the single call
     # (the batch's tiling follows its total rows, so the summation order may
