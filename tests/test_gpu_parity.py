@@ -747,6 +747,55 @@ def test_gemm_w4a8_deterministic(q, m, k, n):
     check_products(runs[0], Y_ref, B, f"deterministic gemm_w4a8 n={n}")
 
 
+def test_threads_on_their_own_streams(q):
+    # the C ABI keeps no per-call state: four host threads, each calling every
+    # product on a stream of its own at the same time (ctypes releases the
+    # interpreter lock during each call), get the bytes and products that the
+    # calls give one at a time
+    import threading
+    m, k = 300, 4096
+    w = mixed_blocks(m, k, 55)
+    wd = dev(w)
+    xs = [dev(np.random.default_rng(56 + t).standard_normal(k).astype(np.float16)) for t in range(4)]
+    Xs = [dev_bf16(WL.bf16_bits(np.random.default_rng(60 + t).standard_normal((24, k)).astype(np.float32)))
+          for t in range(4)]
+    # expected results, one call at a time
+    b_ref = q.quantize(wd, q.SB4)
+    want = [(host(q.gemv(b_ref, q.SB4, m, k, xs[t])), host(q.gemm(b_ref, q.SB4, m, k, Xs[t]))) for t in range(4)]
+    b_ref = host(b_ref)
+    got, errors = [None] * 4, []
+
+    def work(t):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                out = []
+                for _ in range(10):
+                    b = q.quantize(wd, q.SB4, stream=st)
+                    y = q.gemv(b, q.SB4, m, k, xs[t], stream=st)
+                    (yb,) = q.gemv_batch(q.SB4, k, [(b, m, xs[t])], stream=st)
+                    Y = q.gemm(b, q.SB4, m, k, Xs[t], stream=st)
+                    out.append((b, y, yb, Y))
+            st.synchronize()
+            got[t] = [(host(b), host(y), host(yb), host(Y)) for b, y, yb, Y in out]
+        except Exception as e:  # reported below, in the test's own thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(120)
+    assert not errors, errors
+    for t in range(4):
+        y_want, Y_want = want[t]
+        for b, y, yb, Y in got[t]:
+            assert np.array_equal(b, b_ref)
+            assert np.array_equal(y.view(np.uint32), y_want.view(np.uint32))
+            assert np.allclose(yb, y_want, rtol=0, atol=1e-4 * float(np.max(np.abs(y_want))))
+            assert np.allclose(Y, Y_want, rtol=0, atol=1e-4 * float(np.max(np.abs(Y_want))))
+
+
 def test_side_stream(q):
     # every step enqueues on the stream it is handed: the same calls on a
     # second stream give the oracle's bytes and products
