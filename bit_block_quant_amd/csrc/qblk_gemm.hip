@@ -30,9 +30,10 @@
 // load issued up front, K split over the grid), up to 64 tokens k_gemm_s (the
 // same stages walked over the whole K range, the next stage's loads in flight
 // while the current one is multiplied), beyond that k_gemm_w (32x32x16
-// matrix ops, 128 rows x 128 tokens per workgroup).  When a K range is split
-// over a third grid dimension the partial products are added into Y (zeroed
-// first).
+// matrix ops, 128 rows x 128 tokens per workgroup; Type 1 and Q4_K 128 x 64
+// when that fills the GPU better).  When a K range is split over a third
+// grid dimension the partial products are added into Y (zeroed first); with
+// reproducible products on (qblk_set_deterministic) nothing is split.
 #include "qblk_device.h"
 #include "qblk_launch.h"
 
