@@ -251,9 +251,12 @@ qblk_status_t qblk_gemv(qblk_format_t fmt, const void* blocks, int64_t m, int64_
 
 qblk_status_t qblk_gemv_batch(qblk_format_t fmt, int64_t k, qblk_dtype_t xt,
                               const qblk_gemv_item_t* items, int count, qblk_stream_t stream) {
+  // the checks of qblk_gemv, in its order, then every item's
+  QBLK_TRY(check_shape(fmt, 0, k));
+  if (!dtype_ok(xt)) return QBLK_ERR_DTYPE;
+  if (fmt == QBLK_W4G128) return QBLK_ERR_UNSUPPORTED;  // its product is qblk_gemm_w4a8
   if (count < 0 || count > QBLK_GEMV_BATCH_MAX) return QBLK_ERR_SHAPE;
   if (count > 0 && items == nullptr) return QBLK_ERR_NULL;
-  if (!dtype_ok(xt)) return QBLK_ERR_DTYPE;
   for (int i = 0; i < count; i++) {
     const qblk_gemv_item_t& it = items[i];
     QBLK_TRY(check_shape(fmt, it.m, k));
@@ -261,7 +264,6 @@ qblk_status_t qblk_gemv_batch(qblk_format_t fmt, int64_t k, qblk_dtype_t xt,
     QBLK_TRY(check_ptr(it.x, it.m > 0 && k > 0));
     QBLK_TRY(check_ptr(it.y, it.m > 0));
   }
-  if (fmt == QBLK_W4G128) return QBLK_ERR_UNSUPPORTED;  // its product is qblk_gemm_w4a8
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (k == 0) {
     for (int i = 0; i < count; i++)

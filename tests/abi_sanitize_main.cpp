@@ -225,6 +225,8 @@ int main() {
     REJECTS(qblk_gemv_batch(QBLK_SB4, 256, static_cast<qblk_dtype_t>(9), it, 2, s), QBLK_ERR_DTYPE);
     REJECTS(qblk_gemv_batch(QBLK_W4G128, 256, QBLK_F16, it, 2, s), QBLK_ERR_UNSUPPORTED);
     REJECTS(qblk_gemv_batch(QBLK_SB4, 100, QBLK_F16, it, 2, s), QBLK_ERR_SHAPE);
+    REJECTS(qblk_gemv_batch(static_cast<qblk_format_t>(9), 256, QBLK_F16, nullptr, 0, s), QBLK_ERR_FORMAT);
+    REJECTS(qblk_gemv_batch(QBLK_SB4, -256, QBLK_F16, nullptr, 0, s), QBLK_ERR_SHAPE);
     it[2].x = MIS;  // a bad item anywhere stops the whole call
     REJECTS(qblk_gemv_batch(QBLK_SB4, 256, QBLK_F16, it, 3, s), QBLK_ERR_ALIGN);
     it[2].x = B;
