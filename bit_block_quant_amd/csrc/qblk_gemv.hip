@@ -761,11 +761,16 @@ hipError_t launch_h_t(const GemvJob& j, int64_t k, int rows_per_wg, hipStream_t 
 }
 
 // Rows per workgroup: an even share of the rows over the CUs, between one and
-// rmax_cap rounds of `slots` rows.
-inline int rows_per_wg(int64_t m, int slots, int rmax_cap) {
+// rmax_cap rounds of `slots` rows.  Where the share exceeds that cap, either
+// the cap (even_rounds false: the last round of workgroups can run partly
+// empty), or the share split into equal rounds of workgroups of at most the
+// cap (even_rounds true: every CU gets the same rows in each round).
+inline int rows_per_wg(int64_t m, int slots, int rmax_cap, bool even_rounds) {
   int64_t per = (m + cu_count() - 1) / cu_count();
+  const int64_t cap = static_cast<int64_t>(slots) * rmax_cap;
+  const int64_t rounds = (per + cap - 1) / cap;
+  if (rounds > 1) per = even_rounds ? (per + rounds - 1) / rounds : cap;
   per = per < slots ? slots : per;
-  per = per > static_cast<int64_t>(slots) * rmax_cap ? static_cast<int64_t>(slots) * rmax_cap : per;
   return static_cast<int>(per);
 }
 
@@ -779,9 +784,9 @@ hipError_t launch_h_r(int rmax, const GemvJob& j, int64_t k, int rpw, hipStream_
 }
 
 template <int FMT, int UPL, int KS, int RCAP, int WAVES = kWavesH, int XL = 0>
-hipError_t launch_h_k(const GemvJob& j, int64_t k, hipStream_t s) {
+hipError_t launch_h_k(const GemvJob& j, int64_t k, hipStream_t s, bool even_rounds = true) {
   constexpr int slots = WAVES / KS;
-  const int rpw = rows_per_wg(j.m, slots, RCAP);
+  const int rpw = rows_per_wg(j.m, slots, RCAP, even_rounds);
   return launch_h_r<FMT, UPL, KS, RCAP, WAVES, XL>((rpw + slots - 1) / slots, j, k, rpw, s);
 }
 
@@ -790,10 +795,10 @@ hipError_t launch_h_k(const GemvJob& j, int64_t k, hipStream_t s) {
 // so x is re-read once per wave; splitting a row over two waves halves the x
 // each wave loads (it matters most when a CU holds few rows). By units per
 // row S: up to 64 one wave per row and one unit per lane; up to 128 two
-// waves per row with one unit per lane each, up to 6 rows per wave (at
+// waves per row with one unit per lane each, up to 8 rows per wave (at
 // 4096 x 4096: 4.8-4.9 -> 4.3-4.5 us; at 11008 x 4096 Q4_0 8.0 -> 7.7,
 // Type 1 7.6 -> 7.4, Q4_K 7.8 -> 7.5 us) -- except Type 0 and Q4_0 with
-// more than 32 rows per CU: one wave per row, two units per lane, up to 3
+// more than 32 rows per CU: one wave per row, two units per lane, up to 4
 // rows per wave of 16-wave workgroups, x staged once per workgroup through
 // LDS before any weight load is issued (11008 x 4096 Type 0: 7.03 us with
 // every wave loading its own x in 12-wave workgroups, 6.66 us with x staged,
@@ -811,7 +816,15 @@ hipError_t launch_h_k(const GemvJob& j, int64_t k, hipStream_t s) {
 // Type 1 beyond 256 (4096 x 11008: 8.35 -> 7.68 us); for Type 0 and Q4_K it
 // was not (4096 x 4096 within 2%, 4096 x 11008 Type 0 +9%).  These two keep
 // the barrier after the weight loads (staging before them: 4.00 -> 4.09 and
-// 7.71 -> 7.99 us).
+// 7.71 -> 7.99 us).  Up to 128 units a workgroup takes up to 64 rows (4 slots
+// of 16 or 8 of 8): from 49 to 64 rows per CU that is one round of workgroups
+// where 48-row workgroups made 1.2-1.3 rounds (14336 x 4096: Type 0 10.7 ->
+// 8.2 us, Q4_0 10.9 -> 8.7, Type 1 12.0 -> 8.9, Q4_K 12.3 -> 8.6).  With more
+// rows per CU than a workgroup takes, rows of up to 256 units are split into
+// equal rounds (16385 x 4096 Type 0 11.0 -> 10.3 us, Type 1 12.3 -> 11.0;
+// 28672 x 4096 Type 0 16.8 -> 15.6, Q4_K 19.3 -> 16.5; 11008 x 8192 2-3% in
+// every format); longer rows keep full workgroups and a partly empty last
+// round (14336 x 11008 Q4_K: 29.5 us, 31.1 in equal rounds).
 template <int FMT>
 bool launch_h(const GemvJob& j, int64_t k, hipStream_t s, hipError_t* err) {
   const int64_t S = k / 32;
@@ -822,15 +835,15 @@ bool launch_h(const GemvJob& j, int64_t k, hipStream_t s, hipError_t* err) {
   const bool few = per_cu <= kWavesH;  // one row per wave at most
   if (S <= 64) *err = launch_h_k<FMT, 1, 1, 3>(j, k, s);
   else if (S <= 128 && FMT == QBLK_Q4_0 && few)
-    *err = launch_h_t<FMT, 1, 2, 1, kWavesH, 1>(j, k, rows_per_wg(m, kWavesH, 1), s);
+    *err = launch_h_t<FMT, 1, 2, 1, kWavesH, 1>(j, k, rows_per_wg(m, kWavesH, 1, true), s);
   else if (S > 256 && FMT == QBLK_SB4_AFFINE && few)
-    *err = launch_h_t<FMT, 1, 6, 1, kWavesH, 1>(j, k, rows_per_wg(m, kWavesH, 1), s);
-  else if (S <= 128 && kSigned && per_cu > 32) *err = launch_h_k<FMT, 2, 1, 3, kWavesH, 2>(j, k, s);
-  else if (S <= 128) *err = launch_h_k<FMT, 1, 2, 6>(j, k, s);
+    *err = launch_h_t<FMT, 1, 6, 1, kWavesH, 1>(j, k, rows_per_wg(m, kWavesH, 1, true), s);
+  else if (S <= 128 && kSigned && per_cu > 32) *err = launch_h_k<FMT, 2, 1, 4, kWavesH, 2>(j, k, s);
+  else if (S <= 128) *err = launch_h_k<FMT, 1, 2, 8>(j, k, s);
   else if (S <= 256) *err = launch_h_k<FMT, 2, 2, 3>(j, k, s);
-  else if (FMT == QBLK_SB4 && few) *err = launch_h_k<FMT, 3, 2, 2, kWavesH, 2>(j, k, s);
-  else if (FMT == QBLK_SB4) *err = launch_h_k<FMT, 3, 2, 3, 12>(j, k, s);
-  else *err = launch_h_k<FMT, 3, 2, 2>(j, k, s);
+  else if (FMT == QBLK_SB4 && few) *err = launch_h_k<FMT, 3, 2, 2, kWavesH, 2>(j, k, s, false);
+  else if (FMT == QBLK_SB4) *err = launch_h_k<FMT, 3, 2, 3, 12>(j, k, s, false);
+  else *err = launch_h_k<FMT, 3, 2, 2>(j, k, s, false);
   return true;
 }
 

@@ -399,14 +399,17 @@ def test_gemv_stack_matrices(q):
 # (Type 0 and Q4_0 beyond 32 rows per CU: 16-wave workgroups with x staged
 # in LDS before the weight loads, one wave per row, two units per lane, 3 row
 # slots per wave -- from 33 rows per CU, where most waves repeat a row, to a
-# last workgroup of 12 rows at 12300 x 4096); S <= 256 two
-# units per lane; S <= 384 three (Type 0 in 12-wave workgroups) -- with 1 to 6 row slots per wave (rows per
-# CU 2 .. 48 and beyond, on 256 CUs), ragged halves (S = 33, 73), fewer
+# last workgroup of 12 rows at 12300 x 4096; workgroups of up to 64 rows: 4
+# slots of 16 rows, or 8 of 8 for the affine formats -- 14336 x 4096 with 56
+# rows each; more rows per CU than that in equal rounds: 16385 x 4096 two
+# rounds of 33, 12545 x 2048 (one wave per row) two of 25); S <= 256 two
+# units per lane; S <= 384 three (Type 0 in 12-wave workgroups) -- with 1 to 8 row slots per wave (rows per
+# CU 2 .. 64 and beyond, on 256 CUs), ragged halves (S = 33, 73), fewer
 # rows than waves on every branch, and a one-unit row (S = 1).
 GEMV_TILINGS = [(300, 2048), (5000, 2048), (11008, 2048), (2048, 4096), (6144, 4096), (8192, 4096), (8448, 4096),
-                (8704, 4096), (10240, 4096), (12300, 4096), (500, 8192), (4096, 8192), (6200, 8192), (90, 1056),
-                (700, 2336), (9000, 2336), (9000, 4064), (2560, 11008), (3990, 11264), (3, 1024), (3, 4096), (5, 8192),
-                (2, 11264), (7, 32)]
+                (8704, 4096), (10240, 4096), (12300, 4096), (12545, 2048), (14336, 4096), (16385, 4096),
+                (500, 8192), (4096, 8192), (6200, 8192), (90, 1056), (700, 2336), (9000, 2336), (9000, 4064),
+                (2560, 11008), (3990, 11264), (3, 1024), (3, 4096), (5, 8192), (2, 11264), (7, 32)]
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: NAMES[f])
