@@ -60,6 +60,9 @@ void log_launch(const char* fmt, ...) {
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+// Rows of one qblk_gemm / qblk_gemm_w4a8 call: the product kernels run up to
+// 8 threads per row in one launch, which holds at most 2^32 - 1 threads.
+constexpr int64_t kMaxGemmRows = int64_t(1) << 28;
 constexpr int64_t kMaxBytes = int64_t(1) << 40;
 
 int elems_of(int fmt) {
@@ -211,6 +214,7 @@ qblk_status_t qblk_quantize_act_i8(const void* x, qblk_dtype_t xt, int64_t n, in
 qblk_status_t qblk_gemm_w4a8(const void* blocks, int64_t m, int64_t k, const int8_t* xq,
                              const float* scale, int64_t n, float* y, qblk_stream_t stream) {
   QBLK_TRY(check_shape(QBLK_W4G128, m, k));
+  if (m > kMaxGemmRows) return QBLK_ERR_SHAPE;
   if (n < 0 || n > kMaxDim) return QBLK_ERR_SHAPE;
   const bool out = m > 0 && n > 0;
   QBLK_TRY(check_ptr(blocks, out && k > 0));
@@ -283,6 +287,7 @@ qblk_status_t qblk_gemm(qblk_format_t fmt, const void* blocks, int64_t m, int64_
                         const void* x, qblk_dtype_t xt, int64_t n, float* y,
                         qblk_stream_t stream) {
   QBLK_TRY(check_shape(fmt, m, k));
+  if (m > kMaxGemmRows) return QBLK_ERR_SHAPE;
   if (!dtype_ok(xt)) return QBLK_ERR_DTYPE;
   if (n < 0 || n > kMaxDim) return QBLK_ERR_SHAPE;
   // the matrix-core kernels take bf16 activations and whole 256-weight groups

@@ -860,16 +860,31 @@ hipError_t launch_fmt(const void* blocks, int64_t m, int64_t k, const void* x, i
 }  // namespace
 
 namespace {
+// One matrix in pieces of at most kGemvRowsPerLaunch rows (a piece starts
+// at a row, so it is laid out like any other row start).
+template <int FMT>
+hipError_t launch_rows(const void* blocks, int64_t m, int64_t k, const void* x, int xt, float* y, hipStream_t s) {
+  const int64_t rowbytes = (k / Fmt<FMT>::E) * Fmt<FMT>::B;
+  for (int64_t r0 = 0; r0 < m; r0 += kGemvRowsPerLaunch) {
+    const int64_t n = m - r0 < kGemvRowsPerLaunch ? m - r0 : kGemvRowsPerLaunch;
+    const hipError_t e = launch_fmt<FMT>(static_cast<const uint8_t*>(blocks) + r0 * rowbytes, n, k, x, xt, y + r0, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <int FMT>
 hipError_t launch_batch_fmt(int64_t k, int xt, const qblk_gemv_item_t* items, int count, hipStream_t s) {
   int64_t rows = 0;
   for (int i = 0; i < count; i++) rows += items[i].m;
   hipError_t err = hipSuccess;
-  if (xt == QBLK_F16 && launch_h<FMT>(GemvJob{nullptr, nullptr, nullptr, rows, items, count}, k, s, &err))
+  if (xt == QBLK_F16 && rows <= kGemvRowsPerLaunch &&
+      launch_h<FMT>(GemvJob{nullptr, nullptr, nullptr, rows, items, count}, k, s, &err))
     return err;
-  // other x types, or rows past 12288 weights: one launch per matrix
+  // other x types, rows past 12288 weights or past one launch's rows: one
+  // launch per matrix (or piece of one)
   for (int i = 0; i < count && err == hipSuccess; i++)
-    err = launch_fmt<FMT>(items[i].blocks, items[i].m, k, items[i].x, xt, items[i].y, s);
+    err = launch_rows<FMT>(items[i].blocks, items[i].m, k, items[i].x, xt, items[i].y, s);
   return err;
 }
 }  // namespace
@@ -884,10 +899,10 @@ hipError_t launch_gemv_batch(int fmt, int64_t k, int xt, const qblk_gemv_item_t*
 
 hipError_t launch_gemv(int fmt, const void* blocks, int64_t m, int64_t k, const void* x, int xt,
                        float* y, hipStream_t s) {
-  if (fmt == QBLK_Q4_0) return launch_fmt<QBLK_Q4_0>(blocks, m, k, x, xt, y, s);
-  if (fmt == QBLK_SB4) return launch_fmt<QBLK_SB4>(blocks, m, k, x, xt, y, s);
-  if (fmt == QBLK_Q4_K) return launch_fmt<QBLK_Q4_K>(blocks, m, k, x, xt, y, s);
-  return launch_fmt<QBLK_SB4_AFFINE>(blocks, m, k, x, xt, y, s);
+  if (fmt == QBLK_Q4_0) return launch_rows<QBLK_Q4_0>(blocks, m, k, x, xt, y, s);
+  if (fmt == QBLK_SB4) return launch_rows<QBLK_SB4>(blocks, m, k, x, xt, y, s);
+  if (fmt == QBLK_Q4_K) return launch_rows<QBLK_Q4_K>(blocks, m, k, x, xt, y, s);
+  return launch_rows<QBLK_SB4_AFFINE>(blocks, m, k, x, xt, y, s);
 }
 
 hipError_t launch_fill_zero(float* y, int64_t n, hipStream_t s) {

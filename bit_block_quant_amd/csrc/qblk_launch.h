@@ -35,6 +35,29 @@ hipError_t launch_gemm(int fmt, const void* blocks, int64_t m, int64_t k, const 
                        int64_t n, float* y, hipStream_t s);
 hipError_t launch_fill_zero(float* y, int64_t n, hipStream_t s);
 
+// A dispatch packet counts its work-items in 32 bits per grid dimension, so
+// one launch covers at most 2^32 - 1 threads along x.  Launchers whose grid
+// grows with the data run it in pieces of whole workgroups:
+// launch(first, count) for consecutive ranges of `units` work units, at most
+// (max_threads / threads) * per_wg units each, stopping at the first error.
+constexpr int64_t kMaxDispatchThreads = 0xFFFFFFFFLL;
+
+template <class Launch>
+hipError_t in_pieces(int64_t units, int64_t per_wg, int64_t threads, Launch&& launch,
+                     int64_t max_threads = kMaxDispatchThreads) {
+  const int64_t per = (max_threads / threads) * per_wg;
+  for (int64_t u0 = 0; u0 < units; u0 += per) {
+    const hipError_t e = launch(u0, units - u0 < per ? units - u0 : per);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Rows of one GEMV launch: every GEMV kernel runs at most 128 threads per
+// row (two waves per row, one row per wave), so 2^24 rows stay far below
+// the dispatch limit; longer matrices are multiplied in pieces of rows.
+constexpr int64_t kGemvRowsPerLaunch = int64_t(1) << 24;
+
 // Compute units of the current device (queried once per device, then cached;
 // 256 if the query fails).  Every launcher sizes its grid from this.
 int cu_count();

@@ -766,51 +766,68 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict_
   store8<OT>(out, (g0 + gl) * E + (t % (E / 8)) * 8, y);
 }
 
-inline unsigned grid_for(int64_t weights) {
-  return static_cast<unsigned>((weights + kWgWeights - 1) / kWgWeights);
-}
+// Bytes per input or output element of a float type id.
+inline int64_t elem_bytes(int t) { return t == QBLK_F32 ? 4 : 2; }
+
+// Workgroups for `units` units of `per_wg` each (one launch's piece).
+inline unsigned wgs(int64_t units, int64_t per_wg) { return static_cast<unsigned>((units + per_wg - 1) / per_wg); }
 
 }  // namespace
 
 // ------------------------------------------------------------- launchers
+// Every launcher walks a flat sequence of independent blocks (or rows); a
+// sequence longer than one dispatch can hold runs in pieces of whole
+// workgroups, each with its pointers moved to its first block.
 hipError_t launch_quantize_q4_0(const void* w, int wt, int64_t rows, int64_t k, void* blocks,
                                 hipStream_t s) {
   const int64_t nb = rows * k / 32;
+  const uint8_t* wb = static_cast<const uint8_t*>(w);
   uint8_t* out = static_cast<uint8_t*>(blocks);
-  if (wt == QBLK_F32) {  // 8 weights per thread: 32-byte coalesced loads
-    const unsigned g = grid_for(rows * k);
-    if (log_enabled()) log_launch("quantize k_quant_q4_0 in=%d rows=%lld k=%lld grid=%u", wt, (long long)rows, (long long)k, g);
-    hipLaunchKernelGGL(k_quant_q4_0<QBLK_F32>, dim3(g), dim3(kThreads), 0, s, w, out, nb);
+  const int64_t es = elem_bytes(wt);
+  // fp32: 8 weights per thread (32-byte coalesced loads), 64 blocks per
+  // workgroup; 16-bit inputs: one 32-weight block per thread (64-byte loads)
+  const int64_t per = wt == QBLK_F32 ? kWgWeights / 32 : kThreads;
+  if (log_enabled())
+    log_launch("quantize %s in=%d rows=%lld k=%lld grid=%u", wt == QBLK_F32 ? "k_quant_q4_0" : "k_quant_q4_0_g", wt,
+               (long long)rows, (long long)k, wgs(nb, per));
+  return in_pieces(nb, per, kThreads, [&](int64_t b0, int64_t n) {
+    const void* wp = wb + b0 * 32 * es;
+    uint8_t* op = out + b0 * 18;
+    if (wt == QBLK_F32) hipLaunchKernelGGL(k_quant_q4_0<QBLK_F32>, dim3(wgs(n, per)), dim3(kThreads), 0, s, wp, op, n);
+    else if (wt == QBLK_F16) hipLaunchKernelGGL(k_quant_q4_0_g<QBLK_F16>, dim3(wgs(n, per)), dim3(kThreads), 0, s, wp, op, n);
+    else hipLaunchKernelGGL(k_quant_q4_0_g<QBLK_BF16>, dim3(wgs(n, per)), dim3(kThreads), 0, s, wp, op, n);
     return hipGetLastError();
-  }
-  // 16-bit inputs: one 32-weight block per thread (64-byte loads)
-  const unsigned g = static_cast<unsigned>((nb + kThreads - 1) / kThreads);
-  if (log_enabled()) log_launch("quantize k_quant_q4_0_g in=%d rows=%lld k=%lld grid=%u", wt, (long long)rows, (long long)k, g);
-  if (wt == QBLK_F16) hipLaunchKernelGGL(k_quant_q4_0_g<QBLK_F16>, dim3(g), dim3(kThreads), 0, s, w, out, nb);
-  else hipLaunchKernelGGL(k_quant_q4_0_g<QBLK_BF16>, dim3(g), dim3(kThreads), 0, s, w, out, nb);
-  return hipGetLastError();
+  });
 }
 
 hipError_t launch_quantize_q4_0_ref(const float* w, int64_t rows, int64_t k, void* blocks,
                                     hipStream_t s) {
+  const int64_t nb = rows * k / 32, per = kWgWeights / 32;
   if (log_enabled())
-    log_launch("quantize k_quant_q4_0_ref rows=%lld k=%lld grid=%u", (long long)rows, (long long)k, grid_for(rows * k));
-  hipLaunchKernelGGL(k_quant_q4_0_ref, dim3(grid_for(rows * k)), dim3(kThreads), 0, s, w,
-                     static_cast<uint8_t*>(blocks), rows * k / 32);
-  return hipGetLastError();
+    log_launch("quantize k_quant_q4_0_ref rows=%lld k=%lld grid=%u", (long long)rows, (long long)k, wgs(nb, per));
+  return in_pieces(nb, per, kThreads, [&](int64_t b0, int64_t n) {
+    hipLaunchKernelGGL(k_quant_q4_0_ref, dim3(wgs(n, per)), dim3(kThreads), 0, s, w + b0 * 32,
+                       static_cast<uint8_t*>(blocks) + b0 * 18, n);
+    return hipGetLastError();
+  });
 }
 
 template <bool A>
-static void launch_sb4_t(const void* w, int wt, int64_t nsb, uint8_t* out, hipStream_t s) {
-  if (wt == QBLK_F32) {  // 8 weights per thread: 32-byte coalesced loads
-    const unsigned g = static_cast<unsigned>((nsb + 7) / 8);
-    hipLaunchKernelGGL((k_quant_sb4<QBLK_F32, A>), dim3(g), dim3(kThreads), 0, s, w, out, nsb);
-    return;
-  }
-  // 16-bit inputs: one sub-block per thread (64-byte loads)
-  const unsigned g = static_cast<unsigned>((nsb + kThreads / 8 - 1) / (kThreads / 8));
-  if (wt == QBLK_F16) hipLaunchKernelGGL((k_quant_sb4_g<QBLK_F16, A>), dim3(g), dim3(kThreads), 0, s, w, out, nsb);
-  else hipLaunchKernelGGL((k_quant_sb4_g<QBLK_BF16, A>), dim3(g), dim3(kThreads), 0, s, w, out, nsb);
+static hipError_t launch_sb4_t(const void* w, int wt, int64_t nsb, uint8_t* out, hipStream_t s) {
+  constexpr int64_t B = A ? 148 : 138;
+  const uint8_t* wb = static_cast<const uint8_t*>(w);
+  const int64_t es = elem_bytes(wt);
+  // fp32: 8 weights per thread, 8 super-blocks per workgroup; 16-bit inputs:
+  // one sub-block per thread (64-byte loads), 32 super-blocks per workgroup
+  const int64_t per = wt == QBLK_F32 ? 8 : kThreads / 8;
+  return in_pieces(nsb, per, kThreads, [&](int64_t b0, int64_t n) {
+    const void* wp = wb + b0 * 256 * es;
+    uint8_t* op = out + b0 * B;
+    if (wt == QBLK_F32) hipLaunchKernelGGL((k_quant_sb4<QBLK_F32, A>), dim3(wgs(n, per)), dim3(kThreads), 0, s, wp, op, n);
+    else if (wt == QBLK_F16) hipLaunchKernelGGL((k_quant_sb4_g<QBLK_F16, A>), dim3(wgs(n, per)), dim3(kThreads), 0, s, wp, op, n);
+    else hipLaunchKernelGGL((k_quant_sb4_g<QBLK_BF16, A>), dim3(wgs(n, per)), dim3(kThreads), 0, s, wp, op, n);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_quantize_sb4(const void* w, int wt, int64_t rows, int64_t k, int affine,
@@ -821,57 +838,83 @@ hipError_t launch_quantize_sb4(const void* w, int wt, int64_t rows, int64_t k, i
     log_launch("quantize %s affine=%d in=%d rows=%lld k=%lld super-blocks=%lld",
                wt == QBLK_F32 ? "k_quant_sb4" : "k_quant_sb4_g", affine, wt, (long long)rows, (long long)k,
                (long long)nsb);
-  if (affine) launch_sb4_t<true>(w, wt, nsb, out, s);
-  else launch_sb4_t<false>(w, wt, nsb, out, s);
-  return hipGetLastError();
+  if (affine) return launch_sb4_t<true>(w, wt, nsb, out, s);
+  return launch_sb4_t<false>(w, wt, nsb, out, s);
 }
 
 hipError_t launch_quantize_w4g128(const void* w, int wt, int64_t rows, int64_t k, void* blocks,
                                   hipStream_t s) {
-  const int64_t ng = rows * k / 128;
+  const int64_t ng = rows * k / 128, per = kThreads / 16;  // 16 threads per 128-weight group
+  const uint8_t* wb = static_cast<const uint8_t*>(w);
   uint8_t* codes = static_cast<uint8_t*>(blocks);
   uint8_t* scales = codes + rows * k / 2;
-  const unsigned g = static_cast<unsigned>((ng + kThreads / 16 - 1) / (kThreads / 16));
-  if (log_enabled()) log_launch("quantize k_quant_w4g128 in=%d rows=%lld k=%lld grid=%u", wt, (long long)rows, (long long)k, g);
-  if (wt == QBLK_F32) hipLaunchKernelGGL(k_quant_w4g128<QBLK_F32>, dim3(g), dim3(kThreads), 0, s, w, codes, scales, ng);
-  else if (wt == QBLK_F16) hipLaunchKernelGGL(k_quant_w4g128<QBLK_F16>, dim3(g), dim3(kThreads), 0, s, w, codes, scales, ng);
-  else hipLaunchKernelGGL(k_quant_w4g128<QBLK_BF16>, dim3(g), dim3(kThreads), 0, s, w, codes, scales, ng);
-  return hipGetLastError();
+  const int64_t es = elem_bytes(wt);
+  if (log_enabled())
+    log_launch("quantize k_quant_w4g128 in=%d rows=%lld k=%lld grid=%u", wt, (long long)rows, (long long)k, wgs(ng, per));
+  return in_pieces(ng, per, kThreads, [&](int64_t g0, int64_t n) {
+    const void* wp = wb + g0 * 128 * es;
+    uint8_t* cp = codes + g0 * 64;
+    uint8_t* sp = scales + g0 * 2;
+    if (wt == QBLK_F32) hipLaunchKernelGGL(k_quant_w4g128<QBLK_F32>, dim3(wgs(n, per)), dim3(kThreads), 0, s, wp, cp, sp, n);
+    else if (wt == QBLK_F16) hipLaunchKernelGGL(k_quant_w4g128<QBLK_F16>, dim3(wgs(n, per)), dim3(kThreads), 0, s, wp, cp, sp, n);
+    else hipLaunchKernelGGL(k_quant_w4g128<QBLK_BF16>, dim3(wgs(n, per)), dim3(kThreads), 0, s, wp, cp, sp, n);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_quantize_act_i8(const void* x, int xt, int64_t n, int64_t k, int8_t* xq, float* scale,
                                   hipStream_t s) {
-  const dim3 g(static_cast<unsigned>(n));
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  const int64_t es = elem_bytes(xt);
   if (log_enabled()) log_launch("quantize k_quant_act_i8 in=%d n=%lld k=%lld grid=%lld", xt, (long long)n, (long long)k, (long long)n);
-  if (xt == QBLK_F32) hipLaunchKernelGGL(k_quant_act_i8<QBLK_F32>, g, dim3(kThreads), 0, s, x, xq, scale, k);
-  else if (xt == QBLK_F16) hipLaunchKernelGGL(k_quant_act_i8<QBLK_F16>, g, dim3(kThreads), 0, s, x, xq, scale, k);
-  else hipLaunchKernelGGL(k_quant_act_i8<QBLK_BF16>, g, dim3(kThreads), 0, s, x, xq, scale, k);
-  return hipGetLastError();
+  // one workgroup per row
+  return in_pieces(n, 1, kThreads, [&](int64_t r0, int64_t nr) {
+    const void* xp = xb + r0 * k * es;
+    int8_t* qp = xq + r0 * k;
+    float* sp = scale + r0;
+    const dim3 g(static_cast<unsigned>(nr));
+    if (xt == QBLK_F32) hipLaunchKernelGGL(k_quant_act_i8<QBLK_F32>, g, dim3(kThreads), 0, s, xp, qp, sp, k);
+    else if (xt == QBLK_F16) hipLaunchKernelGGL(k_quant_act_i8<QBLK_F16>, g, dim3(kThreads), 0, s, xp, qp, sp, k);
+    else hipLaunchKernelGGL(k_quant_act_i8<QBLK_BF16>, g, dim3(kThreads), 0, s, xp, qp, sp, k);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_quantize_q4_k(const void* w, int wt, int64_t rows, int64_t k, void* blocks,
                                 hipStream_t s) {
   const int64_t nsb = rows * k / 256;
+  const uint8_t* wb = static_cast<const uint8_t*>(w);
   uint8_t* out = static_cast<uint8_t*>(blocks);
+  const int64_t es = elem_bytes(wt);
+  const int64_t per = wt == QBLK_F32 ? 8 : kThreads / 8;
   if (log_enabled())
     log_launch("quantize %s in=%d rows=%lld k=%lld super-blocks=%lld", wt == QBLK_F32 ? "k_quant_q4k" : "k_quant_q4k_g",
                wt, (long long)rows, (long long)k, (long long)nsb);
-  if (wt == QBLK_F32) {
-    hipLaunchKernelGGL(k_quant_q4k<QBLK_F32>, dim3(static_cast<unsigned>((nsb + 7) / 8)), dim3(kThreads), 0, s,
-                       w, out, nsb);
+  return in_pieces(nsb, per, kThreads, [&](int64_t b0, int64_t n) {
+    const void* wp = wb + b0 * 256 * es;
+    uint8_t* op = out + b0 * 144;
+    if (wt == QBLK_F32) hipLaunchKernelGGL(k_quant_q4k<QBLK_F32>, dim3(wgs(n, per)), dim3(kThreads), 0, s, wp, op, n);
+    else if (wt == QBLK_F16) hipLaunchKernelGGL(k_quant_q4k_g<QBLK_F16>, dim3(wgs(n, per)), dim3(kThreads), 0, s, wp, op, n);
+    else hipLaunchKernelGGL(k_quant_q4k_g<QBLK_BF16>, dim3(wgs(n, per)), dim3(kThreads), 0, s, wp, op, n);
     return hipGetLastError();
-  }
-  const unsigned g = static_cast<unsigned>((nsb + kThreads / 8 - 1) / (kThreads / 8));
-  if (wt == QBLK_F16) hipLaunchKernelGGL(k_quant_q4k_g<QBLK_F16>, dim3(g), dim3(kThreads), 0, s, w, out, nsb);
-  else hipLaunchKernelGGL(k_quant_q4k_g<QBLK_BF16>, dim3(g), dim3(kThreads), 0, s, w, out, nsb);
-  return hipGetLastError();
+  });
 }
 
 template <int FMT>
-static void launch_deq_t(const uint8_t* b, int64_t nblk, void* out, int ot, unsigned g, hipStream_t s) {
-  if (ot == QBLK_F32) hipLaunchKernelGGL((k_dequant<FMT, QBLK_F32>), dim3(g), dim3(kThreads), 0, s, b, out, nblk);
-  else if (ot == QBLK_F16) hipLaunchKernelGGL((k_dequant<FMT, QBLK_F16>), dim3(g), dim3(kThreads), 0, s, b, out, nblk);
-  else hipLaunchKernelGGL((k_dequant<FMT, QBLK_BF16>), dim3(g), dim3(kThreads), 0, s, b, out, nblk);
+static hipError_t launch_deq_t(const uint8_t* b, int64_t nblk, void* out, int ot, hipStream_t s) {
+  constexpr int64_t E = FMT == QBLK_Q4_0 ? 32 : 256;
+  constexpr int64_t B = FMT == QBLK_Q4_0 ? 18 : FMT == QBLK_SB4 ? 138 : FMT == QBLK_Q4_K ? 144 : 148;
+  constexpr int64_t per = kWgWeights / E;  // blocks per workgroup
+  uint8_t* ob = static_cast<uint8_t*>(out);
+  const int64_t es = elem_bytes(ot);
+  return in_pieces(nblk, per, kThreads, [&](int64_t b0, int64_t n) {
+    const uint8_t* bp = b + b0 * B;
+    void* op = ob + b0 * E * es;
+    if (ot == QBLK_F32) hipLaunchKernelGGL((k_dequant<FMT, QBLK_F32>), dim3(wgs(n, per)), dim3(kThreads), 0, s, bp, op, n);
+    else if (ot == QBLK_F16) hipLaunchKernelGGL((k_dequant<FMT, QBLK_F16>), dim3(wgs(n, per)), dim3(kThreads), 0, s, bp, op, n);
+    else hipLaunchKernelGGL((k_dequant<FMT, QBLK_BF16>), dim3(wgs(n, per)), dim3(kThreads), 0, s, bp, op, n);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_dequant(int fmt, const void* blocks, int64_t rows, int64_t k, void* out, int ot,
@@ -881,20 +924,24 @@ hipError_t launch_dequant(int fmt, const void* blocks, int64_t rows, int64_t k, 
     log_launch("dequant %s fmt=%d out=%d rows=%lld k=%lld", fmt == QBLK_W4G128 ? "k_dequant_w4g128" : "k_dequant", fmt,
                ot, (long long)rows, (long long)k);
   if (fmt == QBLK_W4G128) {
-    const int64_t ng = rows * k / 128;
+    const int64_t ng = rows * k / 128, per = kThreads / 16;
     const uint8_t* sc = b + rows * k / 2;
-    const unsigned g = static_cast<unsigned>((ng + kThreads / 16 - 1) / (kThreads / 16));
-    if (ot == QBLK_F32) hipLaunchKernelGGL(k_dequant_w4g128<QBLK_F32>, dim3(g), dim3(kThreads), 0, s, b, sc, out, ng);
-    else if (ot == QBLK_F16) hipLaunchKernelGGL(k_dequant_w4g128<QBLK_F16>, dim3(g), dim3(kThreads), 0, s, b, sc, out, ng);
-    else hipLaunchKernelGGL(k_dequant_w4g128<QBLK_BF16>, dim3(g), dim3(kThreads), 0, s, b, sc, out, ng);
-    return hipGetLastError();
+    uint8_t* ob = static_cast<uint8_t*>(out);
+    const int64_t es = elem_bytes(ot);
+    return in_pieces(ng, per, kThreads, [&](int64_t g0, int64_t n) {
+      const uint8_t* cp = b + g0 * 64;
+      const uint8_t* sp = sc + g0 * 2;
+      void* op = ob + g0 * 128 * es;
+      if (ot == QBLK_F32) hipLaunchKernelGGL(k_dequant_w4g128<QBLK_F32>, dim3(wgs(n, per)), dim3(kThreads), 0, s, cp, sp, op, n);
+      else if (ot == QBLK_F16) hipLaunchKernelGGL(k_dequant_w4g128<QBLK_F16>, dim3(wgs(n, per)), dim3(kThreads), 0, s, cp, sp, op, n);
+      else hipLaunchKernelGGL(k_dequant_w4g128<QBLK_BF16>, dim3(wgs(n, per)), dim3(kThreads), 0, s, cp, sp, op, n);
+      return hipGetLastError();
+    });
   }
-  const unsigned g = grid_for(rows * k);
-  if (fmt == QBLK_Q4_0) launch_deq_t<QBLK_Q4_0>(b, rows * k / 32, out, ot, g, s);
-  else if (fmt == QBLK_SB4) launch_deq_t<QBLK_SB4>(b, rows * k / 256, out, ot, g, s);
-  else if (fmt == QBLK_Q4_K) launch_deq_t<QBLK_Q4_K>(b, rows * k / 256, out, ot, g, s);
-  else launch_deq_t<QBLK_SB4_AFFINE>(b, rows * k / 256, out, ot, g, s);
-  return hipGetLastError();
+  if (fmt == QBLK_Q4_0) return launch_deq_t<QBLK_Q4_0>(b, rows * k / 32, out, ot, s);
+  if (fmt == QBLK_SB4) return launch_deq_t<QBLK_SB4>(b, rows * k / 256, out, ot, s);
+  if (fmt == QBLK_Q4_K) return launch_deq_t<QBLK_Q4_K>(b, rows * k / 256, out, ot, s);
+  return launch_deq_t<QBLK_SB4_AFFINE>(b, rows * k / 256, out, ot, s);
 }
 
 }  // namespace qblk

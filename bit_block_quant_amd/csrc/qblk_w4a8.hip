@@ -629,7 +629,16 @@ hipError_t launch_gemm_w4a8(const void* blocks, int64_t m, int64_t k, const int8
                             int64_t n, float* y, hipStream_t s) {
   const uint8_t* codes = static_cast<const uint8_t*>(blocks);
   const uint16_t* scales = reinterpret_cast<const uint16_t*>(codes + m * k / 2);
-  if (n == 1 && k <= 8 * 64 * 32) return launch_v(codes, scales, m, k, xq, xs, y, s);
+  if (n == 1 && k <= 8 * 64 * 32) {
+    // in pieces of at most kGemvRowsPerLaunch rows (codes and scales of a
+    // piece start at its first row)
+    for (int64_t r0 = 0; r0 < m; r0 += kGemvRowsPerLaunch) {
+      const int64_t nr = m - r0 < kGemvRowsPerLaunch ? m - r0 : kGemvRowsPerLaunch;
+      const hipError_t e = launch_v(codes + r0 * (k / 2), scales + r0 * (k / 128), nr, k, xq, xs, y + r0, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   // tilings measured at 14336 x 4096 and 4096 x 14336: up to N = 32 the
   // unit-loaded kernel, 64 rows x 4 groups per workgroup of 8 waves (N = 2 /
   // 16: 12.0 / 14.8 us, against 16.4 / 17.9 us for operand-order loads with

@@ -80,7 +80,11 @@
  *   - k must be a multiple of the format's block size (QBLK_ERR_SHAPE);
  *     rows/m/n/k may be 0 (an empty product writes zeros to y when m, n > 0).
  *   - rows, m, n and k must each stay below 2^31, and a packed matrix below
- *     2^40 bytes (QBLK_ERR_SHAPE).
+ *     2^40 bytes (QBLK_ERR_SHAPE); qblk_gemm and qblk_gemm_w4a8 take at most
+ *     m = 2^28 rows (QBLK_ERR_SHAPE).  A call whose grid would exceed the
+ *     2^32 - 1 threads one launch can hold (the quantizers, dequant, the
+ *     activation quantizer and the batch-1 products at very large sizes)
+ *     is run as several launches in stream order.
  *   - Inputs must be finite; non-finite inputs give unspecified results.
  *     A block whose scale overflows fp16 (|w| > 7 * 65504 for Q4_0 and
  *     Type 0, a 32-weight range above 15 * 65504 for Type 1) is stored with an

@@ -10,6 +10,8 @@
 #include <string.h>
 
 #include <string>
+#include <utility>
+#include <vector>
 
 namespace {
 
@@ -264,6 +266,50 @@ int main() {
   EXPECT(g_call.a == 8);
   LAUNCHES(qblk_gemm_w4a8(A, 4, 128, static_cast<const int8_t*>(B), Y, 2, Y, s), "gemm_w4a8");
   EXPECT(g_call.c == 2);
+
+  // at most 2^28 rows per product call
+  const int64_t kGemmRows = int64_t(1) << 28;
+  REJECTS(qblk_gemm(QBLK_SB4, A, kGemmRows + 1, 256, B, QBLK_BF16, 2, Y, s), QBLK_ERR_SHAPE);
+  LAUNCHES(qblk_gemm(QBLK_SB4, A, kGemmRows, 256, B, QBLK_BF16, 2, Y, s), "gemm");
+  REJECTS(qblk_gemm_w4a8(A, kGemmRows + 1, 128, static_cast<const int8_t*>(B), Y, 2, Y, s), QBLK_ERR_SHAPE);
+  LAUNCHES(qblk_gemm_w4a8(A, kGemmRows, 128, static_cast<const int8_t*>(B), Y, 2, Y, s), "gemm_w4a8");
+
+  // launches in pieces of whole workgroups: every unit once, in order
+  {
+    std::vector<std::pair<int64_t, int64_t>> got;
+    auto rec = [&](int64_t u0, int64_t n) {
+      got.emplace_back(u0, n);
+      return hipSuccess;
+    };
+    auto covers = [&](int64_t units, int64_t per) {
+      int64_t next = 0;
+      bool ok = true;
+      for (const auto& p : got) {
+        ok = ok && p.first == next && p.second > 0 && p.second <= per && (p.first % per) == 0;
+        next += p.second;
+      }
+      return ok && next == units;
+    };
+    // a limit of 10 workgroups of 256 threads, 8 units each: 80 units a launch
+    EXPECT(qblk::in_pieces(1000, 8, 256, rec, 256 * 10) == hipSuccess);
+    EXPECT(got.size() == 13 && covers(1000, 80));
+    // the dispatch limit itself: (2^32 - 1) / 256 = 16777215 workgroups
+    const int64_t wg_max = 16777215;
+    got.clear();
+    EXPECT(qblk::in_pieces(wg_max * 64, 64, 256, rec) == hipSuccess && got.size() == 1 && covers(wg_max * 64, wg_max * 64));
+    got.clear();
+    EXPECT(qblk::in_pieces(wg_max * 64 + 1, 64, 256, rec) == hipSuccess && got.size() == 2 &&
+           covers(wg_max * 64 + 1, wg_max * 64) && got[1].second == 1);
+    got.clear();
+    EXPECT(qblk::in_pieces(wg_max + 5, 1, 256, rec) == hipSuccess && got.size() == 2 && covers(wg_max + 5, wg_max));
+    // nothing to do: no launch; an error stops the sequence and is returned
+    got.clear();
+    EXPECT(qblk::in_pieces(0, 8, 256, rec) == hipSuccess && got.empty());
+    int calls = 0;
+    EXPECT(qblk::in_pieces(1000, 8, 256, [&](int64_t, int64_t) { return ++calls == 2 ? hipErrorInvalidValue : hipSuccess; },
+                           256 * 10) == hipErrorInvalidValue &&
+           calls == 2);
+  }
 
   // a launcher's error becomes QBLK_ERR_LAUNCH
   g_ret = hipErrorInvalidValue;

@@ -76,6 +76,8 @@ def test_argument_errors(q):
     assert L.qblk_quantize_sb4(A, 0, -1, 256, 1, B, S) == 2
     assert L.qblk_gemv(1, A, 1 << 31, 256, B, 1, Y, S) == 2
     assert L.qblk_gemm(1, A, 16, 256, B, 2, -1, Y, S) == 2
+    assert L.qblk_gemm(1, A, (1 << 28) + 1, 256, B, 2, 2, Y, S) == 2  # at most 2^28 rows per product
+    assert L.qblk_gemm_w4a8(A, (1 << 28) + 1, 128, B, Y, 2, Y, S) == 2
     # format / dtype
     assert L.qblk_dequant(7, A, 1, 256, B, 0, S) == 7
     assert L.qblk_gemv(1, A, 1, 256, B, 5, Y, S) == 3
