@@ -437,6 +437,11 @@ def measure_rows(torch, q, WL, np, dev):
     gemv_row("gemv_q4_0_256x4096_f32", q.Q4_0, torch.from_numpy(w).to(dev), torch.from_numpy(x).to(dev))
     w, x = WL.sb4_decode("up")
     gemv_row("gemv_q4k_11008x4096_f16", q.Q4_K, torch.from_numpy(w).to(dev), torch.from_numpy(x).to(dev))
+    # the prefill workload's 14336x4096 Type 0 matrix (gate/up of an 8B
+    # model) at batch 1, with the decode workload's x
+    w14, _ = WL.sb4_prefill("up", 1)
+    gemv_row("gemv_sb4_14336x4096_f16", q.SB4, torch.from_numpy(w14).to(dev), torch.from_numpy(x).to(dev))
+    del w14
 
     # the headline matrix as a layer's gate and up projections: two 11008x4096
     # Type 0 matrices against one x in one qblk_gemv_batch launch (pairs of
