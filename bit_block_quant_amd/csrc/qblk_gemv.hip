@@ -644,7 +644,7 @@ __device__ __forceinline__ void gemv_h_body(const uint8_t* __restrict__ blocks, 
 }
 
 template <int FMT, int RMAX, int UPL, int KS, int WAVES = kWavesH, int XL = 0>
-__global__ __launch_bounds__(WAVES * kWave) void k_gemv_h(const uint8_t* __restrict__ blocks,
+__global__ __launch_bounds__(WAVES * kWave, WAVES == 8 ? 4 : 1) void k_gemv_h(const uint8_t* __restrict__ blocks,
                                                       const uint16_t* __restrict__ x,
                                                       float* __restrict__ y, int M, int K,
                                                       int rows_per_wg) {
@@ -664,7 +664,7 @@ struct GemvBatch {
 };
 
 template <int FMT, int RMAX, int UPL, int KS, int WAVES = kWavesH, int XL = 0>
-__global__ __launch_bounds__(WAVES * kWave) void k_gemv_hb(const GemvBatch b, int K, int rows_per_wg) {
+__global__ __launch_bounds__(WAVES * kWave, WAVES == 8 ? 4 : 1) void k_gemv_hb(const GemvBatch b, int K, int rows_per_wg) {
   const unsigned w = blockIdx.x;
   int i = 0;
   while (i + 1 < b.count && w >= b.wg_end[i]) i++;
@@ -783,6 +783,22 @@ hipError_t launch_h_r(int rmax, const GemvJob& j, int64_t k, int rpw, hipStream_
   return launch_h_t<FMT, R, UPL, KS, WAVES, XL>(j, k, rpw, s);
 }
 
+// Two workgroups per CU: 8 waves each, at most 128 registers per lane (the
+// kernels' launch bounds ask for 4 waves per SIMD at 8 waves), rows shared
+// evenly over 2 x CUs workgroup slots, in equal rounds of at most RCAP row
+// slots per wave.
+template <int FMT, int UPL, int KS, int RCAP, int XL = 0>
+hipError_t launch_h_k2(const GemvJob& j, int64_t k, hipStream_t s) {
+  constexpr int WAVES = 8, slots = WAVES / KS;
+  int64_t per = (j.m + 2 * cu_count() - 1) / (2 * cu_count());
+  const int64_t cap = static_cast<int64_t>(slots) * RCAP;
+  const int64_t rounds = (per + cap - 1) / cap;
+  if (rounds > 1) per = (per + rounds - 1) / rounds;
+  per = per < slots ? slots : per;
+  const int rpw = static_cast<int>(per);
+  return launch_h_r<FMT, UPL, KS, RCAP, WAVES, XL>((rpw + slots - 1) / slots, j, k, rpw, s);
+}
+
 template <int FMT, int UPL, int KS, int RCAP, int WAVES = kWavesH, int XL = 0>
 hipError_t launch_h_k(const GemvJob& j, int64_t k, hipStream_t s, bool even_rounds = true) {
   constexpr int slots = WAVES / KS;
@@ -824,7 +840,13 @@ hipError_t launch_h_k(const GemvJob& j, int64_t k, hipStream_t s, bool even_roun
 // equal rounds (16385 x 4096 Type 0 11.0 -> 10.3 us, Type 1 12.3 -> 11.0;
 // 28672 x 4096 Type 0 16.8 -> 15.6, Q4_K 19.3 -> 16.5; 11008 x 8192 2-3% in
 // every format); longer rows keep full workgroups and a partly empty last
-// round (14336 x 11008 Q4_K: 29.5 us, 31.1 in equal rounds).
+// round (14336 x 11008 Q4_K: 29.5 us, 31.1 in equal rounds).  Past one round
+// of 64-row workgroups the affine formats (up to 128 units) run two 8-wave
+// workgroups per CU, so one workgroup's loads are in flight while the other
+// finishes: Type 1 4-12% and Q4_K 1-15% faster from 16385 to 44032 rows
+// (38400 x 4096 Type 1: 22.5 -> 21.0 us); for Type 0 and Q4_0 it was mixed
+// (Type 0 +3-5% from 16385 to 22016 rows, -10% at 44032), so they keep one
+// 16-wave workgroup per CU.
 template <int FMT>
 bool launch_h(const GemvJob& j, int64_t k, hipStream_t s, hipError_t* err) {
   const int64_t S = k / 32;
@@ -839,6 +861,7 @@ bool launch_h(const GemvJob& j, int64_t k, hipStream_t s, hipError_t* err) {
   else if (S > 256 && FMT == QBLK_SB4_AFFINE && few)
     *err = launch_h_t<FMT, 1, 6, 1, kWavesH, 1>(j, k, rows_per_wg(m, kWavesH, 1, true), s);
   else if (S <= 128 && kSigned && per_cu > 32) *err = launch_h_k<FMT, 2, 1, 4, kWavesH, 2>(j, k, s);
+  else if (S <= 128 && per_cu > 64) *err = launch_h_k2<FMT, 1, 2, 8>(j, k, s);
   else if (S <= 128) *err = launch_h_k<FMT, 1, 2, 8>(j, k, s);
   else if (S <= 256) *err = launch_h_k<FMT, 2, 2, 3>(j, k, s);
   else if (FMT == QBLK_SB4 && few) *err = launch_h_k<FMT, 3, 2, 2, kWavesH, 2>(j, k, s, false);

@@ -402,7 +402,8 @@ def test_gemv_stack_matrices(q):
 # last workgroup of 12 rows at 12300 x 4096; workgroups of up to 64 rows: 4
 # slots of 16 rows, or 8 of 8 for the affine formats -- 14336 x 4096 with 56
 # rows each; more rows per CU than that in equal rounds: 16385 x 4096 two
-# rounds of 33, 12545 x 2048 (one wave per row) two of 25); S <= 256 two
+# rounds of 33 (the affine formats: two 8-wave workgroups per CU of 17 rows
+# each), 12545 x 2048 (one wave per row) two of 25); S <= 256 two
 # units per lane; S <= 384 three (Type 0 in 12-wave workgroups) -- with 1 to 8 row slots per wave (rows per
 # CU 2 .. 64 and beyond, on 256 CUs), ragged halves (S = 33, 73), fewer
 # rows than waves on every branch, and a one-unit row (S = 1).
