@@ -458,6 +458,36 @@ def test_gemm_tolerance_small(q, n):
     check_products(Y, Y_ref, B, f"gemm n={n}")
 
 
+# Activations of extreme spread and magnitude: within one token's super-block
+# a largest |x| of 1.5 beside 2^-29 or 2^-30, a token scaled by 2^100, a value
+# of 2^116, a super-block scaled by 2^-90, and whole tokens of zeros (exactly
+# zero outputs), in a ragged shape (150 rows, 9 super-blocks).
+@pytest.mark.parametrize("case", ["spread_2e-29", "spread_2e-30", "times_2e100", "value_2e116", "times_2e-90", "zero_tokens"])
+def test_gemm_sb4_extreme_activations(q, case):
+    m, k, n = 150, 2304, 11
+    w = mixed_blocks(m, k, 21)
+    blocks = O.quantize_sb4(w)
+    Xf = np.random.default_rng(22).standard_normal((n, k)).astype(np.float32)
+    if case == "spread_2e-29":      # 1.5 beside 2^-29
+        Xf[3, 256:512] = 0.0
+        Xf[3, 300], Xf[3, 301] = 1.5, 2.0 ** -29
+    elif case == "spread_2e-30":   # 1.5 beside 2^-30
+        Xf[3, 300], Xf[3, 301] = 1.5, 2.0 ** -30
+    elif case == "times_2e100":    # a token's first super-block times 2^100
+        Xf[5, :256] *= 2.0 ** 100
+    elif case == "value_2e116":   # one value of 2^116
+        Xf[5, :256] = 0.5
+        Xf[5, 7] = 2.0 ** 116
+    elif case == "times_2e-90":  # a super-block times 2^-90
+        Xf[2, 1024:1280] *= 2.0 ** -90
+    else:                      # whole tokens of zeros
+        Xf[[0, 4, 10]] = 0.0
+    X = WL.bf16_bits(Xf)
+    Y = host(q.gemm(dev(blocks), q.SB4, m, k, dev_bf16(X)))
+    Y_ref, B = O.gemm(O.SB4, blocks, m, k, WL.bf16_values(X).astype(np.float64))
+    check_products(Y, Y_ref, B, f"gemm extreme activations {case}")
+
+
 def gemm_fmt(q, name):
     """(library format id, oracle format id) for a format name."""
     return {"q4_0": (q.Q4_0, O.Q4_0), "sb4a": (q.SB4_AFFINE, O.SB4_AFFINE), "q4k": (q.Q4_K, O.Q4_K)}[name]
