@@ -271,6 +271,38 @@ def test_gemv_tolerance(q, fmt, xt, shape):
     check_products(y, y_ref, bound, f"{NAMES[fmt]} {xt} {shape}")
 
 
+# x at the ends of its type's range: exact zeros, fp16 subnormals and
+# +-65504, bf16/fp32 values near 1e+-30 and their smallest normals, mixed into
+# N(0,1) values; zero units and whole zero rows of x's reach (y exactly 0 where
+# the bound is 0).  Shapes that reach the per-wave, LDS-staged and generic
+# kernels.
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: NAMES[f])
+@pytest.mark.parametrize("xt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("shape", [(37, 2304), (4096, 4096), (300, 11008)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_gemv_extreme_x(q, fmt, xt, shape):
+    m, k = shape
+    w = mixed_blocks(m, k, 90 + m)
+    blocks = O.quantize(fmt, w)
+    rng = np.random.default_rng(91)
+    xs = rng.standard_normal(k).astype(np.float32)
+    idx = rng.permutation(k)
+    if xt == "f16":
+        big, small, tiny = 65504.0, 6.0e-8, 6.104e-5  # max, subnormal, smallest normal
+    else:
+        big, small, tiny = 1.0e30, 1.0e-30, 1.1754944e-38
+    xs[idx[0:40:4]] = big
+    xs[idx[1:40:4]] = -big
+    xs[idx[2:40:4]] = small
+    xs[idx[3:40:4]] = -tiny
+    xs[64:96] = 0.0    # one whole unit of zeros
+    xs[256:512] = 0.0  # one whole super-block of zeros
+    x = xs if xt == "f32" else xs.astype(np.float16) if xt == "f16" else WL.bf16_bits(xs)
+    xd, xr = x_dev(x)
+    y = host(q.gemv(dev(blocks), fmt, m, k, xd))
+    y_ref, bound = O.gemv(fmt, blocks, m, k, xr)
+    check_products(y, y_ref, bound, f"{NAMES[fmt]} {xt} {shape} extreme x")
+
+
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: NAMES[f])
 @pytest.mark.parametrize("k", [2304, 4096, 11008, 13056])
 @pytest.mark.parametrize("xt", ["f16", "f32"])
