@@ -45,10 +45,19 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_sb4_11008x4096.json"
 
 
 def kernel_source_hash():
+    """What the headline kernel's machine code comes from: its sources and the
+    compiler flags of the build (bit_block_quant_amd/build.py, read by path)."""
+    import importlib.util
+
     h = hashlib.sha256()
     for f in ("qblk_gemv.hip", "qblk_device.h"):
         with open(os.path.join(ROOT, "bit_block_quant_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    spec = importlib.util.spec_from_file_location("_qblk_build_flags",
+                                                  os.path.join(ROOT, "bit_block_quant_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    h.update(" ".join(mod.FLAGS).encode())
     return h.hexdigest()[:16]
 
 
